@@ -1,0 +1,346 @@
+"""CPU oracle of the MM-DiT block, the single-stream block and the denoise step.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module. The product path (the
+HIP library and its binding) never calls it, and shares no code with it.
+
+Plain, slow, obviously correct numpy in float64: every dot product, mean and
+softmax sum is taken in fp64 from the bf16-exact inputs, with no intermediate
+rounding, no tiling and no fusion. A numpy matrix product is used as the one
+library primitive (the definition of a linear layer).
+
+Sources (cited by page title and section):
+
+* Luminal blog, "Reducing image generation cost with...":
+  - section "What the compiler found on its own": a matrix product is a
+    broadcast multiply and a sum; attention is two such products, a scale, a
+    max, an exponent, a sum and a divide; RMSNorm is a square, a sum, a
+    reciprocal square root and a multiply; LayerNorm adds a mean and a
+    subtraction; the adaLN modulation after it is a scale and a shift; RoPE
+    multiplies each element and its partner against cosine and sine tables;
+    a gate-and-residual add follows each branch; the text and image streams
+    are concatenated; a timestep embedding conditions the blocks.
+  - section "Flux.2 Klein 9B": a double-stream block has its own projections
+    before the attention and its own norm and feed-forward network after it,
+    per stream; a single-stream block shares them.
+  - section "The AMD MI300X pipeline": bf16 GEMMs accumulate in fp32 (here:
+    fp64, a superset); the Euler sampler integrates the latent in fp32.
+* flux-amd-rocm benchmarks page (header): FLUX.1-dev at 28 steps, guidance
+  3.5, int8 weight-only linears.
+
+Readings where the pages are silent (each one is also listed in the design
+notes): GELU in its tanh form; LayerNorm without affine, biased variance,
+eps 1e-6; adaLN as (1 + scale) * LN(x) + shift; SiLU on the conditioning
+vector before every modulation linear; RoPE on adjacent pairs (2j, 2j+1),
+axes (t, h, w) in that order, theta 1e4, applied after RMSNorm; no attention
+mask; text tokens first in the joint sequence; a bias on every linear;
+timestep embedding of width 256 over 1000 * t, max period 1e4, [cos | sin].
+
+Chunk orders (conventions, weights are random): double-block modulation
+[shift1, scale1, gate1, shift2, scale2, gate2]; single-block [shift, scale,
+gate]; final layer [shift, scale]; qkv columns [q | k | v], each head-major
+(column h * D + d); linear1 columns [q | k | v | mlp]; linear2 input
+[attention | GELU(mlp)].
+"""
+from __future__ import annotations
+
+import math
+from collections import Counter
+from typing import Optional, Sequence
+
+import numpy as np
+
+# Counts how many times each normalisation / attention site runs, so that a
+# test can compare the block structure with the launch counts the Luminal
+# blog reports per diffusion step.
+SITE_COUNTS: Counter = Counter()
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# elementwise functions
+# --------------------------------------------------------------------------
+def silu(x):
+    """SiLU(x) = x / (1 + e^-x)."""
+    x = _f64(x)
+    return x / (1.0 + np.exp(-x))
+
+
+def gelu_tanh(x):
+    """GELU, tanh form: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))."""
+    x = _f64(x)
+    return 0.5 * x * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (x + 0.044715 * x ** 3)))
+
+
+# --------------------------------------------------------------------------
+# linear layers ("What the compiler found on its own": multiply then sum)
+# --------------------------------------------------------------------------
+def weight_matrix(lin) -> np.ndarray:
+    """The layer's weight as fp64: W itself, or diag(s) Q for an int8 layer
+    (flux-amd-rocm benchmarks page: int8 weight-only linears)."""
+    if lin.q is not None:
+        return _f64(lin.s)[:, None] * _f64(lin.q)
+    return _f64(lin.w)
+
+
+def linear(x, lin) -> np.ndarray:
+    """y = x W^T + b, for x [..., in]."""
+    return _f64(x) @ weight_matrix(lin).T + _f64(lin.b)
+
+
+# --------------------------------------------------------------------------
+# normalisations ("What the compiler found on its own")
+# --------------------------------------------------------------------------
+def layer_norm(x, eps: float) -> np.ndarray:
+    """(x - mean) / sqrt(var + eps) over the last axis, biased var, no affine."""
+    x = _f64(x)
+    mu = x.mean(axis=-1, keepdims=True)
+    d = x - mu
+    var = (d * d).mean(axis=-1, keepdims=True)
+    return d / np.sqrt(var + eps)
+
+
+def modulate(y, shift, scale) -> np.ndarray:
+    """adaLN modulation: y * (1 + scale) + shift."""
+    return _f64(y) * (1.0 + _f64(scale)) + _f64(shift)
+
+
+def ln_modulate(x, shift, scale, eps: float) -> np.ndarray:
+    """One LayerNorm + modulate site."""
+    SITE_COUNTS["ln_modulate"] += 1
+    return modulate(layer_norm(x, eps), shift, scale)
+
+
+def rms_norm(u, g, eps: float) -> np.ndarray:
+    """u / sqrt(mean(u^2) + eps) * g over the last axis (one head's D values)."""
+    u = _f64(u)
+    ms = (u * u).mean(axis=-1, keepdims=True)
+    return u / np.sqrt(ms + eps) * _f64(g)
+
+
+# --------------------------------------------------------------------------
+# axial rotary embedding ("What the compiler found on its own": a partner
+# gather and a multiply-add against cosine and sine tables)
+# --------------------------------------------------------------------------
+def rope_angles(ids, axes: Sequence[int], theta: float) -> np.ndarray:
+    """Angles phi [L, D/2]. Pair p belongs to axis a (segments t, h, w of the
+    head dim in that order); its j-th pair in that axis turns by
+    pos_a * theta^(-2j / d_a)."""
+    ids = np.asarray(ids)
+    cols = []
+    for a, d_a in enumerate(axes):
+        j = np.arange(d_a // 2, dtype=np.float64)
+        freq = theta ** (-2.0 * j / d_a)
+        cols.append(ids[:, a].astype(np.float64)[:, None] * freq[None, :])
+    return np.concatenate(cols, axis=1)
+
+
+def apply_rope(u, phi) -> np.ndarray:
+    """Rotate adjacent pairs (u_2j, u_2j+1) of u [L, D] by phi [L, D/2]."""
+    u = _f64(u)
+    u0, u1 = u[:, 0::2], u[:, 1::2]
+    c, s = np.cos(phi), np.sin(phi)
+    out = np.empty_like(u)
+    out[:, 0::2] = u0 * c - u1 * s
+    out[:, 1::2] = u0 * s + u1 * c
+    return out
+
+
+def qk_norm_rope(u, g, phi, eps: float) -> np.ndarray:
+    """One fused RMSNorm + RoPE site: per token, RMSNorm over the head dim, then
+    the rotation. u [L, D] for one head."""
+    return apply_rope(rms_norm(u, g, eps), phi)
+
+
+# --------------------------------------------------------------------------
+# attention ("What the compiler found on its own": two multiply-sums, a scale,
+# a max, an exponent, another sum and a divide; no mask in the transformer)
+# --------------------------------------------------------------------------
+def softmax_rows(s) -> np.ndarray:
+    s = _f64(s)
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def attention_head(q, k, v, rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """softmax(q k^T / sqrt(D)) v for one head; q, k, v [L, D]. With ``rows``
+    only those query rows are evaluated (each output row depends on its own
+    query and on every key and value)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if rows is not None:
+        q = q[rows]
+    s = (q @ k.T) / math.sqrt(q.shape[-1])
+    return softmax_rows(s) @ v
+
+
+def attention(q, k, v, heads: int, rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Multi-head attention over [L, heads*D] tensors, heads side by side."""
+    SITE_COUNTS["attention"] += 1
+    L, HD = _f64(k).shape
+    D = HD // heads
+    n = L if rows is None else len(rows)
+    out = np.empty((n, HD), dtype=np.float64)
+    for h in range(heads):
+        sl = slice(h * D, (h + 1) * D)
+        out[:, sl] = attention_head(q[:, sl], k[:, sl], v[:, sl], rows)
+    return out
+
+
+# --------------------------------------------------------------------------
+# block pieces
+# --------------------------------------------------------------------------
+def modulation(vec, lin, chunks: int):
+    """SiLU(vec) W^T + b, split into ``chunks`` equal parts of width H."""
+    m = linear(silu(vec)[None, :], lin)[0]
+    return np.split(m, chunks)
+
+
+def norm_rope_heads(u, g, phi, heads: int, eps: float) -> np.ndarray:
+    """Apply RMSNorm + RoPE to every head of u [L, heads*D] (one site)."""
+    SITE_COUNTS["rmsnorm_rope"] += 1
+    L, HD = u.shape
+    D = HD // heads
+    out = np.empty((L, HD), dtype=np.float64)
+    for h in range(heads):
+        sl = slice(h * D, (h + 1) * D)
+        out[:, sl] = qk_norm_rope(u[:, sl], g, phi, eps)
+    return out
+
+
+def double_block(x, vec, ids, w, shp, rows: Optional[np.ndarray] = None,
+                 return_stages: bool = False):
+    """Double-stream block ("Flux.2 Klein 9B" and "What the compiler found on
+    its own" sections of the Luminal blog).
+
+    x [L, H] holds the text rows first, then the image rows. For each stream s
+    with its own weights:
+      m_s = modulation(vec) -> shift1, scale1, gate1, shift2, scale2, gate2
+      h_s = LN(x_s) * (1 + scale1) + shift1
+      q_s, k_s, v_s = split(h_s W_qkv^T + b)
+      q_s, k_s = RMSNorm per head (per-stream scales)
+    then over the joint sequence: RoPE, attention; then per stream
+      x_s += gate1 * (O_s W_proj^T + b)
+      x_s += gate2 * (GELU(LN(x_s) * (1 + scale2) + shift2) W_fc1^T + b) W_fc2^T + b)
+    With ``rows`` only those output rows are returned (all keys and values
+    are still computed).
+    """
+    H, heads, L_t = shp.hidden, shp.heads, shp.txt_len
+    x = _f64(x)
+    L = x.shape[0]
+    phi = rope_angles(ids, shp.axes, shp.theta)
+    seg = {"txt": slice(0, L_t), "img": slice(L_t, L)}
+    mods = {s: modulation(vec, w[s]["mod"], 6) for s in seg}
+    q = np.empty((L, H)); k = np.empty((L, H)); v = np.empty((L, H))
+    stages = {}
+    for s, sl in seg.items():
+        sh1, sc1 = mods[s][0], mods[s][1]
+        h = ln_modulate(x[sl], sh1, sc1, shp.ln_eps)
+        qkv = linear(h, w[s]["qkv"])
+        q[sl], k[sl], v[sl] = qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:]
+        stages[f"h1_{s}"] = h
+        stages[f"qkv_{s}"] = qkv
+    # RMSNorm + RoPE: q and k of each stream are normalised with that stream's
+    # scales; the rotation uses the joint positions.
+    for s, sl in seg.items():
+        q[sl] = norm_rope_heads(q[sl], w[s]["q_norm"], phi[sl], heads, shp.rms_eps)
+        k[sl] = norm_rope_heads(k[sl], w[s]["k_norm"], phi[sl], heads, shp.rms_eps)
+    stages["q"], stages["k"], stages["v"] = q, k, v
+    out_rows = np.arange(L) if rows is None else np.asarray(rows)
+    o = attention(q, k, v, heads, out_rows)
+    stages["attn"] = o
+    xo = x[out_rows].copy()
+    is_txt = out_rows < L_t
+    for s, mask in (("txt", is_txt), ("img", ~is_txt)):
+        if not mask.any():
+            continue
+        sh1, sc1, g1, sh2, sc2, g2 = mods[s]
+        xs = xo[mask] + g1 * linear(o[mask], w[s]["proj"])
+        h2 = ln_modulate(xs, sh2, sc2, shp.ln_eps)
+        a = gelu_tanh(linear(h2, w[s]["fc1"]))
+        xs = xs + g2 * linear(a, w[s]["fc2"])
+        xo[mask] = xs
+    if return_stages:
+        stages["mods"] = mods
+        return xo, stages
+    return xo
+
+
+def single_block(x, vec, ids, w, shp, rows: Optional[np.ndarray] = None,
+                 return_stages: bool = False):
+    """Single-stream block: one set of weights over the joint sequence.
+      shift, scale, gate = modulation(vec)
+      u = (LN(x) * (1 + scale) + shift) W_1^T + b_1 -> q | k | v | m
+      q, k = RMSNorm per head, then RoPE; O = attention(q, k, v)
+      x += gate * ([O | GELU(m)] W_2^T + b_2)
+    """
+    H, heads = shp.hidden, shp.heads
+    x = _f64(x)
+    L = x.shape[0]
+    phi = rope_angles(ids, shp.axes, shp.theta)
+    sh, sc, g = modulation(vec, w["mod"], 3)
+    h = ln_modulate(x, sh, sc, shp.ln_eps)
+    u = linear(h, w["linear1"])
+    q, k, v, m = u[:, :H], u[:, H:2 * H], u[:, 2 * H:3 * H], u[:, 3 * H:]
+    q = norm_rope_heads(q, w["q_norm"], phi, heads, shp.rms_eps)
+    k = norm_rope_heads(k, w["k_norm"], phi, heads, shp.rms_eps)
+    out_rows = np.arange(L) if rows is None else np.asarray(rows)
+    o = attention(q, k, v, heads, out_rows)
+    cat = np.concatenate([o, gelu_tanh(m[out_rows])], axis=1)
+    xo = x[out_rows] + g * linear(cat, w["linear2"])
+    if return_stages:
+        return xo, {"h": h, "u": u, "q": q, "k": k, "v": v, "attn": o, "mod": (sh, sc, g)}
+    return xo
+
+
+# --------------------------------------------------------------------------
+# denoise step
+# --------------------------------------------------------------------------
+def timestep_embedding(t: float, dim: int = 256, max_period: float = 10000.0,
+                       time_factor: float = 1000.0) -> np.ndarray:
+    """Sinusoidal embedding of a scalar: [cos(1000 t f_k) | sin(1000 t f_k)],
+    f_k = exp(-ln(max_period) k / (dim/2)), k < dim/2."""
+    half = dim // 2
+    f = np.exp(-math.log(max_period) * np.arange(half, dtype=np.float64) / half)
+    a = time_factor * float(t) * f
+    return np.concatenate([np.cos(a), np.sin(a)])
+
+
+def mlp_embedder(e, lins) -> np.ndarray:
+    """Linear(256 -> H), SiLU, Linear(H -> H)."""
+    return linear(silu(linear(e[None, :], lins[0])), lins[1])[0]
+
+
+def conditioning(t: float, guidance: float, m) -> np.ndarray:
+    """vec = MLP_t(emb(t)) + MLP_g(emb(guidance))."""
+    return mlp_embedder(timestep_embedding(t), m["time_in"]) + \
+        mlp_embedder(timestep_embedding(guidance), m["guid_in"])
+
+
+def euler(z, v, t_cur: float, t_next: float) -> np.ndarray:
+    """Flow-matching Euler update z <- z + (t_next - t_cur) v."""
+    return _f64(z) + (float(t_next) - float(t_cur)) * _f64(v)
+
+
+def velocity(z, txt, ids, m, shp, t_cur: float, guidance: float) -> np.ndarray:
+    """The denoiser's prediction v for latent z [L_i, C] and text states
+    txt [L_t, H]: embed, run the double then the single blocks, and apply the
+    final modulated LayerNorm and projection to the image rows."""
+    vec = conditioning(t_cur, guidance, m)
+    x = np.concatenate([_f64(txt), linear(z, m["img_in"])], axis=0)
+    for wd in m["double"]:
+        x = double_block(x, vec, ids, wd, shp)
+    for ws in m["single"]:
+        x = single_block(x, vec, ids, ws, shp)
+    sh, sc = modulation(vec, m["final_mod"], 2)
+    h = ln_modulate(x[shp.txt_len:], sh, sc, shp.ln_eps)
+    return linear(h, m["final_out"])
+
+
+def denoise_step(z, txt, ids, m, shp, t_cur: float, t_next: float, guidance: float):
+    """One flow-matching Euler step of the latent; returns (z_next, v)."""
+    v = velocity(z, txt, ids, m, shp, t_cur, guidance)
+    return euler(z, v, t_cur, t_next), v

@@ -1,0 +1,441 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Each test checks one oracle function against something other than itself: an
+invariant, a closed form, a special case that reduces to a textbook routine,
+brute force on tiny inputs, or the structure the Luminal blog reports. The
+cases are chosen so that a dropped term, a wrong sign, a swapped operand or a
+wrong index in the oracle fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.special import erf, expit
+
+import oracle as O
+from diffusion_transformer_image_mm_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(1234)
+
+
+# ---------------------------------------------------------------- softmax / attention
+def test_softmax_rows_sum_to_one():
+    s = rng.standard_normal((37, 53)) * 30
+    p = O.softmax_rows(s)
+    assert np.all(p >= 0)
+    assert np.max(np.abs(p.sum(axis=1) - 1.0)) <= 1e-12
+
+
+def test_attention_identical_keys_is_mean_of_values():
+    L, D = 29, 16
+    q = rng.standard_normal((L, D))
+    k = np.tile(rng.standard_normal((1, D)), (L, 1))
+    v = rng.standard_normal((L, D))
+    o = O.attention_head(q, k, v)
+    np.testing.assert_allclose(o, np.tile(v.mean(axis=0), (L, 1)), rtol=0, atol=1e-13)
+
+
+def test_attention_single_token_returns_v():
+    q, k, v = rng.standard_normal((3, 1, 8))
+    np.testing.assert_array_equal(O.attention_head(q, k, v), v)
+
+
+def _attention_brute(q, k, v):
+    """Attention by explicit Python loops and math.exp, no numpy reductions."""
+    L, D = len(q), len(q[0])
+    out = []
+    for i in range(L):
+        s = [sum(q[i][d] * k[j][d] for d in range(D)) / math.sqrt(D) for j in range(L)]
+        m = max(s)
+        e = [math.exp(x - m) for x in s]
+        z = math.fsum(e)
+        out.append([math.fsum(e[j] * v[j][d] for j in range(L)) / z for d in range(D)])
+    return np.array(out)
+
+
+@pytest.mark.parametrize("L,D", [(1, 4), (5, 8), (17, 6), (32, 16)])
+def test_attention_brute_force_tiny(L, D):
+    q, k, v = (rng.standard_normal((L, D)) * 2 for _ in range(3))
+    np.testing.assert_allclose(O.attention_head(q, k, v), _attention_brute(q.tolist(), k.tolist(), v.tolist()),
+                               rtol=0, atol=1e-12)
+
+
+def test_attention_sharp_key_selects_its_value():
+    L, D = 40, 16
+    k = rng.standard_normal((L, D))
+    v = rng.standard_normal((L, D))
+    q = 200.0 * k[7:8] / np.linalg.norm(k[7])  # query aligned with key 7 only
+    o = O.attention_head(q, k, v)
+    np.testing.assert_allclose(o[0], v[7], atol=1e-6)
+
+
+def test_softmax_large_logits_stay_finite():
+    # logits far past exp's fp64 range (e^710 overflows): the max-subtracted
+    # softmax stays finite and still sums to one
+    s = np.array([[1000.0, 999.0, -1000.0], [5000.0, 5000.0, 0.0]])
+    p = O.softmax_rows(s)
+    assert np.all(np.isfinite(p))
+    np.testing.assert_allclose(p[0], [1 / (1 + math.exp(-1)), math.exp(-1) / (1 + math.exp(-1)), 0], atol=1e-15)
+    np.testing.assert_allclose(p[1], [0.5, 0.5, 0], atol=1e-15)
+
+
+def test_attention_multihead_heads_independent_and_rows_subset():
+    L, heads, D = 23, 3, 8
+    q, k, v = (rng.standard_normal((L, heads * D)) for _ in range(3))
+    full = O.attention(q, k, v, heads)
+    for h in range(heads):
+        sl = slice(h * D, (h + 1) * D)
+        np.testing.assert_allclose(full[:, sl], _attention_brute(q[:, sl].tolist(), k[:, sl].tolist(),
+                                                                 v[:, sl].tolist()), atol=1e-12)
+    rows = np.array([0, 5, 22])
+    np.testing.assert_allclose(O.attention(q, k, v, heads, rows), full[rows], atol=1e-13)
+
+
+def test_attention_permutation_equivariant():
+    L, D = 31, 8
+    q, k, v = (rng.standard_normal((L, D)) for _ in range(3))
+    perm = rng.permutation(L)
+    o = O.attention_head(q, k, v)
+    op = O.attention_head(q[perm], k[perm], v[perm])
+    np.testing.assert_allclose(op, o[perm], atol=1e-13)
+
+
+# ---------------------------------------------------------------- norms
+def test_layer_norm_closed_form_moments():
+    x = rng.standard_normal((11, 64)) * np.array([1e-4, 1e-3, 1e-2, 0.1, 1, 3, 10, 1e2, 1, 1, 1])[:, None] + 5
+    eps = 1e-6
+    y = O.layer_norm(x, eps)
+    var = x.var(axis=1)
+    np.testing.assert_allclose(y.mean(axis=1), 0, atol=1e-9)
+    # the biased variance of the output is var / (var + eps): catches a dropped
+    # eps, an unbiased (n - 1) divisor or a missing mean subtraction
+    np.testing.assert_allclose((y * y).mean(axis=1), var / (var + eps), rtol=1e-10)
+
+
+def test_layer_norm_two_values_closed_form():
+    # a row of +a and -a (mean 0, var a^2): LN gives +-a / sqrt(a^2 + eps)
+    a, eps = 0.003, 1e-6
+    x = np.array([[a, -a] * 8])
+    y = O.layer_norm(x, eps)
+    np.testing.assert_allclose(y[0, 0], a / math.sqrt(a * a + eps), rtol=1e-14)
+    assert y[0, 1] == -y[0, 0]
+
+
+def test_modulate_identity_scale_and_shift():
+    x = rng.standard_normal((5, 32))
+    y = O.layer_norm(x, 1e-6)
+    z = np.zeros(32)
+    np.testing.assert_array_equal(O.modulate(y, z, z), y)
+    c = np.full(32, 0.75)
+    np.testing.assert_allclose(O.modulate(y, z, c), 1.75 * y, rtol=1e-15)      # (1 + scale)
+    np.testing.assert_allclose(O.modulate(y, c, z).mean(axis=1), 0.75, atol=1e-12)  # + shift
+    idx = np.arange(32.0)
+    np.testing.assert_allclose(O.modulate(y, z, idx), y * (1 + idx), rtol=1e-15)  # per column
+
+
+def test_rms_norm_closed_forms():
+    eps = 1e-6
+    u = rng.standard_normal((7, 64)) * 3
+    y = O.rms_norm(u, np.ones(64), eps)
+    ms = (u * u).mean(axis=1)
+    np.testing.assert_allclose((y * y).mean(axis=1), ms / (ms + eps), rtol=1e-12)
+    # one-hot input c e_i: output g_i c / sqrt(c^2 / D + eps) at i, zero elsewhere
+    g = np.linspace(0.5, 1.5, 64)
+    for i in (0, 17, 63):
+        e = np.zeros((1, 64)); e[0, i] = 2.5
+        y = O.rms_norm(e, g, eps)
+        want = np.zeros(64); want[i] = g[i] * 2.5 / math.sqrt(2.5 ** 2 / 64 + eps)
+        np.testing.assert_allclose(y[0], want, rtol=1e-14, atol=0)
+
+
+# ---------------------------------------------------------------- rope
+AXES = (16, 56, 56)
+
+
+def _ids(L, hi=90):
+    return rng.integers(0, hi, size=(L, 3)).astype(np.int32)
+
+
+def test_rope_zero_position_is_identity():
+    u = rng.standard_normal((4, 128))
+    phi = O.rope_angles(np.zeros((4, 3), np.int32), AXES, 1e4)
+    np.testing.assert_array_equal(O.apply_rope(u, phi), u)
+
+
+def test_rope_preserves_pair_and_vector_norms():
+    u = rng.standard_normal((20, 128))
+    r = O.apply_rope(u, O.rope_angles(_ids(20), AXES, 1e4))
+    pair = lambda a: a[:, 0::2] ** 2 + a[:, 1::2] ** 2
+    np.testing.assert_allclose(pair(r), pair(u), rtol=1e-12)
+    np.testing.assert_allclose(np.linalg.norm(r, axis=1), np.linalg.norm(u, axis=1), rtol=1e-13)
+
+
+def test_rope_relative_position_property():
+    # <R_m q, R_n k> = <q, R_(n-m) k> for every axis
+    q, k = rng.standard_normal((2, 1, 128))
+    for m, n in [((0, 3, 5), (0, 7, 2)), ((2, 0, 40), (5, 63, 1))]:
+        pm = O.rope_angles(np.array([m], np.int32), AXES, 1e4)
+        pn = O.rope_angles(np.array([n], np.int32), AXES, 1e4)
+        pd = O.rope_angles(np.array([np.subtract(n, m)], np.int32), AXES, 1e4)
+        lhs = (O.apply_rope(q, pm) * O.apply_rope(k, pn)).sum()
+        rhs = (q * O.apply_rope(k, pd)).sum()
+        assert abs(lhs - rhs) < 1e-12
+
+
+def test_rope_axis_segments_and_unit_frequency():
+    # the first pair of each axis turns by exactly its position (frequency 1);
+    # the t axis owns pairs [0, 8), h [8, 36), w [36, 64)
+    ids = np.array([[3, 5, 7]], np.int32)
+    phi = O.rope_angles(ids, AXES, 1e4)[0]
+    assert phi[0] == 3 and phi[8] == 5 and phi[36] == 7
+    only_h = O.rope_angles(np.array([[0, 5, 0]], np.int32), AXES, 1e4)[0]
+    assert np.all(only_h[:8] == 0) and np.all(only_h[36:] == 0) and np.all(only_h[8:36] > 0)
+    # frequencies fall geometrically within an axis: ratio theta^(-2/d_a)
+    np.testing.assert_allclose(only_h[9:36] / only_h[8:35], 1e4 ** (-2 / 56), rtol=1e-13)
+    # unit vector e_0 at t-position 1 turns to (cos 1, sin 1)
+    e = np.zeros((1, 128)); e[0, 0] = 1
+    r = O.apply_rope(e, O.rope_angles(np.array([[1, 0, 0]], np.int32), AXES, 1e4))
+    np.testing.assert_allclose(r[0, :2], [math.cos(1), math.sin(1)], rtol=1e-15)
+
+
+# ---------------------------------------------------------------- elementwise
+def test_gelu_against_erf_form_and_identities():
+    x = np.linspace(-8, 8, 2001)
+    g = O.gelu_tanh(x)
+    exact = 0.5 * x * (1 + erf(x / math.sqrt(2)))
+    assert np.max(np.abs(g - exact)) < 5e-4  # the tanh form is within 4.7e-4 of the erf form
+    np.testing.assert_allclose(g - O.gelu_tanh(-x), x, atol=1e-13)  # GELU(x) - GELU(-x) = x
+    assert O.gelu_tanh(np.array([0.0]))[0] == 0
+    assert abs(O.gelu_tanh(np.array([12.0]))[0] - 12.0) < 1e-12
+
+
+def test_silu_against_logistic():
+    x = np.linspace(-30, 30, 601)
+    np.testing.assert_allclose(O.silu(x), x * expit(x), rtol=1e-14, atol=1e-300)
+    np.testing.assert_allclose(O.silu(x) - O.silu(-x), x, atol=1e-12)
+
+
+# ---------------------------------------------------------------- linear
+def test_linear_brute_force_tiny_rectangular():
+    x = rng.standard_normal((3, 5))
+    lin = synth.Linear(rng.standard_normal((4, 5)), rng.standard_normal(4))
+    y = O.linear(x, lin)
+    want = [[math.fsum([x[i][k] * lin.w[n][k] for k in range(5)]) + lin.b[n] for n in range(4)] for i in range(3)]
+    np.testing.assert_allclose(y, want, rtol=0, atol=1e-14)
+
+
+def test_linear_int8_is_scale_after_integer_product():
+    q = rng.integers(-127, 128, size=(6, 9)).astype(np.int8)
+    s = rng.uniform(1e-4, 1e-2, 6).astype(np.float32)
+    b = rng.standard_normal(6)
+    x = rng.standard_normal((4, 9))
+    lin = synth.Linear(None, b, q, s)
+    y = O.linear(x, lin)
+    want = [[math.fsum([x[i][k] * int(q[n][k]) for k in range(9)]) * float(s[n]) + b[n] for n in range(6)]
+            for i in range(4)]
+    np.testing.assert_allclose(y, want, rtol=1e-14, atol=1e-15)
+
+
+# ---------------------------------------------------------------- time embedding / euler
+def test_timestep_embedding_closed_forms():
+    e0 = O.timestep_embedding(0.0)
+    np.testing.assert_array_equal(e0, np.concatenate([np.ones(128), np.zeros(128)]))
+    t = 0.37
+    e = O.timestep_embedding(t)
+    assert e.shape == (256,)
+    assert abs(e[0] - math.cos(370.0)) < 1e-12 and abs(e[128] - math.sin(370.0)) < 1e-12
+    # lowest frequency: 1e4^(-127/128)
+    f = 1e4 ** (-127 / 128)
+    assert abs(e[127] - math.cos(370.0 * f)) < 1e-12 and abs(e[255] - math.sin(370.0 * f)) < 1e-12
+    np.testing.assert_allclose(e[:128] ** 2 + e[128:] ** 2, 1.0, rtol=1e-14)
+
+
+def test_euler_closed_form_multi_step():
+    z0 = rng.standard_normal((10, 4))
+    c = rng.standard_normal(4)
+    ts = synth.sigma_schedule(28)
+    z = z0
+    for i in range(28):
+        z = O.euler(z, np.tile(c, (10, 1)), ts[i], ts[i + 1])
+    np.testing.assert_allclose(z, z0 - c, atol=1e-13)
+
+
+# ---------------------------------------------------------------- blocks
+TINY = synth.custom_shape("pin-tiny", 900, 64, 2, 128, 8, (4, 6))
+
+
+def _zero(lin, rows=None):
+    w = lin.w.copy(); b = lin.b.copy()
+    if rows is None:
+        w[:] = 0; b[:] = 0
+    else:
+        w[rows] = 0; b[rows] = 0
+    return synth.Linear(w, b)
+
+
+def test_double_block_zero_gate_identity():
+    d = synth.block_inputs(TINY, "double")
+    H = TINY.hidden
+    w = d["w"]
+    gates = np.r_[2 * H:3 * H, 5 * H:6 * H]
+    for s in ("txt", "img"):
+        w[s]["mod"] = _zero(w[s]["mod"], gates)
+    out = O.double_block(d["x"], d["vec"], d["ids"], w, TINY)
+    np.testing.assert_array_equal(out, d["x"].astype(np.float64))
+
+
+def test_double_block_constant_branch_closed_form():
+    """With zero qkv and fc1 weights (biases kept), every key and value is the
+    bias, attention returns the v-bias, and each stream's update is
+    gate1 * (W_o b_v + b_o) + gate2 * (W_2 GELU(b_1) + b_2): a closed form that
+    pins the gate chunks, the [q|k|v] split and the proj / fc2 wiring."""
+    d = synth.block_inputs(TINY, "double", variant=1)
+    H = TINY.hidden
+    w = d["w"]
+    x = d["x"].astype(np.float64)
+    want = x.copy()
+    silu_vec = d["vec"] / (1 + np.exp(-d["vec"].astype(np.float64)))
+    for s, sl in (("txt", slice(0, TINY.txt_len)), ("img", slice(TINY.txt_len, None))):
+        w[s]["qkv"] = synth.Linear(np.zeros_like(w[s]["qkv"].w), w[s]["qkv"].b)
+        w[s]["fc1"] = synth.Linear(np.zeros_like(w[s]["fc1"].w), w[s]["fc1"].b)
+    # both streams get one v-bias, so every value is that bias and attention
+    # returns it whatever the (RoPE-dependent) attention weights are
+    bq = w["img"]["qkv"].b.copy(); bq[2 * H:] = w["txt"]["qkv"].b[2 * H:]
+    w["img"]["qkv"] = synth.Linear(w["img"]["qkv"].w, bq)
+    o = w["txt"]["qkv"].b[2 * H:].astype(np.float64)
+    for s, sl in (("txt", slice(0, TINY.txt_len)), ("img", slice(TINY.txt_len, None))):
+        m = w[s]["mod"].w.astype(np.float64) @ silu_vec + w[s]["mod"].b
+        g1, g2 = m[2 * H:3 * H], m[5 * H:6 * H]
+        c1 = w[s]["proj"].w.astype(np.float64) @ o + w[s]["proj"].b
+        b1 = w[s]["fc1"].b.astype(np.float64)
+        gb1 = 0.5 * b1 * (1 + erf(b1 / math.sqrt(2)))  # erf GELU, tanh form within 5e-4
+        c2 = w[s]["fc2"].w.astype(np.float64) @ gb1 + w[s]["fc2"].b
+        want[sl] += g1 * c1 + g2 * c2
+    out = O.double_block(x, d["vec"], d["ids"], w, TINY)
+    # the only slack is the gap between the tanh and erf forms of GELU, at most
+    # 4.8e-4 per element, carried through |W_2| and |gate2|
+    for s, sl in (("txt", slice(0, TINY.txt_len)), ("img", slice(TINY.txt_len, None))):
+        m = w[s]["mod"].w.astype(np.float64) @ silu_vec + w[s]["mod"].b
+        bound = np.abs(m[5 * H:6 * H]) * 4.8e-4 * np.abs(w[s]["fc2"].w.astype(np.float64)).sum(axis=1) + 1e-12
+        assert np.all(np.abs(out[sl] - want[sl]) <= bound[None, :])
+
+
+def test_double_block_norm_scales_wired_per_tensor_and_stream():
+    """RoPE keeps each (2j, 2j+1) pair's norm, so the pair norms of the block's
+    q and k equal those of the RMSNorm (already pinned) of the raw projections
+    with that tensor's and that stream's own scale."""
+    d = synth.block_inputs(TINY, "double", variant=4)
+    H, D = TINY.hidden, TINY.head_dim
+    _, st = O.double_block(d["x"], d["vec"], d["ids"], d["w"], TINY, return_stages=True)
+    pair = lambda a: a[:, 0::2] ** 2 + a[:, 1::2] ** 2
+    for s, sl in (("txt", slice(0, TINY.txt_len)), ("img", slice(TINY.txt_len, None))):
+        raw = st[f"qkv_{s}"]
+        for name, off in (("q", 0), ("k", H)):
+            for h in range(TINY.heads):
+                cols = slice(h * D, (h + 1) * D)
+                want = O.rms_norm(raw[:, off + h * D: off + (h + 1) * D], d["w"][s][f"{name}_norm"], TINY.rms_eps)
+                np.testing.assert_allclose(pair(st[name][sl][:, cols]), pair(want), rtol=1e-10, atol=1e-14)
+
+
+def test_double_block_within_stream_permutation_equivariance():
+    """Permuting tokens inside each stream together with their position ids
+    permutes the output the same way (attention has no mask and RoPE travels
+    with the ids)."""
+    d = synth.block_inputs(TINY, "double", variant=2)
+    L_t, L = TINY.txt_len, TINY.seq_len
+    perm = np.r_[rng.permutation(L_t), L_t + rng.permutation(L - L_t)]
+    out = O.double_block(d["x"], d["vec"], d["ids"], d["w"], TINY)
+    outp = O.double_block(d["x"][perm], d["vec"], d["ids"][perm], d["w"], TINY)
+    np.testing.assert_allclose(outp, out[perm], atol=1e-11)
+    # and it is not invariant to moving a token's position id alone
+    ids2 = d["ids"].copy(); ids2[[L_t, L_t + 1]] = ids2[[L_t + 1, L_t]]
+    out2 = O.double_block(d["x"], d["vec"], ids2, d["w"], TINY)
+    assert np.max(np.abs(out2 - out)) > 1e-6
+
+
+def test_double_block_rows_subset_matches_full():
+    d = synth.block_inputs(TINY, "double", variant=3)
+    out = O.double_block(d["x"], d["vec"], d["ids"], d["w"], TINY)
+    rows = np.array([0, 3, TINY.txt_len, TINY.seq_len - 1])
+    np.testing.assert_allclose(O.double_block(d["x"], d["vec"], d["ids"], d["w"], TINY, rows=rows), out[rows],
+                               atol=1e-12)
+
+
+def test_single_block_zero_gate_and_constant_branch():
+    d = synth.block_inputs(TINY, "single")
+    H, M = TINY.hidden, TINY.mlp
+    w = d["w"]
+    w0 = dict(w); w0["mod"] = _zero(w["mod"], np.r_[2 * H:3 * H])
+    np.testing.assert_array_equal(O.single_block(d["x"], d["vec"], d["ids"], w0, TINY), d["x"].astype(np.float64))
+    # zero linear1 weight: q, k, v, m are the bias chunks; attention returns b_v
+    w1 = dict(w); w1["linear1"] = synth.Linear(np.zeros_like(w["linear1"].w), w["linear1"].b)
+    b = w["linear1"].b.astype(np.float64)
+    bm = b[3 * H:]
+    cat = np.concatenate([b[2 * H:3 * H], 0.5 * bm * (1 + np.tanh(math.sqrt(2 / math.pi) * (bm + 0.044715 * bm ** 3)))])
+    v = d["vec"].astype(np.float64)
+    mod = w["mod"].w.astype(np.float64) @ (v * expit(v)) + w["mod"].b
+    gate = mod[2 * H:]
+    want = d["x"] + gate * (w["linear2"].w.astype(np.float64) @ cat + w["linear2"].b)
+    np.testing.assert_allclose(O.single_block(d["x"], d["vec"], d["ids"], w1, TINY), want, atol=1e-11)
+
+
+def test_single_block_permutation_equivariance():
+    d = synth.block_inputs(TINY, "single", variant=1)
+    perm = rng.permutation(TINY.seq_len)
+    out = O.single_block(d["x"], d["vec"], d["ids"], d["w"], TINY)
+    outp = O.single_block(d["x"][perm], d["vec"], d["ids"][perm], d["w"], TINY)
+    np.testing.assert_allclose(outp, out[perm], atol=1e-11)
+
+
+def test_denoise_step_closed_form_zero_final_weight():
+    shp = synth.custom_shape("pin-step", 901, 64, 2, 128, 8, (4, 4), n_double=1, n_single=1, in_channels=16)
+    m = synth.model_weights(shp, int8=False)
+    c = rng.standard_normal(16)
+    m["final_out"] = synth.Linear(np.zeros((16, 64)), c)
+    s = synth.step_inputs(shp)
+    z1, v = O.denoise_step(s["z"], s["txt"], s["ids"], m, shp, 1.0, 1.0 - 1 / 28, 3.5)
+    np.testing.assert_allclose(v, np.tile(c, (shp.img_len, 1)), atol=1e-14)
+    np.testing.assert_allclose(z1, s["z"] - c / 28, atol=1e-14)
+
+
+def test_block_structure_matches_reported_launch_counts():
+    """A Klein-structured step (8 double + 24 single blocks and a final layer)
+    runs exactly the per-step fused-kernel counts the Luminal blog reports."""
+    with open(os.path.join(GOLDEN, "klein_structure.json")) as f:
+        g = json.load(f)
+    shp = synth.custom_shape("pin-klein", 902, 64, 2, 64, 4, (2, 2), n_double=g["double_blocks"],
+                             n_single=g["single_blocks"], in_channels=8)
+    m = synth.model_weights(shp, int8=False)
+    s = synth.step_inputs(shp)
+    O.SITE_COUNTS.clear()
+    O.velocity(s["z"], s["txt"], s["ids"], m, shp, 0.5, 3.5)
+    assert O.SITE_COUNTS["rmsnorm_rope"] == g["rmsnorm_rope_per_step"]
+    assert O.SITE_COUNTS["ln_modulate"] == g["ln_modulate_per_step"]
+    assert O.SITE_COUNTS["attention"] == g["attention_sites_per_step"]
+
+
+def test_int8_step_matches_dequantised_bf16_step():
+    """An int8 model and the same model with W := diag(s) Q in float give the
+    same velocity (the oracle dequantises exactly in fp64)."""
+    shp = synth.custom_shape("pin-int8", 903, 64, 2, 128, 8, (4, 4), n_double=1, n_single=1, in_channels=16)
+    m8 = synth.model_weights(shp, int8=True)
+
+    def deq(l):
+        return synth.Linear(l.s.astype(np.float64)[:, None] * l.q.astype(np.float64), l.b)
+
+    def walk(o):
+        if isinstance(o, synth.Linear):
+            return deq(o)
+        if isinstance(o, dict):
+            return {k: walk(v) for k, v in o.items()}
+        if isinstance(o, list):
+            return [walk(v) for v in o]
+        return o
+    mf = walk(m8)
+    s = synth.step_inputs(shp)
+    v8 = O.velocity(s["z"], s["txt"], s["ids"], m8, shp, 0.8, 3.5)
+    vf = O.velocity(s["z"], s["txt"], s["ids"], mf, shp, 0.8, 3.5)
+    np.testing.assert_array_equal(v8, vf)
