@@ -1,0 +1,228 @@
+"""Benchmark of the MM-DiT block hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-step] [--no-cpu]
+
+Workload: the FLUX.1-dev-shaped double-stream block at 1024x1024 (hidden
+3072, 24 heads x 128, MLP 12288, 512 text + 4096 image tokens, batch 1),
+bf16 weights N(0, 0.02), inputs N(0, 1), seeded and synthetic. A timed
+"step" is one mmdit_block_forward call (modulation, LN+modulate, QKV,
+QK-RMSNorm+RoPE, joint attention, gated projections, GELU MLP); inputs are
+resident in HBM before the timed region starts.
+
+The JSON line also carries: ms per full FLUX.1-dev-shaped denoise step (19
+double + 38 single blocks + embedders + final layer + Euler update) with bf16
+and with int8 weight-only linears; the roofline of the dominant kernel (the
+MLP-in GEMM, timed live with events on the launch stream); and the CPU
+oracle's throughput on a bounded sample of the same block.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+
+
+def block_flops(shp) -> float:
+    """Algorithmic FLOPs of one double block: 2*M*N*K per projection (both
+    streams) plus 4*L^2*H for QK^T and PV; modulation GEMVs included."""
+    L, H, M = shp.seq_len, shp.hidden, shp.mlp
+    lin = 2 * L * H * (3 * H + H + M + M)
+    attn = 4 * L * L * H
+    mod = 2 * 2 * 6 * H * H
+    return float(lin + attn + mod)
+
+
+def single_flops(shp) -> float:
+    L, H, M = shp.seq_len, shp.hidden, shp.mlp
+    return float(2 * L * H * (3 * H + M) + 2 * L * (H + M) * H + 4 * L * L * H + 2 * 3 * H * H)
+
+
+def step_flops(shp) -> float:
+    L, H, C = shp.seq_len, shp.hidden, shp.in_channels
+    extra = 2 * shp.img_len * C * H * 2 + 2 * 2 * (256 * H + H * H) + 2 * 2 * H * H
+    return shp.n_double * block_flops(shp) + shp.n_single * single_flops(shp) + extra
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-step", action="store_true", help="skip the full denoise-step timing")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=512)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the sharded path is described in the design notes, not built)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from diffusion_transformer_image_mm_amd import binding as B
+    from diffusion_transformer_image_mm_amd import synth
+    from diffusion_transformer_image_mm_amd.device import DeviceArena, TimingModel, dims_for
+
+    def log(*a):
+        print(*a, file=sys.stderr, flush=True)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    shp = synth.FLUX_DOUBLE
+
+    # ------------------------------------------------------------ block
+    log("bench: generating FLUX double-block inputs")
+    inp = synth.block_inputs(shp, "double")
+    A = DeviceArena()
+    d = dims_for(shp)
+    rope = A.empty_f32(shp.seq_len, shp.head_dim // 2, 2)
+    B.check(B.mmdit_rope_table(d, A.i32(inp["ids"]), rope, stream), "rope")
+    w = A.double_weights(inp["w"])
+    vec = A.f32(inp["vec"])
+    x0 = A.f32(inp["x"])
+    x = A.empty_f32(shp.seq_len, shp.hidden)
+    ws = A.workspace(B.mmdit_workspace_bytes(d, B.MMDIT_WS_DOUBLE))
+    torch.cuda.synchronize()
+
+    def block_call():
+        B.check(B.mmdit_block_forward(d, w, vec, rope, x0, x, ws, ws.numel(), stream), "block")
+
+    log(f"bench: block warmup {args.warmup}, timed {args.steps}")
+    for _ in range(args.warmup):
+        block_call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        block_call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+    ms_block = float(np.median(per))
+    flops = block_flops(shp)
+    tflops = flops / (ms_block * 1e-3) / 1e12
+    log(f"bench: block median {ms_block:.3f} ms p10 {np.percentile(per, 10):.3f} p90 {np.percentile(per, 90):.3f} "
+        f"-> {tflops:.1f} TFLOP/s; wall {wall * 1e3 / args.steps:.3f} ms/iter")
+
+    # ------------------------------------------------------------ dominant kernel: MLP-in GEMM
+    L, H, M = shp.seq_len, shp.hidden, shp.mlp
+    a_in = A.empty_bf16(L, H)
+    a_in.zero_()
+    a_out = A.empty_bf16(L, M)
+    g = B.mmdit_gemm(m=L, n=M, k=H, weight_dtype=B.MMDIT_BF16, a=a_in.data_ptr(), lda=H,
+                     w=w.img.fc1, epilogue=B.MMDIT_EPI_BIAS_GELU, out=a_out.data_ptr(), ldo=M)
+    for _ in range(3):
+        B.check(B.mmdit_k_gemm(g, stream), "gemm")
+    n_g = 20
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    g0.record(stream)
+    for _ in range(n_g):
+        B.check(B.mmdit_k_gemm(g, stream), "gemm")
+    g1.record(stream)
+    torch.cuda.synchronize()
+    ms_gemm = g0.elapsed_time(g1) / n_g
+    gemm_flops = 2.0 * L * M * H
+    gemm_tflops = gemm_flops / (ms_gemm * 1e-3) / 1e12
+    log(f"bench: fc1 GEMM {L}x{M}x{H} {ms_gemm * 1e3:.1f} us -> {gemm_tflops:.1f} TFLOP/s")
+
+    result = {
+        "metric": "MM-DiT block TFLOP/s + ms/denoise step (bf16, FLUX-shaped 1024^2, 1 GPU)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_block, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) inputs)",
+        "config": {"workload": "flux-dev double-stream block 1024px: H3072 24x128 MLP12288 L512+4096 batch1",
+                   "block_gflop": round(flops / 1e9, 1), "ms_p10": round(float(np.percentile(per, 10)), 4),
+                   "ms_p90": round(float(np.percentile(per, 90)), 4),
+                   "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4)},
+        "roofline": {"kernel": "gemm_kernel<bf16, BIAS_GELU> (MLP-in, 4608x12288x3072)", "bound": "mfma",
+                     "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "avg_us": round(ms_gemm * 1e3, 2)},
+    }
+
+    # ------------------------------------------------------------ full denoise step
+    if not args.no_step:
+        del A
+        torch.cuda.empty_cache()
+        for int8 in (False, True):
+            sshp = synth.FLUX_STEP
+            log(f"bench: generating full FLUX-shaped step weights on the device (int8={int8})")
+            tm = TimingModel(sshp, int8=int8, seed=42)
+            mm = tm.model
+            S = DeviceArena()
+            sd = dims_for(sshp, int8)
+            srope = S.empty_f32(sshp.seq_len, sshp.head_dim // 2, 2)
+            B.check(B.mmdit_rope_table(sd, S.i32(synth.position_ids(sshp)), srope, stream), "rope")
+            st = synth.step_inputs(sshp)
+            z = S.f32(st["z"])
+            txt = S.f32(st["txt"])
+            sws = S.workspace(B.mmdit_workspace_bytes(sd, B.MMDIT_WS_STEP))
+            ts = synth.sigma_schedule(28)
+            torch.cuda.synchronize()
+            for i in range(2):
+                B.check(B.mmdit_denoise_step(sd, mm, z, txt, srope, ts[i], ts[i + 1], 3.5, sws, sws.numel(), stream))
+            torch.cuda.synchronize()
+            n_steps = 4
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            for i in range(n_steps):
+                B.check(B.mmdit_denoise_step(sd, mm, z, txt, srope, ts[i], ts[i + 1], 3.5, sws, sws.numel(), stream))
+            s1.record(stream)
+            torch.cuda.synchronize()
+            ms_step = s0.elapsed_time(s1) / n_steps
+            key = "int8" if int8 else "bf16"
+            result[f"ms_per_denoise_step_{key}"] = round(ms_step, 3)
+            result[f"denoise_step_tflops_{key}"] = round(step_flops(sshp) / (ms_step * 1e-3) / 1e12, 2)
+            log(f"bench: denoise step ({key}) {ms_step:.2f} ms -> "
+                f"{result[f'denoise_step_tflops_{key}']:.1f} TFLOP/s; 28 steps = {28 * ms_step / 1e3:.2f} s")
+            del S, mm, tm
+            torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ CPU oracle baseline
+    if not args.no_cpu:
+        import oracle as O
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        rng = np.random.default_rng(7)
+        rows = np.sort(rng.choice(shp.seq_len, size=min(args.cpu_rows, shp.seq_len), replace=False))
+        log(f"bench: CPU oracle on {len(rows)} sampled rows of the block ({threads} BLAS threads)")
+        c0 = time.perf_counter()
+        O.double_block(inp["x"], inp["vec"], inp["ids"], inp["w"], shp, rows=rows)
+        cdt = time.perf_counter() - c0
+        r = len(rows)
+        sample_flops = (2 * L * H * 3 * H + 4 * r * L * H + 2 * r * H * (H + 2 * M) + 2 * 2 * 6 * H * H)
+        result["cpu_baseline"] = {
+            "value": round(sample_flops / cdt / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"numpy fp64 oracle of the FLUX double block: QKV for all {L} tokens, attention, "
+                      f"projections and MLP for {r} sampled rows; {sample_flops / 1e9:.0f} GFLOP in {cdt:.1f} s",
+            "seconds": round(cdt, 2)}
+        log(f"bench: CPU oracle {cdt:.1f} s")
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

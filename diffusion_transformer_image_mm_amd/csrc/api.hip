@@ -1,0 +1,576 @@
+// C ABI of libmmdit.so: argument validation, workspace carving and the
+// orchestration of the block / step kernels on one stream.
+#include <cmath>
+
+#include "common.h"
+
+using namespace mmdit;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validate the sizes of a model. Returns MMDIT_OK or the status.
+int check_dims(const mmdit_dims* d) {
+    if (!d) return MMDIT_E_NULL;
+    if (d->head_dim != 64 && d->head_dim != 128) return MMDIT_E_SHAPE;
+    if (d->heads < 1 || d->hidden != d->heads * d->head_dim) return MMDIT_E_SHAPE;
+    if (d->hidden % 64 != 0 || d->hidden > 4096) return MMDIT_E_SHAPE;
+    if (d->mlp_hidden < 64 || d->mlp_hidden % 64 != 0) return MMDIT_E_SHAPE;
+    if (d->txt_len < 1 || d->img_len < 1) return MMDIT_E_SHAPE;
+    if ((int64_t)d->txt_len + d->img_len > (1 << 20)) return MMDIT_E_SHAPE;
+    int sum = 0;
+    for (int a = 0; a < 3; ++a) {
+        if (d->rope_axes[a] < 0 || d->rope_axes[a] % 2 != 0) return MMDIT_E_SHAPE;
+        sum += d->rope_axes[a];
+    }
+    if (sum != d->head_dim) return MMDIT_E_SHAPE;
+    if (!(d->ln_eps > 0.f) || !(d->rms_eps > 0.f) || !(d->rope_theta > 1.f)) return MMDIT_E_SHAPE;
+    if (d->weight_dtype != MMDIT_BF16 && d->weight_dtype != MMDIT_INT8) return MMDIT_E_DTYPE;
+    return MMDIT_OK;
+}
+
+int check_ptr(const void* p) {
+    if (!p) return MMDIT_E_NULL;
+    if (!aligned16(p)) return MMDIT_E_ALIGN;
+    return MMDIT_OK;
+}
+
+int check_linear(const mmdit_linear& l, int dtype) {
+    int st;
+    if ((st = check_ptr(l.w)) != MMDIT_OK) return st;
+    if ((st = check_ptr(l.bias)) != MMDIT_OK) return st;
+    if (dtype == MMDIT_INT8) {
+        if (!l.scale) return MMDIT_E_DTYPE;
+        if (!aligned16(l.scale)) return MMDIT_E_ALIGN;
+    }
+    return MMDIT_OK;
+}
+
+#define MMDIT_TRY(expr)               \
+    do {                              \
+        int _st = (expr);             \
+        if (_st != MMDIT_OK) return _st; \
+    } while (0)
+
+#define MMDIT_HIP(expr)                          \
+    do {                                         \
+        if ((expr) != hipSuccess) return MMDIT_E_HIP; \
+    } while (0)
+
+int stream_weights_ok(const mmdit_stream_weights& s, int dt) {
+    MMDIT_TRY(check_linear(s.mod, dt));
+    MMDIT_TRY(check_linear(s.qkv, dt));
+    MMDIT_TRY(check_linear(s.proj, dt));
+    MMDIT_TRY(check_linear(s.fc1, dt));
+    MMDIT_TRY(check_linear(s.fc2, dt));
+    MMDIT_TRY(check_ptr(s.q_norm));
+    MMDIT_TRY(check_ptr(s.k_norm));
+    return MMDIT_OK;
+}
+
+int double_weights_ok(const mmdit_double_weights* w, int dt) {
+    if (!w) return MMDIT_E_NULL;
+    MMDIT_TRY(stream_weights_ok(w->txt, dt));
+    MMDIT_TRY(stream_weights_ok(w->img, dt));
+    return MMDIT_OK;
+}
+
+int single_weights_ok(const mmdit_single_weights* w, int dt) {
+    if (!w) return MMDIT_E_NULL;
+    MMDIT_TRY(check_linear(w->mod, dt));
+    MMDIT_TRY(check_linear(w->linear1, dt));
+    MMDIT_TRY(check_linear(w->linear2, dt));
+    MMDIT_TRY(check_ptr(w->q_norm));
+    MMDIT_TRY(check_ptr(w->k_norm));
+    return MMDIT_OK;
+}
+
+// ---------------------------------------------------------------- workspace
+int seq_len(const mmdit_dims* d) { return d->txt_len + d->img_len; }
+int padded_len(const mmdit_dims* d) { return (seq_len(d) + 127) / 128 * 128; }
+
+struct Carver {
+    char* base;
+    size_t off = 0;
+    explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+    template <class T>
+    T* take(size_t count) {
+        T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+        off = align_up(off + count * sizeof(T));
+        return p;
+    }
+};
+
+struct DoubleWs {
+    float* mod;      // [2][6H] fp32
+    uint16_t* h;     // [L, H] fp16 (LayerNorm + modulate output)
+    uint16_t* qkv;   // [L, 3H] bf16
+    uint16_t* q;     // [heads, l_pad, D] bf16
+    uint16_t* k;
+    uint16_t* vt;    // [heads, D, l_pad] bf16
+    uint16_t* o;     // [L, H] fp16 (attention output)
+    uint16_t* a;     // [L, M] fp16 (GELU hidden)
+};
+
+DoubleWs carve_double(const mmdit_dims* d, Carver& c) {
+    const size_t L = seq_len(d), H = d->hidden, M = d->mlp_hidden, LP = padded_len(d);
+    DoubleWs w;
+    w.mod = c.take<float>(12 * H);
+    w.h = c.take<uint16_t>(L * H);
+    w.qkv = c.take<uint16_t>(L * 3 * H);
+    w.q = c.take<uint16_t>(LP * H);
+    w.k = c.take<uint16_t>(LP * H);
+    w.vt = c.take<uint16_t>(LP * H);
+    w.o = c.take<uint16_t>(L * H);
+    w.a = c.take<uint16_t>(L * M);
+    return w;
+}
+
+struct SingleWs {
+    float* mod;      // [3H] fp32
+    uint16_t* h;     // [L, H] fp16
+    uint16_t* qkv;   // [L, 3H] bf16
+    uint16_t* q;
+    uint16_t* k;
+    uint16_t* vt;
+    uint16_t* cat;   // [L, H + M] fp16: [attention | GELU(mlp)]
+};
+
+SingleWs carve_single(const mmdit_dims* d, Carver& c) {
+    const size_t L = seq_len(d), H = d->hidden, M = d->mlp_hidden, LP = padded_len(d);
+    SingleWs w;
+    w.mod = c.take<float>(3 * H);
+    w.h = c.take<uint16_t>(L * H);
+    w.qkv = c.take<uint16_t>(L * 3 * H);
+    w.q = c.take<uint16_t>(LP * H);
+    w.k = c.take<uint16_t>(LP * H);
+    w.vt = c.take<uint16_t>(LP * H);
+    w.cat = c.take<uint16_t>(L * (H + M));
+    return w;
+}
+
+struct StepWs {
+    float* emb;      // [512]
+    float* tmp;      // [2H]
+    float* vec;      // [H]
+    float* fmod;     // [2H]
+    float* x;        // [L, H]
+    uint16_t* z16;   // [L_i, C] fp16
+    char* blocks;    // shared by the block calls
+    size_t block_bytes;
+};
+
+size_t block_ws_bytes(const mmdit_dims* d) {
+    Carver c1(nullptr), c2(nullptr);
+    carve_double(d, c1);
+    carve_single(d, c2);
+    return c1.off > c2.off ? c1.off : c2.off;
+}
+
+StepWs carve_step(const mmdit_dims* d, Carver& c) {
+    const size_t L = seq_len(d), H = d->hidden;
+    StepWs w;
+    w.emb = c.take<float>(512);
+    w.tmp = c.take<float>(2 * H);
+    w.vec = c.take<float>(H);
+    w.fmod = c.take<float>(2 * H);
+    w.x = c.take<float>(L * H);
+    w.z16 = c.take<uint16_t>((size_t)d->img_len * d->in_channels);
+    w.block_bytes = block_ws_bytes(d);
+    w.blocks = c.take<char>(w.block_bytes);
+    return w;
+}
+
+// ---------------------------------------------------------------- helpers
+hipError_t gemv(const float* x, int k, const mmdit_linear& l, int n, int dt, int silu_in, int acc,
+                float* out, hipStream_t s) {
+    return launch_gemv(x, k, l.w, l.scale, l.bias, n, dt == MMDIT_INT8, silu_in, acc, out, s);
+}
+
+GemmGroup group(int row0, int m, const mmdit_linear& l, const float* gate = nullptr) {
+    GemmGroup g;
+    g.row0 = row0;
+    g.m = m;
+    g.w = l.w;
+    g.scale = l.scale;
+    g.bias = l.bias;
+    g.gate = gate;
+    return g;
+}
+
+GemmArgs gemm_base(int n, int k, int dt, const uint16_t* a, int lda, int epi, void* out, int ldo) {
+    GemmArgs g = {};
+    g.n = n;
+    g.k = k;
+    g.int8 = dt == MMDIT_INT8;
+    g.a = a;
+    g.lda = lda;
+    g.epilogue = epi;
+    g.out = out;
+    g.ldo = ldo;
+    return g;
+}
+
+hipError_t gemm_2(GemmArgs g, const GemmGroup& g0, const GemmGroup& g1, hipStream_t s) {
+    g.ngroups = 2;
+    g.g[0] = g0;
+    g.g[1] = g1;
+    return launch_gemm(g, s);
+}
+
+hipError_t gemm_1(GemmArgs g, const GemmGroup& g0, hipStream_t s) {
+    g.ngroups = 1;
+    g.g[0] = g0;
+    return launch_gemm(g, s);
+}
+
+// fp32 latent -> fp16 activation operand of the patch-embedding projection
+__global__ void f32_to_f16_kernel(const float* __restrict__ x, uint16_t* __restrict__ y, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        y[i] = f2h(x[i]);
+}
+
+// ---------------------------------------------------------------- blocks
+int run_double(const mmdit_dims* d, const mmdit_double_weights* w, const float* vec, const float* rope,
+               const float* x_in, float* x_out, const DoubleWs& ws, hipStream_t s) {
+    const int Lt = d->txt_len, Li = d->img_len, L = Lt + Li, H = d->hidden, M = d->mlp_hidden;
+    const int dt = d->weight_dtype, LP = padded_len(d);
+    float* mt = ws.mod;
+    float* mi = ws.mod + 6 * H;
+    // a1: modulation of each stream
+    MMDIT_HIP(gemv(vec, H, w->txt.mod, 6 * H, dt, 1, 0, mt, s));
+    MMDIT_HIP(gemv(vec, H, w->img.mod, 6 * H, dt, 1, 0, mi, s));
+    // a2: LN1 + modulate
+    MMDIT_HIP(launch_ln_modulate(x_in, L, H, Lt, mt, mt + H, mi, mi + H, d->ln_eps, ws.h, s));
+    // a3: QKV
+    MMDIT_HIP(gemm_2(gemm_base(3 * H, H, dt, ws.h, H, MMDIT_EPI_BIAS, ws.qkv, 3 * H),
+                     group(0, Lt, w->txt.qkv), group(Lt, Li, w->img.qkv), s));
+    // a4: QK-RMSNorm + RoPE + relayout
+    MMDIT_HIP(launch_qknorm_rope(ws.qkv, 3 * H, L, d->heads, d->head_dim, Lt,
+                                 w->txt.q_norm, w->txt.k_norm, w->img.q_norm, w->img.k_norm, rope,
+                                 d->rms_eps, LP, ws.q, ws.k, ws.vt, s));
+    // a5: joint attention
+    MMDIT_HIP(launch_attention(ws.q, ws.k, ws.vt, d->heads, L, d->head_dim, LP, ws.o, H, s));
+    // a6: out projection + gated residual
+    {
+        GemmArgs g = gemm_base(H, H, dt, ws.o, H, MMDIT_EPI_GATE_RESID, x_out, H);
+        g.resid = x_in;
+        g.ldr = H;
+        MMDIT_HIP(gemm_2(g, group(0, Lt, w->txt.proj, mt + 2 * H), group(Lt, Li, w->img.proj, mi + 2 * H), s));
+    }
+    // a7: LN2 + modulate
+    MMDIT_HIP(launch_ln_modulate(x_out, L, H, Lt, mt + 3 * H, mt + 4 * H, mi + 3 * H, mi + 4 * H,
+                                 d->ln_eps, ws.h, s));
+    // a8: fc1 + GELU
+    MMDIT_HIP(gemm_2(gemm_base(M, H, dt, ws.h, H, MMDIT_EPI_BIAS_GELU, ws.a, M),
+                     group(0, Lt, w->txt.fc1), group(Lt, Li, w->img.fc1), s));
+    // a9: fc2 + gated residual
+    {
+        GemmArgs g = gemm_base(H, M, dt, ws.a, M, MMDIT_EPI_GATE_RESID, x_out, H);
+        g.resid = x_out;
+        g.ldr = H;
+        MMDIT_HIP(gemm_2(g, group(0, Lt, w->txt.fc2, mt + 5 * H), group(Lt, Li, w->img.fc2, mi + 5 * H), s));
+    }
+    return MMDIT_OK;
+}
+
+int run_single(const mmdit_dims* d, const mmdit_single_weights* w, const float* vec, const float* rope,
+               const float* x_in, float* x_out, const SingleWs& ws, hipStream_t s) {
+    const int L = seq_len(d), H = d->hidden, M = d->mlp_hidden;
+    const int dt = d->weight_dtype, LP = padded_len(d);
+    float* m = ws.mod;
+    MMDIT_HIP(gemv(vec, H, w->mod, 3 * H, dt, 1, 0, m, s));
+    MMDIT_HIP(launch_ln_modulate(x_in, L, H, 0, m, m + H, m, m + H, d->ln_eps, ws.h, s));
+    {
+        GemmArgs g = gemm_base(3 * H + M, H, dt, ws.h, H, MMDIT_EPI_SPLIT_GELU, ws.qkv, 3 * H);
+        g.split_n = 3 * H;
+        g.out2 = ws.cat;
+        g.ldo2 = H + M;
+        g.out2_col = H;
+        MMDIT_HIP(gemm_1(g, group(0, L, w->linear1), s));
+    }
+    MMDIT_HIP(launch_qknorm_rope(ws.qkv, 3 * H, L, d->heads, d->head_dim, L, w->q_norm, w->k_norm,
+                                 w->q_norm, w->k_norm, rope, d->rms_eps, LP, ws.q, ws.k, ws.vt, s));
+    MMDIT_HIP(launch_attention(ws.q, ws.k, ws.vt, d->heads, L, d->head_dim, LP, ws.cat, H + M, s));
+    {
+        GemmArgs g = gemm_base(H, H + M, dt, ws.cat, H + M, MMDIT_EPI_GATE_RESID, x_out, H);
+        g.resid = x_in;
+        g.ldr = H;
+        MMDIT_HIP(gemm_1(g, group(0, L, w->linear2, m + 2 * H), s));
+    }
+    return MMDIT_OK;
+}
+
+int run_time_embed(const mmdit_dims* d, const mmdit_model* m, float t, float guidance, float* vec,
+                   float* emb, float* tmp, hipStream_t s) {
+    const int H = d->hidden, dt = d->weight_dtype;
+    MMDIT_HIP(launch_time_and_guidance_embedding(t, guidance, emb, s));
+    MMDIT_HIP(gemv(emb, 256, m->time_in[0], H, dt, 0, 0, tmp, s));
+    MMDIT_HIP(gemv(emb + 256, 256, m->guid_in[0], H, dt, 0, 0, tmp + H, s));
+    MMDIT_HIP(gemv(tmp, H, m->time_in[1], H, dt, 1, 0, vec, s));
+    MMDIT_HIP(gemv(tmp + H, H, m->guid_in[1], H, dt, 1, 1, vec, s));
+    return MMDIT_OK;
+}
+
+}  // namespace
+
+// ======================================================================== ABI
+extern "C" {
+
+int mmdit_abi_version(void) { return MMDIT_ABI_VERSION; }
+
+const char* mmdit_status_string(int st) {
+    switch (st) {
+        case MMDIT_OK: return "ok";
+        case MMDIT_E_NULL: return "null pointer";
+        case MMDIT_E_ALIGN: return "pointer or stride not 16-byte aligned";
+        case MMDIT_E_SHAPE: return "unsupported or inconsistent sizes";
+        case MMDIT_E_DTYPE: return "bad weight dtype or missing int8 scales";
+        case MMDIT_E_WORKSPACE: return "workspace too small";
+        case MMDIT_E_HIP: return "kernel launch failed";
+        case MMDIT_E_ARG: return "invalid argument";
+        default: return "unknown status";
+    }
+}
+
+size_t mmdit_workspace_bytes(const mmdit_dims* d, int kind) {
+    if (check_dims(d) != MMDIT_OK) return 0;
+    Carver c(nullptr);
+    if (kind == MMDIT_WS_DOUBLE) carve_double(d, c);
+    else if (kind == MMDIT_WS_SINGLE) carve_single(d, c);
+    else if (kind == MMDIT_WS_STEP) carve_step(d, c);
+    else return 0;
+    return c.off;
+}
+
+int mmdit_block_forward(const mmdit_dims* d, const mmdit_double_weights* w, const float* vec,
+                        const float* rope, const float* x_in, float* x_out, void* ws, size_t ws_bytes,
+                        hipStream_t s) {
+    MMDIT_TRY(check_dims(d));
+    MMDIT_TRY(double_weights_ok(w, d->weight_dtype));
+    MMDIT_TRY(check_ptr(vec));
+    MMDIT_TRY(check_ptr(rope));
+    MMDIT_TRY(check_ptr(x_in));
+    MMDIT_TRY(check_ptr(x_out));
+    MMDIT_TRY(check_ptr(ws));
+    Carver c(ws);
+    const DoubleWs dw = carve_double(d, c);
+    if (ws_bytes < c.off) return MMDIT_E_WORKSPACE;
+    return run_double(d, w, vec, rope, x_in, x_out, dw, s);
+}
+
+int mmdit_single_block_forward(const mmdit_dims* d, const mmdit_single_weights* w, const float* vec,
+                               const float* rope, const float* x_in, float* x_out, void* ws,
+                               size_t ws_bytes, hipStream_t s) {
+    MMDIT_TRY(check_dims(d));
+    MMDIT_TRY(single_weights_ok(w, d->weight_dtype));
+    MMDIT_TRY(check_ptr(vec));
+    MMDIT_TRY(check_ptr(rope));
+    MMDIT_TRY(check_ptr(x_in));
+    MMDIT_TRY(check_ptr(x_out));
+    MMDIT_TRY(check_ptr(ws));
+    Carver c(ws);
+    const SingleWs sw = carve_single(d, c);
+    if (ws_bytes < c.off) return MMDIT_E_WORKSPACE;
+    return run_single(d, w, vec, rope, x_in, x_out, sw, s);
+}
+
+int mmdit_denoise_step(const mmdit_dims* d, const mmdit_model* m, float* latent, const float* txt,
+                       const float* rope, float t_cur, float t_next, float guidance, void* ws,
+                       size_t ws_bytes, hipStream_t s) {
+    MMDIT_TRY(check_dims(d));
+    if (!m) return MMDIT_E_NULL;
+    if (d->in_channels < 64 || d->in_channels % 64 != 0) return MMDIT_E_SHAPE;
+    if (d->n_double < 0 || d->n_single < 0) return MMDIT_E_SHAPE;
+    const int dt = d->weight_dtype;
+    MMDIT_TRY(check_linear(m->img_in, dt));
+    for (int i = 0; i < 2; ++i) {
+        MMDIT_TRY(check_linear(m->time_in[i], dt));
+        MMDIT_TRY(check_linear(m->guid_in[i], dt));
+    }
+    MMDIT_TRY(check_linear(m->final_mod, dt));
+    MMDIT_TRY(check_linear(m->final_out, dt));
+    if (d->n_double > 0 && !m->doubles) return MMDIT_E_NULL;
+    if (d->n_single > 0 && !m->singles) return MMDIT_E_NULL;
+    for (int i = 0; i < d->n_double; ++i) MMDIT_TRY(double_weights_ok(&m->doubles[i], dt));
+    for (int i = 0; i < d->n_single; ++i) MMDIT_TRY(single_weights_ok(&m->singles[i], dt));
+    MMDIT_TRY(check_ptr(latent));
+    MMDIT_TRY(check_ptr(txt));
+    MMDIT_TRY(check_ptr(rope));
+    MMDIT_TRY(check_ptr(ws));
+    if (!std::isfinite(t_cur) || !std::isfinite(t_next) || !std::isfinite(guidance)) return MMDIT_E_ARG;
+    Carver c(ws);
+    const StepWs sw = carve_step(d, c);
+    if (ws_bytes < c.off) return MMDIT_E_WORKSPACE;
+
+    const int Lt = d->txt_len, Li = d->img_len, L = Lt + Li, H = d->hidden, C = d->in_channels;
+    MMDIT_TRY(run_time_embed(d, m, t_cur, guidance, sw.vec, sw.emb, sw.tmp, s));
+    // x = [txt | img_in(latent)]
+    MMDIT_HIP(launch_copy_f32(sw.x, txt, (int64_t)Lt * H, s));
+    {
+        const int64_t n = (int64_t)Li * C;
+        int64_t blocks = (n + 255) / 256;
+        if (blocks > 4096) blocks = 4096;
+        hipLaunchKernelGGL(f32_to_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, latent, sw.z16, n);
+        MMDIT_HIP(hipGetLastError());
+        GemmArgs g = gemm_base(H, C, dt, sw.z16, C, MMDIT_EPI_BIAS_F32, sw.x + (size_t)Lt * H, H);
+        MMDIT_HIP(gemm_1(g, group(0, Li, m->img_in), s));
+    }
+    Carver cb(sw.blocks);
+    const DoubleWs dws = carve_double(d, cb);
+    Carver cs(sw.blocks);
+    const SingleWs sws = carve_single(d, cs);
+    for (int i = 0; i < d->n_double; ++i)
+        MMDIT_TRY(run_double(d, &m->doubles[i], sw.vec, rope, sw.x, sw.x, dws, s));
+    for (int i = 0; i < d->n_single; ++i)
+        MMDIT_TRY(run_single(d, &m->singles[i], sw.vec, rope, sw.x, sw.x, sws, s));
+    // final layer on the image rows, fused with the Euler update
+    MMDIT_HIP(gemv(sw.vec, H, m->final_mod, 2 * H, dt, 1, 0, sw.fmod, s));
+    MMDIT_HIP(launch_ln_modulate(sw.x + (size_t)Lt * H, Li, H, 0, sw.fmod, sw.fmod + H, sw.fmod,
+                                 sw.fmod + H, d->ln_eps, dws.h, s));
+    {
+        GemmArgs g = gemm_base(C, H, dt, dws.h, H, MMDIT_EPI_EULER, latent, C);
+        g.alpha = t_next - t_cur;
+        MMDIT_HIP(gemm_1(g, group(0, Li, m->final_out), s));
+    }
+    (void)L;
+    return MMDIT_OK;
+}
+
+int mmdit_rope_table(const mmdit_dims* d, const int32_t* ids, float* rope, hipStream_t s) {
+    MMDIT_TRY(check_dims(d));
+    MMDIT_TRY(check_ptr(ids));
+    MMDIT_TRY(check_ptr(rope));
+    MMDIT_HIP(launch_rope_table(ids, seq_len(d), d->head_dim, d->rope_axes[0], d->rope_axes[1],
+                                d->rope_axes[2], d->rope_theta, rope, s));
+    return MMDIT_OK;
+}
+
+// ------------------------------------------------------------ kernel entries
+int mmdit_k_ln_modulate(const float* x, int rows, int hidden, int split, const float* shift0,
+                        const float* scale0, const float* shift1, const float* scale1, float eps,
+                        mmdit_bf16* out, hipStream_t s) {
+    if (rows < 0 || hidden < 64 || hidden % 64 != 0 || hidden > 4096) return MMDIT_E_SHAPE;
+    if (!(eps > 0.f)) return MMDIT_E_ARG;
+    MMDIT_TRY(check_ptr(x));
+    MMDIT_TRY(check_ptr(out));
+    MMDIT_TRY(check_ptr(shift0));
+    MMDIT_TRY(check_ptr(scale0));
+    if (split < rows) {
+        MMDIT_TRY(check_ptr(shift1));
+        MMDIT_TRY(check_ptr(scale1));
+    }
+    MMDIT_HIP(launch_ln_modulate(x, rows, hidden, split, shift0, scale0, shift1 ? shift1 : shift0,
+                                 scale1 ? scale1 : scale0, eps, out, s));
+    return MMDIT_OK;
+}
+
+int mmdit_k_qknorm_rope(const mmdit_bf16* qkv, int ld, int seq, int heads, int head_dim, int split,
+                        const mmdit_bf16* qn0, const mmdit_bf16* kn0, const mmdit_bf16* qn1,
+                        const mmdit_bf16* kn1, const float* rope, float eps, int l_pad,
+                        mmdit_bf16* q_out, mmdit_bf16* k_out, mmdit_bf16* vt_out, hipStream_t s) {
+    if (head_dim != 64 && head_dim != 128) return MMDIT_E_SHAPE;
+    if (seq < 1 || heads < 1 || ld < 3 * heads * head_dim || ld % 8 != 0) return MMDIT_E_SHAPE;
+    if (l_pad < seq || l_pad % 64 != 0) return MMDIT_E_SHAPE;
+    if (!(eps > 0.f)) return MMDIT_E_ARG;
+    for (const void* p : {(const void*)qkv, (const void*)qn0, (const void*)kn0, (const void*)rope,
+                          (const void*)q_out, (const void*)k_out, (const void*)vt_out})
+        MMDIT_TRY(check_ptr(p));
+    if (split < seq) {
+        MMDIT_TRY(check_ptr(qn1));
+        MMDIT_TRY(check_ptr(kn1));
+    }
+    MMDIT_HIP(launch_qknorm_rope(qkv, ld, seq, heads, head_dim, split, qn0, kn0, qn1 ? qn1 : qn0,
+                                 kn1 ? kn1 : kn0, rope, eps, l_pad, q_out, k_out, vt_out, s));
+    return MMDIT_OK;
+}
+
+int mmdit_k_attention(const mmdit_bf16* q, const mmdit_bf16* k, const mmdit_bf16* vt, int heads, int seq,
+                      int head_dim, int l_pad, mmdit_bf16* out, int ldo, hipStream_t s) {
+    if (head_dim != 64 && head_dim != 128) return MMDIT_E_SHAPE;
+    if (seq < 1 || heads < 1 || l_pad < seq || l_pad % 64 != 0) return MMDIT_E_SHAPE;
+    if (ldo < heads * head_dim || ldo % 8 != 0) return MMDIT_E_SHAPE;
+    for (const void* p : {(const void*)q, (const void*)k, (const void*)vt, (const void*)out})
+        MMDIT_TRY(check_ptr(p));
+    MMDIT_HIP(launch_attention(q, k, vt, heads, seq, head_dim, l_pad, out, ldo, s));
+    return MMDIT_OK;
+}
+
+int mmdit_k_gemm(const mmdit_gemm* g, hipStream_t s) {
+    if (!g) return MMDIT_E_NULL;
+    if (g->m < 1 || g->n < 64 || g->n % 64 != 0 || g->k < 64 || g->k % 64 != 0) return MMDIT_E_SHAPE;
+    if (g->lda < g->k || g->lda % 8 != 0) return MMDIT_E_SHAPE;
+    if (g->weight_dtype != MMDIT_BF16 && g->weight_dtype != MMDIT_INT8) return MMDIT_E_DTYPE;
+    if (g->epilogue < MMDIT_EPI_BIAS || g->epilogue > MMDIT_EPI_EULER) return MMDIT_E_ARG;
+    MMDIT_TRY(check_ptr(g->a));
+    MMDIT_TRY(check_linear(g->w, g->weight_dtype));
+    MMDIT_TRY(check_ptr(g->out));
+    const bool f32out = g->epilogue == MMDIT_EPI_GATE_RESID || g->epilogue == MMDIT_EPI_BIAS_F32 ||
+                        g->epilogue == MMDIT_EPI_EULER;
+    const int ncols = g->epilogue == MMDIT_EPI_SPLIT_GELU ? g->split_n : g->n;
+    if (g->ldo < ncols || g->ldo % (f32out ? 4 : 8) != 0) return MMDIT_E_SHAPE;
+    if (g->epilogue == MMDIT_EPI_GATE_RESID) {
+        MMDIT_TRY(check_ptr(g->gate));
+        MMDIT_TRY(check_ptr(g->resid));
+        if (g->ldr < g->n || g->ldr % 4 != 0) return MMDIT_E_SHAPE;
+    }
+    if (g->epilogue == MMDIT_EPI_SPLIT_GELU) {
+        if (g->split_n < 0 || g->split_n > g->n || g->split_n % 64 != 0) return MMDIT_E_SHAPE;
+        MMDIT_TRY(check_ptr(g->out2));
+        if (g->out2_col < 0 || g->out2_col % 8 != 0 || g->ldo2 % 8 != 0 ||
+            g->ldo2 < g->out2_col + (g->n - g->split_n))
+            return MMDIT_E_SHAPE;
+    }
+    GemmArgs a = gemm_base(g->n, g->k, g->weight_dtype, g->a, g->lda, g->epilogue, g->out, g->ldo);
+    a.resid = g->resid;
+    a.ldr = g->ldr;
+    a.split_n = g->split_n;
+    a.out2 = g->out2;
+    a.ldo2 = g->ldo2;
+    a.out2_col = g->out2_col;
+    a.alpha = g->alpha;
+    MMDIT_HIP(gemm_1(a, group(0, g->m, g->w, g->gate), s));
+    return MMDIT_OK;
+}
+
+int mmdit_k_gemv(const float* x, int k, const mmdit_linear* w, int n, int weight_dtype, int silu_input,
+                 int accumulate, float* out, hipStream_t s) {
+    if (!w) return MMDIT_E_NULL;
+    if (k < 64 || k % 64 != 0 || n < 1 || k > 16384) return MMDIT_E_SHAPE;
+    if (weight_dtype != MMDIT_BF16 && weight_dtype != MMDIT_INT8) return MMDIT_E_DTYPE;
+    MMDIT_TRY(check_ptr(x));
+    MMDIT_TRY(check_linear(*w, weight_dtype));
+    MMDIT_TRY(check_ptr(out));
+    MMDIT_HIP(gemv(x, k, *w, n, weight_dtype, silu_input != 0, accumulate != 0, out, s));
+    return MMDIT_OK;
+}
+
+int mmdit_k_time_embed(const mmdit_dims* d, const mmdit_model* m, float t, float guidance, float* vec,
+                       void* ws, size_t ws_bytes, hipStream_t s) {
+    MMDIT_TRY(check_dims(d));
+    if (!m) return MMDIT_E_NULL;
+    for (int i = 0; i < 2; ++i) {
+        MMDIT_TRY(check_linear(m->time_in[i], d->weight_dtype));
+        MMDIT_TRY(check_linear(m->guid_in[i], d->weight_dtype));
+    }
+    MMDIT_TRY(check_ptr(vec));
+    MMDIT_TRY(check_ptr(ws));
+    if (ws_bytes < 4 * (512 + 2 * (size_t)d->hidden)) return MMDIT_E_WORKSPACE;
+    float* emb = static_cast<float*>(ws);
+    return run_time_embed(d, m, t, guidance, vec, emb, emb + 512, s);
+}
+
+int mmdit_k_euler(float* z, const float* v, int64_t n, float dt, hipStream_t s) {
+    if (n < 0) return MMDIT_E_SHAPE;
+    MMDIT_TRY(check_ptr(z));
+    MMDIT_TRY(check_ptr(v));
+    MMDIT_HIP(launch_euler(z, v, n, dt, s));
+    return MMDIT_OK;
+}
+
+}  // extern "C"

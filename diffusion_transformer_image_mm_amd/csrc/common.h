@@ -1,0 +1,143 @@
+// Shared device helpers of the gfx950 kernels (internal header).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mmdit.h"
+
+#define MMDIT_DEV __device__ __forceinline__
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+namespace mmdit {
+
+// bf16 bits -> fp32 (exact)
+MMDIT_DEV float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (the conversion instruction of gfx950)
+MMDIT_DEV uint16_t f2bf(float f) {
+    __bf16 h = static_cast<__bf16>(f);
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+// two fp32 -> packed bf16 pair (low = a)
+MMDIT_DEV uint32_t pack2bf(float a, float b) {
+    return uint32_t(f2bf(a)) | (uint32_t(f2bf(b)) << 16);
+}
+
+// fp32 -> fp16 bits, round to nearest even
+MMDIT_DEV uint16_t f2h(float f) {
+    _Float16 h = static_cast<_Float16>(f);
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+// two fp32 -> packed fp16 pair (low = a)
+MMDIT_DEV uint32_t pack2h(float a, float b) {
+    return uint32_t(f2h(a)) | (uint32_t(f2h(b)) << 16);
+}
+
+// fp16 bits -> fp32 (exact)
+MMDIT_DEV float h2f(uint16_t b) { return static_cast<float>(__builtin_bit_cast(_Float16, b)); }
+
+// Sum over all 64 lanes of a wavefront (butterfly; every lane gets the total).
+MMDIT_DEV float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Sum over aligned groups of G lanes (G a power of two <= 64).
+template <int G>
+MMDIT_DEV float group_sum(float v) {
+#pragma unroll
+    for (int o = G / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// SiLU(x) = x / (1 + e^-x)
+MMDIT_DEV float silu(float x) { return x / (1.0f + __expf(-x)); }
+
+// GELU, tanh form: 0.5 x (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3).
+// tanh(u) = 1 - 2 / (e^{2u} + 1), so 0.5 (1 + tanh u) = 1 - 1/(e^{2u} + 1);
+// exact for large |u| (the exponential saturates to 0 or inf).
+MMDIT_DEV float gelu_tanh(float x) {
+    const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+    const float k1 = 0.044715f;
+    float u = k0 * (x + k1 * x * x * x);
+    float e = __expf(2.0f * u);
+    return x * (1.0f - 1.0f / (e + 1.0f));
+}
+
+}  // namespace mmdit
+
+// Launchers (defined in the kernel sources, called by the API layer). Each
+// returns hipSuccess or the launch error.
+namespace mmdit {
+
+hipError_t launch_ln_modulate(const float* x, int rows, int hidden, int split,
+                              const float* shift0, const float* scale0,
+                              const float* shift1, const float* scale1, float eps,
+                              uint16_t* out, hipStream_t s);
+
+hipError_t launch_qknorm_rope(const uint16_t* qkv, int ld, int seq_len, int heads, int head_dim,
+                              int split, const uint16_t* qn0, const uint16_t* kn0,
+                              const uint16_t* qn1, const uint16_t* kn1, const float* rope,
+                              float eps, int l_pad, uint16_t* q_out, uint16_t* k_out,
+                              uint16_t* vt_out, hipStream_t s);
+
+hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int heads,
+                            int seq_len, int head_dim, int l_pad, uint16_t* out, int ldo,
+                            hipStream_t s);
+
+// One GEMM group: rows [row0, row0 + m) of A / out share one weight set.
+struct GemmGroup {
+    int row0, m;
+    const void* w;
+    const float* scale;
+    const uint16_t* bias;
+    const float* gate;
+};
+
+struct GemmArgs {
+    int n, k;
+    int int8;
+    const uint16_t* a;
+    int lda;
+    int epilogue;
+    void* out;
+    int ldo;
+    const float* resid;
+    int ldr;
+    int split_n;
+    void* out2;
+    int ldo2;
+    int out2_col;
+    float alpha;
+    int ngroups;
+    GemmGroup g[2];
+};
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
+hipError_t launch_gemv(const float* x, int k, const void* w, const float* scale,
+                       const uint16_t* bias, int n, int int8, int silu_input, int accumulate,
+                       float* out, hipStream_t s);
+
+// out[0:256] = emb(t), out[256:512] = emb(g)
+hipError_t launch_time_and_guidance_embedding(float t, float g, float* out, hipStream_t s);
+
+hipError_t launch_euler(float* z, const float* v, int64_t n, float dt, hipStream_t s);
+
+hipError_t launch_rope_table(const int32_t* ids, int seq_len, int head_dim, int a0, int a1, int a2,
+                             float theta, float* rope, hipStream_t s);
+
+hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t s);
+
+}  // namespace mmdit

@@ -1,0 +1,253 @@
+// Flash attention forward (no mask): O = softmax(Q K^T / sqrt(D)) V per head.
+//
+// Luminal blog, "The AMD MI300X pipeline" and "What the compiler found on its
+// own": the attention sites of the diffusion transformer run as one fused
+// kernel that computes softmax(QK^T)V tile by tile; the scaled-dot-product
+// pattern is two matrix products, a scale, a max, an exponent, a sum and a
+// divide. The transformer's attention has no mask.
+//
+// gfx950 design:
+// * workgroup = 4 wavefronts x 32 query rows (128 rows of one head);
+//   key/value tiles of 64 keys;
+// * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K from LDS as the first
+//   operand, Q^T from registers as the second), so each lane holds 32 scores
+//   of ONE query row: the row max needs one cross-lane exchange (lane ^ 32)
+//   and the row sum none until the end;
+// * online softmax in fp32 with exp2: scores are scaled by log2(e)/sqrt(D)
+//   in one multiply-subtract; O is rescaled only by the lane's own factor;
+// * O^T += V^T P^T: the probabilities are already in the second operand's
+//   register layout (the key order inside one MFMA is free as long as both
+//   operands agree), V^T comes from LDS as two 8-byte reads per fragment;
+// * K and V^T tiles go global -> LDS with 16-byte direct-to-LDS loads into
+//   two distinct LDS buffers (double buffering; distinct variables let the
+//   compiler see that the next tile's loads do not alias this tile's reads);
+//   chunk positions are XOR-swizzled by row to spread LDS banks;
+// * the last key tile masks keys >= seq_len to -inf; query rows >= seq_len
+//   are computed on zero padding and not stored;
+// * O is stored as fp16: it is the activation operand of the output
+//   projection (values lie in the convex hull of V).
+#include "common.h"
+
+namespace mmdit {
+
+namespace {
+typedef __attribute__((address_space(3))) void lds_void;
+MMDIT_DEV void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+MMDIT_DEV void g2l_16(const void* gsrc, lds_void* lds_base) {
+    __builtin_amdgcn_global_load_lds(gsrc, lds_base, 16, 0, 0);
+}
+}  // namespace
+
+template <int D>
+struct AttnTile {
+    static constexpr int KV = 64;           // keys per tile
+    static constexpr int RB = D * 2;        // bytes per K row
+    static constexpr int CPR = D / 8;       // 16-byte chunks per K row
+    static constexpr int K_RPI = 64 / CPR;  // K rows per wavefront load
+    static constexpr int K_LPW = (KV / K_RPI) / 4;  // K loads per wavefront
+    static constexpr int V_LPW = (D / 8) / 4;       // V^T loads per wavefront (8 rows each)
+    static constexpr int K_BYTES = KV * RB;
+    static constexpr int V_BYTES = D * KV * 2;
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void attention_kernel(const uint16_t* __restrict__ q,
+                                                           const uint16_t* __restrict__ k,
+                                                           const uint16_t* __restrict__ vt,
+                                                           int seq_len, int l_pad,
+                                                           uint16_t* __restrict__ out, int ldo,
+                                                           float c_log2) {
+    using T = AttnTile<D>;
+    __shared__ __attribute__((aligned(1024))) char sK0[T::K_BYTES];
+    __shared__ __attribute__((aligned(1024))) char sV0[T::V_BYTES];
+    __shared__ __attribute__((aligned(1024))) char sK1[T::K_BYTES];
+    __shared__ __attribute__((aligned(1024))) char sV1[T::V_BYTES];
+
+    const int h = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 5, r32 = lane & 31;
+    const int qrow = blockIdx.x * 128 + wave * 32 + r32;
+    const int H = gridDim.y * D;
+
+    // ---- Q^T fragments (second MFMA operand): lane holds Q[qrow][ds*16 + 8g .. +7]
+    const int qld = qrow < l_pad ? qrow : l_pad - 1;
+    const uint16_t* qp = q + ((size_t)h * l_pad + qld) * D + g * 8;
+    bf16x8_t qf[D / 16];
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) qf[ds] = *reinterpret_cast<const bf16x8_t*>(qp + ds * 16);
+
+    // ---- load descriptors
+    const uint16_t* kbase = k + (size_t)h * l_pad * D;
+    const uint16_t* vbase = vt + (size_t)h * D * l_pad;
+    const char* k_src[T::K_LPW];
+    int k_dst[T::K_LPW];
+#pragma unroll
+    for (int j = 0; j < T::K_LPW; ++j) {
+        const int first = (wave * T::K_LPW + j) * T::K_RPI;
+        const int r = first + lane / T::CPR;
+        const int c = (lane % T::CPR) ^ (r & (T::CPR - 1));
+        k_src[j] = reinterpret_cast<const char*>(kbase + (size_t)r * D + c * 8);
+        k_dst[j] = first * T::RB;
+    }
+    const char* v_src[T::V_LPW];
+    int v_dst[T::V_LPW];
+#pragma unroll
+    for (int j = 0; j < T::V_LPW; ++j) {
+        const int first = (wave * T::V_LPW + j) * 8;
+        const int d = first + lane / 8;
+        const int c = (lane % 8) ^ ((d >> 1) & 7);
+        v_src[j] = reinterpret_cast<const char*>(vbase + (size_t)d * l_pad + c * 8);
+        v_dst[j] = first * 128;
+    }
+    auto issue = [&](int t, char* sK, char* sV) {
+        const size_t koff = (size_t)t * T::KV * T::RB;  // bytes along the key rows
+        const size_t voff = (size_t)t * T::KV * 2;      // bytes along a V^T row
+#pragma unroll
+        for (int j = 0; j < T::K_LPW; ++j) g2l_16(k_src[j] + koff, (lds_void*)(sK + k_dst[j]));
+#pragma unroll
+        for (int j = 0; j < T::V_LPW; ++j) g2l_16(v_src[j] + voff, (lds_void*)(sV + v_dst[j]));
+    };
+
+    // ---- fragment offsets
+    int k_off[2][D / 16];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int ds = 0; ds < D / 16; ++ds) {
+            const int row = st * 32 + r32;
+            const int c = ds * 2 + g;
+            k_off[st][ds] = row * T::RB + ((c ^ (row & (T::CPR - 1))) * 16);
+        }
+    int v_off[D / 32][4][2];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int d = dt * 32 + r32;
+                const int c = 2 * u + half;
+                v_off[dt][u][half] = d * 128 + ((c ^ ((d >> 1) & 7)) * 16) + g * 8;
+            }
+
+    f32x16_t o[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const int nkv = (seq_len + T::KV - 1) / T::KV;
+
+    auto compute = [&](int t, const char* sK, const char* sV) {
+        // S^T = K Q^T for the two 32-key halves of the tile
+        f32x16_t s[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
+#pragma unroll
+            for (int ds = 0; ds < D / 16; ++ds) {
+                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(sK + k_off[st][ds]);
+                s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s[st], 0, 0, 0);
+            }
+        }
+        // element i of s[st]: key t*64 + st*32 + 8*(i/4) + 4g + i%4
+        const int kv0 = t * T::KV;
+        if (kv0 + T::KV > seq_len) {
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = kv0 + st * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+                    if (key >= seq_len) s[st][i] = -INFINITY;
+                }
+        }
+        float tmax = s[0][0];
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[st][i]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float m_new = fmaxf(m_run, tmax * c_log2);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        float psum = 0.f;
+        bf16x8_t pf[4];
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float p = __builtin_amdgcn_exp2f(s[st][i] * c_log2 - m_new);
+                psum += p;
+                pf[st * 2 + (i >> 3)][i & 7] = static_cast<__bf16>(p);
+            }
+        l_run = l_run * alpha + psum;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+        // O^T += V^T P^T
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const bf16x4_t lo = *reinterpret_cast<const bf16x4_t*>(sV + v_off[dt][u][0]);
+                const bf16x4_t hi = *reinterpret_cast<const bf16x4_t*>(sV + v_off[dt][u][1]);
+                const bf16x8_t vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[u], o[dt], 0, 0, 0);
+            }
+    };
+
+    issue(0, sK0, sV0);
+    wait_vmcnt0();
+    __syncthreads();
+    for (int t = 0; t < nkv; t += 2) {
+        if (t + 1 < nkv) issue(t + 1, sK1, sV1);
+        compute(t, sK0, sV0);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt0();
+        __syncthreads();
+        if (t + 1 >= nkv) break;
+        if (t + 2 < nkv) issue(t + 2, sK0, sV0);
+        compute(t + 1, sK1, sV1);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt0();
+        __syncthreads();
+    }
+
+    // ---- normalise and store: o[dt] element i is O[qrow][dt*32 + 8*(i/4) + 4g + i%4]
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float inv = 1.0f / l_tot;
+    if (qrow < seq_len) {
+        uint16_t* op = out + (size_t)qrow * ldo + h * D + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const uint2 w = make_uint2(pack2h(o[dt][4 * i4] * inv, o[dt][4 * i4 + 1] * inv),
+                                           pack2h(o[dt][4 * i4 + 2] * inv, o[dt][4 * i4 + 3] * inv));
+                *reinterpret_cast<uint2*>(op + dt * 32 + 8 * i4) = w;
+            }
+    }
+    (void)H;
+}
+
+hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int heads,
+                            int seq_len, int head_dim, int l_pad, uint16_t* out, int ldo,
+                            hipStream_t s) {
+    if (seq_len <= 0) return hipSuccess;
+    dim3 grid((seq_len + 127) / 128, heads), block(256);
+    const float c_log2 = 1.4426950408889634f / sqrtf((float)head_dim);
+    if (head_dim == 128)
+        hipLaunchKernelGGL(attention_kernel<128>, grid, block, 0, s, q, k, vt, seq_len, l_pad, out, ldo,
+                           c_log2);
+    else if (head_dim == 64)
+        hipLaunchKernelGGL(attention_kernel<64>, grid, block, 0, s, q, k, vt, seq_len, l_pad, out, ldo,
+                           c_log2);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace mmdit

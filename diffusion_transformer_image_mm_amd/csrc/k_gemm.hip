@@ -1,0 +1,352 @@
+// MFMA GEMM with fused epilogues: out = epi(A W^T), fp32 accumulation.
+//
+// The projections of the block (QKV, output, MLP in/out; linear1/linear2 of
+// the single-stream block) are dense contractions: the Luminal blog ("The
+// AMD MI300X pipeline") runs them as bf16 GEMMs accumulating in fp32 with
+// fused bias epilogues; here the epilogue also carries GELU, the gated
+// residual add and the Euler update. Int8 weight-only layers
+// (flux-amd-rocm benchmarks page) keep int8 codes in HBM and apply the
+// per-channel scale to the fp32 sum.
+//
+// Operand formats: the weights are bf16 (or int8 codes) in HBM and LDS; each
+// weight fragment is converted in registers to fp16, which is exact (bf16's
+// 8-bit significand fits fp16's 11 bits; int8 codes are small integers) for
+// every weight of magnitude >= 2^-14 (smaller ones round at 2^-24). The
+// activation operand A (LayerNorm outputs, attention output, GELU hidden) is
+// stored in fp16 by the kernel that produced it: at FLUX size, bf16 storage
+// of these activations alone puts the block output at ~2e-2 of its RMS away
+// from the exact result, fp16 storage at ~4e-3. The fp16 and bf16 MFMA
+// rates are equal on gfx950.
+//
+// Shape of the kernel (gfx950, 64-wide wavefronts):
+// * workgroup tile 256 (rows of A) x 256 (rows of W) x 64 (k), 4 wavefronts in
+//   a 2 x 2 arrangement, each owning a 128 x 128 sub-tile = 8 x 8 MFMA tiles
+//   of v_mfma_f32_16x16x32_f16 (256 fp32 accumulators per lane);
+// * W is the MFMA's first operand and A the second, so the hardware result
+//   is the transposed tile and each lane ends up with 4 consecutive output
+//   columns of one row: 8-byte 16-bit / 16-byte fp32 epilogue stores;
+// * both operand tiles go HBM/L2 -> LDS with 16-byte direct-to-LDS loads
+//   (no VGPR staging), double-buffered; rows are 128 B in LDS with the
+//   16-byte chunk c of row r stored at position c ^ ((r >> 1) & 7), so the
+//   16 lanes that read one MFMA operand (16 rows, same chunk) hit 16
+//   distinct 16-byte bank groups;
+// * one barrier per k-step: all fragments of the current stage are read into
+//   registers before the next stage's loads are issued;
+// * grouped launch: up to two weight sets (text / image stream) over
+//   disjoint row ranges in one grid;
+// * M and N tails: loads clamp to the last valid row, stores are guarded;
+// * deterministic (no atomics, fixed k order).
+#include "common.h"
+
+namespace mmdit {
+
+namespace {
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int NTHREADS = 256;
+constexpr int A_TILE_BYTES = BM * BK * 2;   // 32 KB
+constexpr int W_TILE_BYTES_BF16 = BN * BK * 2;  // 32 KB
+constexpr int W_TILE_BYTES_I8 = BN * BK;        // 16 KB
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+MMDIT_DEV void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// 16-byte direct global -> LDS load: lane i of the wavefront writes
+// lds_base + 16 * i.
+MMDIT_DEV void g2l_16(const void* gsrc, lds_void* lds_base) {
+    __builtin_amdgcn_global_load_lds(gsrc, lds_base, 16, 0, 0);
+}
+
+// Read an activation fragment (8 fp16) from LDS.
+MMDIT_DEV f16x8_t lds_frag_h(const char* p) { return *reinterpret_cast<const f16x8_t*>(p); }
+
+// 8 bf16 weights (one 16-byte LDS read) -> 8 fp16, pairwise.
+MMDIT_DEV f16x8_t bf16x8_to_f16x8(uint4 v) {
+    f16x8_t r;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[2 * i] = static_cast<_Float16>(__uint_as_float(w[i] << 16));
+        r[2 * i + 1] = static_cast<_Float16>(__uint_as_float(w[i] & 0xffff0000u));
+    }
+    return r;
+}
+
+// 8 int8 codes -> 8 fp16 (exact), pairwise.
+MMDIT_DEV f16x8_t i8x8_to_f16x8(uint2 raw) {
+    f16x8_t r;
+    const int32_t w[2] = {(int32_t)raw.x, (int32_t)raw.y};
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float a = (float)((w[h] << (24 - 16 * i)) >> 24);
+            const float b = (float)((w[h] << (16 - 16 * i)) >> 24);
+            r[4 * h + 2 * i] = static_cast<_Float16>(a);
+            r[4 * h + 2 * i + 1] = static_cast<_Float16>(b);
+        }
+    return r;
+}
+
+struct TileCoord {
+    int g;       // group
+    int m0;      // first row of the tile within the group
+    int n0;      // first output column
+};
+
+MMDIT_DEV TileCoord tile_of(const GemmArgs& a, int bid) {
+    const int tn = (a.n + BN - 1) / BN;
+    const int t0 = ((a.g[0].m + BM - 1) / BM) * tn;
+    TileCoord c;
+    if (bid < t0 || a.ngroups == 1) {
+        c.g = 0;
+    } else {
+        c.g = 1;
+        bid -= t0;
+    }
+    c.m0 = (bid / tn) * BM;
+    c.n0 = (bid % tn) * BN;
+    return c;
+}
+
+}  // namespace
+
+template <bool INT8, int EPI>
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) {
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    constexpr int WT = INT8 ? W_TILE_BYTES_I8 : W_TILE_BYTES_BF16;
+    constexpr int STAGE = A_TILE_BYTES + WT;
+    // stage s: A tile at smem + s*STAGE, W tile right after it
+
+    const TileCoord tc = tile_of(args, blockIdx.x);
+    const GemmGroup& G = args.g[tc.g];
+    const int M = G.m, N = args.n, K = args.k;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    const uint16_t* __restrict__ A = args.a + (size_t)G.row0 * args.lda;
+    const int lda = args.lda;
+
+    // ---- per-lane load descriptors. A tile: 256 rows x 8 chunks; each
+    // wavefront issues 8 loads of 8 rows. Lane i of load j covers row
+    // r = (wave*8 + j)*8 + i/8 at LDS position p = i%8, fetching chunk
+    // c = p ^ ((r >> 1) & 7).
+    const int lrow = lane >> 3, lpos = lane & 7;
+    const uint16_t* a_src[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int r = (wave * 8 + j) * 8 + lrow;
+        const int c = lpos ^ ((r >> 1) & 7);
+        int gr = tc.m0 + r;
+        gr = gr < M ? gr : M - 1;
+        a_src[j] = A + (size_t)gr * lda + c * 8;
+    }
+    // W tile. bf16: same pattern as A over N rows. int8: 64 B per row = 4
+    // chunks of 16 codes; a load covers 16 rows; unit u of row r stored at
+    // position u ^ ((r >> 2) & 3).
+    const char* w_src[8];
+    if (!INT8) {
+        const uint16_t* W = static_cast<const uint16_t*>(G.w);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r = (wave * 8 + j) * 8 + lrow;
+            const int c = lpos ^ ((r >> 1) & 7);
+            int gn = tc.n0 + r;
+            gn = gn < N ? gn : N - 1;
+            w_src[j] = reinterpret_cast<const char*>(W + (size_t)gn * K + c * 8);
+        }
+    } else {
+        const int8_t* W = static_cast<const int8_t*>(G.w);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = (wave * 4 + j) * 16 + (lane >> 2);
+            const int u = (lane & 3) ^ ((r >> 2) & 3);
+            int gn = tc.n0 + r;
+            gn = gn < N ? gn : N - 1;
+            w_src[j] = reinterpret_cast<const char*>(W + (size_t)gn * K + u * 16);
+        }
+    }
+
+    auto issue_stage = [&](int kt, int s) {
+        char* base = smem + s * STAGE;
+        const int k0 = kt * BK;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            g2l_16(a_src[j] + k0, (lds_void*)(base + ((wave * 8 + j) * 8) * 128));
+        char* wb = base + A_TILE_BYTES;
+        if (!INT8) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                g2l_16(w_src[j] + k0 * 2, (lds_void*)(wb + ((wave * 8 + j) * 8) * 128));
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                g2l_16(w_src[j] + k0, (lds_void*)(wb + ((wave * 4 + j) * 16) * 64));
+        }
+    };
+
+    // ---- per-lane fragment offsets. Operand rows: lane & 15; k chunk:
+    // ks*4 + (lane >> 4) for k-substep ks of the 64-wide stage.
+    const int lr = lane & 15, lg = lane >> 4;
+    int a_off[2], w_off[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const int c = ks * 4 + lg;
+        a_off[ks] = (wm * 128 + lr) * 128 + ((c ^ ((lr >> 1) & 7)) * 16);
+        if (!INT8)
+            w_off[ks] = (wn * 128 + lr) * 128 + ((c ^ ((lr >> 1) & 7)) * 16);
+        else
+            w_off[ks] = (wn * 128 + lr) * 64 + (((c >> 1) ^ ((lr >> 2) & 3)) * 16) + (c & 1) * 8;
+    }
+
+    f32x4_t acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = K / BK;
+    issue_stage(0, 0);
+    wait_vmcnt0();
+    __syncthreads();
+
+    for (int kt = 0; kt < nk; ++kt) {
+        const int s = kt & 1;
+        const char* sa = smem + s * STAGE;
+        const char* sw = sa + A_TILE_BYTES;
+        f16x8_t fa[2][8], fw[2][8];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) fa[ks][i] = lds_frag_h(sa + a_off[ks] + i * 16 * 128);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (!INT8)
+                    fw[ks][i] = bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(sw + w_off[ks] + i * 16 * 128));
+                else
+                    fw[ks][i] = i8x8_to_f16x8(*reinterpret_cast<const uint2*>(sw + w_off[ks] + i * 16 * 64));
+            }
+        }
+        if (kt + 1 < nk) issue_stage(kt + 1, s ^ 1);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int in = 0; in < 8; ++in)
+#pragma unroll
+                for (int im = 0; im < 8; ++im)
+                    acc[in][im] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fw[ks][in], fa[ks][im],
+                                                                         acc[in][im], 0, 0, 0);
+        // keep the stage wait and the barrier behind the MFMAs (the compiler
+        // would otherwise hoist them, serialising the loads with the math)
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt0();
+        __syncthreads();
+    }
+
+    // ---- epilogue. acc[in][im] element j: output column
+    // n = n0 + wn*128 + in*16 + lg*4 + j, row m = m0 + wm*128 + im*16 + lr.
+    const int nb = tc.n0 + wn * 128 + lg * 4;
+    const int mb = tc.m0 + wm * 128 + lr;
+#pragma unroll
+    for (int in = 0; in < 8; ++in) {
+        const int n = nb + in * 16;
+        if (n >= N) continue;
+        const uint2 braw = *reinterpret_cast<const uint2*>(G.bias + n);
+        const float b[4] = {bf2f(braw.x & 0xffff), bf2f(braw.x >> 16), bf2f(braw.y & 0xffff),
+                            bf2f(braw.y >> 16)};
+        float sc[4] = {1.f, 1.f, 1.f, 1.f};
+        if (INT8) {
+            const float4 s4 = *reinterpret_cast<const float4*>(G.scale + n);
+            sc[0] = s4.x; sc[1] = s4.y; sc[2] = s4.z; sc[3] = s4.w;
+        }
+        float gt[4] = {0.f, 0.f, 0.f, 0.f};
+        if (EPI == MMDIT_EPI_GATE_RESID) {
+            const float4 g4 = *reinterpret_cast<const float4*>(G.gate + n);
+            gt[0] = g4.x; gt[1] = g4.y; gt[2] = g4.z; gt[3] = g4.w;
+        }
+#pragma unroll
+        for (int im = 0; im < 8; ++im) {
+            const int m = mb + im * 16;
+            if (m >= M) continue;
+            const size_t grow = (size_t)(G.row0 + m);
+            float y[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[j] = acc[in][im][j] * sc[j] + b[j];
+            if (EPI == MMDIT_EPI_BIAS || (EPI == MMDIT_EPI_SPLIT_GELU && n < args.split_n)) {
+                // attention-side operands (q, k, v): bf16
+                uint16_t* o = static_cast<uint16_t*>(args.out) + grow * args.ldo + n;
+                *reinterpret_cast<uint2*>(o) = make_uint2(pack2bf(y[0], y[1]), pack2bf(y[2], y[3]));
+            } else if (EPI == MMDIT_EPI_BIAS_GELU) {
+                // MLP hidden, the next projection's activation operand: fp16
+#pragma unroll
+                for (int j = 0; j < 4; ++j) y[j] = gelu_tanh(y[j]);
+                uint16_t* o = static_cast<uint16_t*>(args.out) + grow * args.ldo + n;
+                *reinterpret_cast<uint2*>(o) = make_uint2(pack2h(y[0], y[1]), pack2h(y[2], y[3]));
+            } else if (EPI == MMDIT_EPI_SPLIT_GELU) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) y[j] = gelu_tanh(y[j]);
+                uint16_t* o = static_cast<uint16_t*>(args.out2) + grow * args.ldo2 + args.out2_col +
+                              (n - args.split_n);
+                *reinterpret_cast<uint2*>(o) = make_uint2(pack2h(y[0], y[1]), pack2h(y[2], y[3]));
+            } else if (EPI == MMDIT_EPI_GATE_RESID) {
+                const float4 r = *reinterpret_cast<const float4*>(args.resid + grow * args.ldr + n);
+                float4 o4 = make_float4(r.x + gt[0] * y[0], r.y + gt[1] * y[1], r.z + gt[2] * y[2],
+                                        r.w + gt[3] * y[3]);
+                *reinterpret_cast<float4*>(static_cast<float*>(args.out) + grow * args.ldo + n) = o4;
+            } else if (EPI == MMDIT_EPI_BIAS_F32) {
+                *reinterpret_cast<float4*>(static_cast<float*>(args.out) + grow * args.ldo + n) =
+                    make_float4(y[0], y[1], y[2], y[3]);
+            } else if (EPI == MMDIT_EPI_EULER) {
+                float* o = static_cast<float*>(args.out) + grow * args.ldo + n;
+                float4 z = *reinterpret_cast<float4*>(o);
+                z.x += args.alpha * y[0]; z.y += args.alpha * y[1];
+                z.z += args.alpha * y[2]; z.w += args.alpha * y[3];
+                *reinterpret_cast<float4*>(o) = z;
+            }
+        }
+    }
+}
+
+template <bool INT8>
+static hipError_t launch_gemm_t(const GemmArgs& a, hipStream_t s) {
+    const int tn = (a.n + BN - 1) / BN;
+    int tiles = 0;
+    for (int g = 0; g < a.ngroups; ++g) tiles += ((a.g[g].m + BM - 1) / BM) * tn;
+    if (tiles == 0) return hipSuccess;
+    const size_t lds = 2 * (size_t)(A_TILE_BYTES + (INT8 ? W_TILE_BYTES_I8 : W_TILE_BYTES_BF16));
+    dim3 grid(tiles), block(NTHREADS);
+#define GEMM_CASE(E)                                                                        \
+    case E: {                                                                               \
+        auto kfn = gemm_kernel<INT8, E>;                                                    \
+        static bool attr_done = false;                                                      \
+        if (!attr_done) {                                                                   \
+            hipError_t e = hipFuncSetAttribute((const void*)kfn,                            \
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, \
+                                               (int)lds);                                   \
+            if (e != hipSuccess) return e;                                                  \
+            attr_done = true;                                                               \
+        }                                                                                   \
+        hipLaunchKernelGGL(kfn, grid, block, lds, s, a);                                    \
+        break;                                                                              \
+    }
+    switch (a.epilogue) {
+        GEMM_CASE(MMDIT_EPI_BIAS)
+        GEMM_CASE(MMDIT_EPI_BIAS_GELU)
+        GEMM_CASE(MMDIT_EPI_GATE_RESID)
+        GEMM_CASE(MMDIT_EPI_SPLIT_GELU)
+        GEMM_CASE(MMDIT_EPI_BIAS_F32)
+        GEMM_CASE(MMDIT_EPI_EULER)
+        default:
+            return hipErrorInvalidValue;
+    }
+#undef GEMM_CASE
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
+    return a.int8 ? launch_gemm_t<true>(a, s) : launch_gemm_t<false>(a, s);
+}
+
+}  // namespace mmdit

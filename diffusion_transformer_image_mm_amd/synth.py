@@ -117,6 +117,11 @@ def bf16_exact(x: np.ndarray) -> np.ndarray:
     return bits_to_f32(bf16_bits(x))
 
 
+def f16_exact(x: np.ndarray) -> np.ndarray:
+    """float32 array holding the IEEE fp16-rounded values of ``x``."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16).astype(np.float32)
+
+
 # --------------------------------------------------------------------------
 # seeded draws
 # --------------------------------------------------------------------------

@@ -1,0 +1,339 @@
+/*
+ * mmdit.h - C ABI of the MI355X (gfx950) MM-DiT block library, libmmdit.so.
+ *
+ * The library runs the bf16 forward pass of a multimodal diffusion-transformer
+ * block (double-stream and single-stream) and one flow-matching Euler denoise
+ * step, as hand-written HIP kernels. The operations follow the Luminal blog
+ * "Reducing image generation cost with..." (sections "Flux.2 Klein 9B", "The
+ * AMD MI300X pipeline" and "What the compiler found on its own") and the
+ * flux-amd-rocm benchmarks page (28 Euler steps, guidance 3.5, int8
+ * weight-only linears).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Pointers to tensors are DEVICE pointers, except the structs themselves
+ *   (mmdit_dims, mmdit_linear, weight structs, mmdit_gemm), which live in host
+ *   memory and hold device pointers.
+ * - Every device pointer must be 16-byte aligned; every row stride (ld*)
+ *   is in elements and must keep 16-byte alignment of every row.
+ * - bf16 tensors are raw IEEE bfloat16 bit patterns (mmdit_bf16), fp16
+ *   tensors raw IEEE binary16 bit patterns (mmdit_f16); fp32 is IEEE
+ *   binary32. Matrices are row-major.
+ * - Precision: weights are bf16 (or int8 codes with fp32 scales); the
+ *   residual stream, conditioning vector, latent and RoPE table are fp32;
+ *   attention runs bf16 MFMA on bf16 q, k, v; the activation operands of the
+ *   projections (LayerNorm outputs, attention output, GELU hidden) are fp16,
+ *   and each weight fragment is converted to fp16 in registers (exact for
+ *   bf16 weights of magnitude >= 2^-14 and for int8 codes); every sum
+ *   accumulates in fp32.
+ * - The caller owns every buffer (weights, activations, tables, workspace).
+ *   The library allocates nothing, frees nothing and keeps no state between
+ *   calls; calls on different streams with distinct workspaces may overlap.
+ * - Every call only enqueues work on `stream` and returns; nothing is
+ *   synchronised. Outputs are defined once the stream has reached the work.
+ * - Arguments are validated before anything is enqueued: on a non-zero
+ *   status nothing was launched. A device fault surfaces at the caller's next
+ *   synchronisation. Status MMDIT_E_HIP reports a failed launch.
+ * - Results are deterministic: the same inputs, sizes and stream order give
+ *   bit-identical outputs (no atomics, fixed reduction order).
+ * - Batch is 1: a "sequence" is one image with its prompt.
+ */
+#ifndef MMDIT_H
+#define MMDIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MMDIT_ABI_VERSION 1
+
+/* raw bfloat16 bits */
+typedef uint16_t mmdit_bf16;
+/* raw IEEE binary16 bits */
+typedef uint16_t mmdit_f16;
+
+/* ------------------------------------------------------------------ status */
+enum mmdit_status {
+    MMDIT_OK = 0,
+    MMDIT_E_NULL = 1,      /* a required pointer is NULL */
+    MMDIT_E_ALIGN = 2,     /* a pointer or row stride breaks 16-byte alignment */
+    MMDIT_E_SHAPE = 3,     /* unsupported or inconsistent sizes */
+    MMDIT_E_DTYPE = 4,     /* unknown weight dtype, or int8 weights without scales */
+    MMDIT_E_WORKSPACE = 5, /* workspace too small */
+    MMDIT_E_HIP = 6,       /* a kernel launch failed */
+    MMDIT_E_ARG = 7        /* another invalid argument (unknown enum value) */
+};
+
+enum mmdit_weight_dtype {
+    MMDIT_BF16 = 0, /* weights are bf16 [out, in] */
+    MMDIT_INT8 = 1  /* weights are int8 codes [out, in] with fp32 scale [out]:
+                       W = diag(scale) * codes (flux-amd-rocm benchmarks page:
+                       int8 weight-only linears) */
+};
+
+/* ------------------------------------------------------------------ sizes */
+/*
+ * Sizes of one model. H = heads * head_dim.
+ *   head_dim in {64, 128}; hidden and mlp_hidden multiples of 64;
+ *   rope_axes[] even, summing to head_dim (axial RoPE over (t, h, w));
+ *   txt_len >= 1, img_len >= 1; in_channels a multiple of 64 (64 for FLUX);
+ *   n_double / n_single: block counts of a whole model (denoise step only).
+ * The joint sequence holds txt_len text tokens, then img_len image tokens.
+ */
+typedef struct mmdit_dims {
+    int32_t txt_len;
+    int32_t img_len;
+    int32_t hidden;
+    int32_t heads;
+    int32_t head_dim;
+    int32_t mlp_hidden;
+    int32_t in_channels;
+    int32_t rope_axes[3];
+    float rope_theta;   /* 1e4 */
+    float ln_eps;       /* LayerNorm epsilon, 1e-6 */
+    float rms_eps;      /* RMSNorm epsilon, 1e-6 */
+    int32_t weight_dtype; /* enum mmdit_weight_dtype */
+    int32_t n_double;
+    int32_t n_single;
+} mmdit_dims;
+
+/* ------------------------------------------------------------------ weights */
+/*
+ * One linear layer y = x W^T + b. w: [out, in] row-major, bf16 bits or int8
+ * codes per the dtype in use; scale: fp32 [out] (int8 only, else ignored);
+ * bias: bf16 [out] (required).
+ */
+typedef struct mmdit_linear {
+    const void* w;
+    const float* scale;
+    const mmdit_bf16* bias;
+} mmdit_linear;
+
+/*
+ * One stream of a double-stream block ("Flux.2 Klein 9B" section: each stream
+ * has its own projections, norm and feed-forward network).
+ *   mod  [6H, H]: SiLU(vec) -> [shift1 | scale1 | gate1 | shift2 | scale2 | gate2]
+ *   qkv  [3H, H]: columns [q | k | v], each head-major (column h*D + d)
+ *   proj [H, H], fc1 [M, H], fc2 [H, M]
+ *   q_norm, k_norm: bf16 [D] RMSNorm scales of this stream
+ */
+typedef struct mmdit_stream_weights {
+    mmdit_linear mod, qkv, proj, fc1, fc2;
+    const mmdit_bf16* q_norm;
+    const mmdit_bf16* k_norm;
+} mmdit_stream_weights;
+
+typedef struct mmdit_double_weights {
+    mmdit_stream_weights txt, img;
+} mmdit_double_weights;
+
+/*
+ * Single-stream block: one set of weights over the joint sequence.
+ *   mod     [3H, H]:   [shift | scale | gate]
+ *   linear1 [3H+M, H]: columns [q | k | v | mlp]
+ *   linear2 [H, H+M]:  input [attention | GELU(mlp)]
+ */
+typedef struct mmdit_single_weights {
+    mmdit_linear mod, linear1, linear2;
+    const mmdit_bf16* q_norm;
+    const mmdit_bf16* k_norm;
+} mmdit_single_weights;
+
+/*
+ * A whole denoiser. img_in [H, C]; time_in / guid_in: Linear(256 -> H), SiLU,
+ * Linear(H -> H) of the sinusoidal embedding; final_mod [2H, H] ->
+ * [shift | scale]; final_out [C, H]. doubles / singles: HOST arrays of
+ * n_double / n_single block weight structs.
+ */
+typedef struct mmdit_model {
+    mmdit_linear img_in;
+    mmdit_linear time_in[2];
+    mmdit_linear guid_in[2];
+    mmdit_linear final_mod;
+    mmdit_linear final_out;
+    const mmdit_double_weights* doubles;
+    const mmdit_single_weights* singles;
+} mmdit_model;
+
+/* ------------------------------------------------------------------ blocks */
+enum mmdit_workspace_kind {
+    MMDIT_WS_DOUBLE = 0,
+    MMDIT_WS_SINGLE = 1,
+    MMDIT_WS_STEP = 2
+};
+
+/* Bytes of workspace the given call needs for these sizes (0 on bad sizes). */
+size_t mmdit_workspace_bytes(const mmdit_dims* dims, int kind);
+
+/*
+ * Double-stream block forward (Luminal blog, "Flux.2 Klein 9B" and "What the
+ * compiler found on its own"): per stream, modulation of SiLU(vec),
+ * LayerNorm + modulate, QKV projection, per-head RMSNorm of q and k; over the
+ * joint sequence, axial RoPE and softmax attention without a mask; per
+ * stream, output projection with gated residual, LayerNorm + modulate, GELU
+ * MLP with gated residual.
+ *   vec:   fp32 [H] conditioning vector
+ *   rope:  fp32 [L, D/2, 2] (cos, sin) per rotated pair (mmdit_rope_table)
+ *   x_in:  fp32 [L, H] joint residual stream, text rows first
+ *   x_out: fp32 [L, H]; may alias x_in
+ *   ws:    device workspace of at least mmdit_workspace_bytes(MMDIT_WS_DOUBLE)
+ */
+int mmdit_block_forward(const mmdit_dims* dims, const mmdit_double_weights* w,
+                        const float* vec, const float* rope,
+                        const float* x_in, float* x_out,
+                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Single-stream block forward: modulation, LayerNorm + modulate, linear1
+ * (q|k|v|mlp), RMSNorm + RoPE on q and k, attention, linear2 over
+ * [attention | GELU(mlp)], gated residual. Arguments as mmdit_block_forward.
+ */
+int mmdit_single_block_forward(const mmdit_dims* dims, const mmdit_single_weights* w,
+                               const float* vec, const float* rope,
+                               const float* x_in, float* x_out,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * One flow-matching Euler denoise step (flux-amd-rocm benchmarks page:
+ * FLUX.1-dev, guidance 3.5; Luminal blog, "The AMD MI300X pipeline": the
+ * latent is integrated in fp32):
+ *   vec = MLP_t(emb(t_cur)) + MLP_g(emb(guidance)), emb = [cos | sin] of
+ *   1000*t times 128 geometric frequencies (max period 1e4);
+ *   x = [txt | img_in(latent)]; n_double double blocks; n_single single
+ *   blocks; v = final_out(LayerNorm(x_img) * (1 + scale) + shift);
+ *   latent += (t_next - t_cur) * v.
+ *   latent: fp32 [img_len, in_channels], updated in place
+ *   txt:    fp32 [txt_len, H] text states
+ *   rope:   fp32 [L, D/2, 2]
+ *   dims->weight_dtype selects bf16 or int8 weights for every linear.
+ */
+int mmdit_denoise_step(const mmdit_dims* dims, const mmdit_model* model,
+                       float* latent, const float* txt, const float* rope,
+                       float t_cur, float t_next, float guidance,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * RoPE table from axial position ids: ids int32 [L, 3] (t, h, w) on the
+ * device; rope fp32 [L, D/2, 2]. Pair p of the head dim belongs to axis a
+ * (consecutive segments of rope_axes[0], [1], [2] dims); its j-th pair in
+ * that axis turns by ids[l][a] * theta^(-2j / rope_axes[a]) (Luminal blog,
+ * "What the compiler found on its own": cosine and sine tables).
+ */
+int mmdit_rope_table(const mmdit_dims* dims, const int32_t* ids, float* rope,
+                     hipStream_t stream);
+
+const char* mmdit_status_string(int status);
+int mmdit_abi_version(void);
+
+/* ------------------------------------------------------------------ kernels */
+/*
+ * Single-kernel entry points, used by the block calls and exposed for tests
+ * and per-kernel measurement. Same conventions as above.
+ */
+
+/*
+ * LayerNorm (no affine, biased variance) + adaLN modulate ("What the compiler
+ * found on its own": a mean, a subtraction, a reciprocal square root, then a
+ * scale and a shift): out = LN(x) * (1 + scale) + shift.
+ *   x: fp32 [rows, hidden]; rows < split take (shift0, scale0), the others
+ *   (shift1, scale1), each fp32 [hidden]; out: fp16 [rows, hidden].
+ */
+int mmdit_k_ln_modulate(const float* x, int rows, int hidden, int split,
+                        const float* shift0, const float* scale0,
+                        const float* shift1, const float* scale1,
+                        float eps, mmdit_f16* out, hipStream_t stream);
+
+/*
+ * Per-head RMSNorm of q and k, then axial RoPE, then relayout for attention
+ * ("What the compiler found on its own": square, sum, reciprocal square root,
+ * multiply; partner gather and multiply-add against cos/sin tables).
+ *   qkv: bf16 [seq_len, ld]; q at columns [0, H), k at [H, 2H), v at [2H, 3H)
+ *   rows < split use (q_norm0, k_norm0), the others (q_norm1, k_norm1): bf16 [D]
+ *   rope: fp32 [seq_len, D/2, 2]
+ *   q_out, k_out: bf16 [heads, l_pad, D]; vt_out: bf16 [heads, D, l_pad]
+ *   l_pad: a multiple of 64, >= seq_len; rows [seq_len, l_pad) are written as 0.
+ */
+int mmdit_k_qknorm_rope(const mmdit_bf16* qkv, int ld, int seq_len, int heads, int head_dim,
+                        int split, const mmdit_bf16* q_norm0, const mmdit_bf16* k_norm0,
+                        const mmdit_bf16* q_norm1, const mmdit_bf16* k_norm1,
+                        const float* rope, float eps, int l_pad,
+                        mmdit_bf16* q_out, mmdit_bf16* k_out, mmdit_bf16* vt_out,
+                        hipStream_t stream);
+
+/*
+ * Softmax attention without a mask (Luminal blog, "What the compiler found on
+ * its own" and "The AMD MI300X pipeline": fused, tiled softmax(QK^T)V).
+ *   q, k: bf16 [heads, l_pad, D]; vt: bf16 [heads, D, l_pad], as written by
+ *   mmdit_k_qknorm_rope (zero beyond seq_len); scale 1/sqrt(D).
+ *   out: fp16 [seq_len, ldo], head h at columns [h*D, (h+1)*D).
+ */
+int mmdit_k_attention(const mmdit_bf16* q, const mmdit_bf16* k, const mmdit_bf16* vt,
+                      int heads, int seq_len, int head_dim, int l_pad,
+                      mmdit_f16* out, int ldo, hipStream_t stream);
+
+/* GEMM epilogues (bias is always added first: y = acc * s + b, s = 1 for bf16) */
+enum mmdit_epilogue {
+    MMDIT_EPI_BIAS = 0,       /* out bf16 [m, ldo] = y (q, k, v for attention) */
+    MMDIT_EPI_BIAS_GELU = 1,  /* out fp16 = GELU_tanh(y) (MLP hidden) */
+    MMDIT_EPI_GATE_RESID = 2, /* out fp32 = resid + gate[n] * y (out may alias resid) */
+    MMDIT_EPI_SPLIT_GELU = 3, /* columns n < split_n: out bf16 [m, ldo] col n = y;
+                                 n >= split_n: out2 fp16 [m, ldo2] col
+                                 out2_col + n - split_n = GELU_tanh(y) */
+    MMDIT_EPI_BIAS_F32 = 4,   /* out fp32 [m, ldo] = y */
+    MMDIT_EPI_EULER = 5       /* out fp32 [m, ldo] += alpha * y (the Euler update) */
+};
+
+/*
+ * out = epilogue(A W^T): A fp16 [m, k] (row stride lda), W = w.w [n, k] bf16
+ * or int8 (weight_dtype). k a multiple of 64, n a multiple of 64, m >= 1.
+ * Weight fragments are converted to fp16 in registers (exact, see above);
+ * accumulation in fp32; the int8 per-channel scale multiplies the fp32 sum.
+ */
+typedef struct mmdit_gemm {
+    int32_t m, n, k;
+    int32_t weight_dtype;
+    const mmdit_f16* a;
+    int32_t lda;
+    mmdit_linear w;
+    int32_t epilogue;
+    void* out;
+    int32_t ldo;
+    const float* gate;  /* fp32 [n], GATE_RESID */
+    const float* resid; /* fp32 [m, ldr], GATE_RESID */
+    int32_t ldr;
+    int32_t split_n;    /* SPLIT_GELU */
+    void* out2;
+    int32_t ldo2;
+    int32_t out2_col;
+    float alpha;        /* EULER */
+} mmdit_gemm;
+
+int mmdit_k_gemm(const mmdit_gemm* g, hipStream_t stream);
+
+/*
+ * out[n] (+)= W act(x) + b for one vector (modulation and embedder layers):
+ *   x fp32 [k]; act = SiLU if silu_input else identity; W [n, k] bf16 or int8;
+ *   accumulate: 0 writes out, 1 adds to it. out fp32 [n].
+ */
+int mmdit_k_gemv(const float* x, int k, const mmdit_linear* w, int n, int weight_dtype,
+                 int silu_input, int accumulate, float* out, hipStream_t stream);
+
+/*
+ * Conditioning vector vec fp32 [H] = MLP_t(emb(t)) + MLP_g(emb(guidance)).
+ * ws: device scratch of at least 4 * (512 + 2 * H) bytes.
+ */
+int mmdit_k_time_embed(const mmdit_dims* dims, const mmdit_model* model, float t,
+                       float guidance, float* vec, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/* Euler update z[i] += dt * v[i], fp32, n elements. */
+int mmdit_k_euler(float* z, const float* v, int64_t n, float dt, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MMDIT_H */

@@ -1,0 +1,75 @@
+"""Helpers shared by the GPU parity tests: error metrics and device plumbing."""
+import sys
+
+import numpy as np
+import torch
+
+from diffusion_transformer_image_mm_amd import binding as B
+from diffusion_transformer_image_mm_amd.device import DeviceArena, dims_for, to_numpy_f32  # noqa: F401
+
+# Bar for floating-point parity: max |gpu - oracle| / RMS(oracle).
+TOL = 2e-2
+
+
+def rel_err(gpu, ref) -> float:
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    assert np.all(np.isfinite(gpu)), "non-finite GPU output"
+    rms = np.sqrt(np.mean(ref * ref))
+    return float(np.max(np.abs(gpu - ref)) / max(rms, 1e-30))
+
+
+def ulp(ref, fmt: str) -> np.ndarray:
+    """Spacing of bf16 (8-bit significand) or fp16 (11-bit) numbers at |ref|."""
+    a = np.abs(np.asarray(ref, dtype=np.float64))
+    if fmt == "bf16":
+        return 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -126))) - 7)
+    assert fmt == "f16"
+    return np.where(a < 2.0 ** -14, 2.0 ** -24, 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -14))) - 10))
+
+
+def bf16_ulp(ref) -> np.ndarray:
+    return ulp(ref, "bf16")
+
+
+def rel_err_rounded_out(gpu, ref, fmt: str) -> float:
+    """rel_err for a kernel whose output is stored in a 16-bit format: the
+    part of |gpu - ref| beyond half a step of that format at ref (the
+    representation band every such output must lose), over RMS(ref).
+    Rounding alone can reach ~2.5e-2 of the RMS for heavy-tailed bf16
+    outputs; this measures the arithmetic error."""
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape and np.all(np.isfinite(g))
+    excess = np.maximum(np.abs(g - r) - 0.5 * ulp(r, fmt), 0.0)
+    return float(np.max(excess) / max(np.sqrt(np.mean(r * r)), 1e-30))
+
+
+def rel_err_bf16_out(gpu, ref) -> float:
+    return rel_err_rounded_out(gpu, ref, "bf16")
+
+
+def within_one_ulp(gpu, ref, fmt: str, abs_floor=1e-6) -> float:
+    """Largest |gpu - ref| in units of the format's step at ref."""
+    d = np.abs(np.asarray(gpu, np.float64) - np.asarray(ref, np.float64))
+    return float(np.max(d / (ulp(ref, fmt) + abs_floor)))
+
+
+def within_one_bf16_ulp(gpu, ref, abs_floor=1e-6) -> float:
+    """Largest |gpu - ref| in units of bf16 ulp(ref) (1 = one rounding step)."""
+    d = np.abs(np.asarray(gpu, np.float64) - np.asarray(ref, np.float64))
+    return float(np.max(d / (bf16_ulp(ref) + abs_floor)))
+
+
+def say(*a):
+    """Print a progress line that names the case (flushed before GPU work)."""
+    print(*a, file=sys.stderr, flush=True)
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+def stream():
+    return torch.cuda.current_stream()

@@ -1,0 +1,139 @@
+"""The C-ABI library loads, exports every function include/mmdit.h declares,
+and rejects bad arguments on the host before launching anything (these
+calls return an error status without touching a GPU)."""
+import ctypes
+
+import pytest
+
+from diffusion_transformer_image_mm_amd import binding as B
+from diffusion_transformer_image_mm_amd import synth
+from diffusion_transformer_image_mm_amd.device import dims_for
+
+FAKE = 1 << 20  # a 16-byte aligned, never-dereferenced address
+
+
+def test_exports_every_header_function():
+    names = B.header_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(B.lib, n), n
+        assert callable(getattr(B, n)), n
+
+
+def test_abi_version_and_status_strings():
+    assert B.mmdit_abi_version() == 1
+    for st in range(8):
+        assert B.mmdit_status_string(st)
+    assert B.mmdit_status_string(99) == "unknown status"
+
+
+def _dims(**kw):
+    d = dims_for(synth.TINY)
+    for k, v in kw.items():
+        if k == "rope_axes":
+            for i in range(3):
+                d.rope_axes[i] = v[i]
+        else:
+            setattr(d, k, v)
+    return d
+
+
+def _linear():
+    return B.mmdit_linear(FAKE, 0, FAKE)
+
+
+def _double():
+    s = B.mmdit_stream_weights(_linear(), _linear(), _linear(), _linear(), _linear(), FAKE, FAKE)
+    return B.mmdit_double_weights(s, s)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"head_dim": 96, "hidden": 384}, B.MMDIT_E_SHAPE),
+    ({"hidden": 320}, B.MMDIT_E_SHAPE),            # hidden != heads * head_dim
+    ({"rope_axes": (8, 28, 26)}, B.MMDIT_E_SHAPE),  # axes do not sum to D
+    ({"rope_axes": (9, 27, 28)}, B.MMDIT_E_SHAPE),  # odd axis
+    ({"txt_len": 0}, B.MMDIT_E_SHAPE),
+    ({"img_len": 0}, B.MMDIT_E_SHAPE),
+    ({"mlp_hidden": 1000}, B.MMDIT_E_SHAPE),
+    ({"weight_dtype": 5}, B.MMDIT_E_DTYPE),
+])
+def test_block_rejects_bad_dims(kw, status):
+    d = _dims(**kw)
+    assert B.mmdit_workspace_bytes(d, B.MMDIT_WS_DOUBLE) == 0
+    w = _double()
+    assert B.mmdit_block_forward(d, w, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40) == status
+
+
+def test_block_rejects_null_misaligned_small_workspace_and_missing_scales():
+    d = _dims()
+    w = _double()
+    need = B.mmdit_workspace_bytes(d, B.MMDIT_WS_DOUBLE)
+    assert need > 0
+    assert B.mmdit_block_forward(d, w, 0, FAKE, FAKE, FAKE, FAKE, need) == B.MMDIT_E_NULL
+    assert B.mmdit_block_forward(d, w, FAKE + 4, FAKE, FAKE, FAKE, FAKE, need) == B.MMDIT_E_ALIGN
+    assert B.mmdit_block_forward(d, w, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1) == B.MMDIT_E_WORKSPACE
+    w.img.fc2.bias = 0
+    assert B.mmdit_block_forward(d, w, FAKE, FAKE, FAKE, FAKE, FAKE, need) == B.MMDIT_E_NULL
+    d8 = _dims(weight_dtype=B.MMDIT_INT8)
+    assert B.mmdit_block_forward(d8, _double(), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40) == B.MMDIT_E_DTYPE
+
+
+def test_single_and_step_validation():
+    d = _dims()
+    sw = B.mmdit_single_weights(_linear(), _linear(), _linear(), FAKE, FAKE)
+    need = B.mmdit_workspace_bytes(d, B.MMDIT_WS_SINGLE)
+    assert B.mmdit_single_block_forward(d, sw, FAKE, FAKE, FAKE, FAKE, FAKE, need - 256) == B.MMDIT_E_WORKSPACE
+    sw.q_norm = FAKE + 2
+    assert B.mmdit_single_block_forward(d, sw, FAKE, FAKE, FAKE, FAKE, FAKE, need) == B.MMDIT_E_ALIGN
+    m = B.mmdit_model()
+    for f in ("img_in", "final_mod", "final_out"):
+        setattr(m, f, _linear())
+    for i in range(2):
+        m.time_in[i] = _linear()
+        m.guid_in[i] = _linear()
+    d.n_double, d.n_single = 1, 0
+    assert B.mmdit_denoise_step(d, m, FAKE, FAKE, FAKE, 1.0, 0.9, 3.5, FAKE, 1 << 40) == B.MMDIT_E_NULL  # no doubles
+    d.n_double = 0
+    need = B.mmdit_workspace_bytes(d, B.MMDIT_WS_STEP)
+    assert B.mmdit_denoise_step(d, m, FAKE, FAKE, FAKE, 1.0, 0.9, 3.5, FAKE, need - 1) == B.MMDIT_E_WORKSPACE
+    assert B.mmdit_denoise_step(d, m, FAKE, FAKE, FAKE, float("nan"), 0.9, 3.5, FAKE, need) == B.MMDIT_E_ARG
+    d.in_channels = 48
+    assert B.mmdit_denoise_step(d, m, FAKE, FAKE, FAKE, 1.0, 0.9, 3.5, FAKE, need) == B.MMDIT_E_SHAPE
+
+
+def test_kernel_entry_validation():
+    assert B.mmdit_k_ln_modulate(FAKE, 10, 100, 0, FAKE, FAKE, FAKE, FAKE, 1e-6, FAKE) == B.MMDIT_E_SHAPE
+    assert B.mmdit_k_ln_modulate(FAKE, 10, 256, 0, FAKE, FAKE, FAKE, FAKE, 0.0, FAKE) == B.MMDIT_E_ARG
+    assert B.mmdit_k_attention(FAKE, FAKE, FAKE, 4, 100, 64, 96, FAKE, 256) == B.MMDIT_E_SHAPE  # l_pad % 64
+    assert B.mmdit_k_attention(FAKE, FAKE, FAKE, 4, 100, 80, 128, FAKE, 320) == B.MMDIT_E_SHAPE
+    assert B.mmdit_k_qknorm_rope(FAKE, 768, 100, 4, 64, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1e-6, 100,
+                                 FAKE, FAKE, FAKE) == B.MMDIT_E_SHAPE
+    g = B.mmdit_gemm(m=10, n=100, k=64, weight_dtype=0, a=FAKE, lda=64, w=_linear(), epilogue=0, out=FAKE, ldo=128)
+    assert B.mmdit_k_gemm(g) == B.MMDIT_E_SHAPE  # n not a multiple of 64
+    g.n = 128
+    g.epilogue = 9
+    assert B.mmdit_k_gemm(g) == B.MMDIT_E_ARG
+    g.epilogue = B.MMDIT_EPI_GATE_RESID
+    assert B.mmdit_k_gemm(g) == B.MMDIT_E_NULL  # gate / resid missing
+    g.epilogue, g.weight_dtype = 0, B.MMDIT_INT8
+    assert B.mmdit_k_gemm(g) == B.MMDIT_E_DTYPE  # int8 without scales
+    lin = _linear()
+    assert B.mmdit_k_gemv(FAKE, 100, lin, 10, 0, 1, 0, FAKE) == B.MMDIT_E_SHAPE
+    assert B.mmdit_k_euler(FAKE + 8, FAKE, 10, 0.1) == B.MMDIT_E_ALIGN
+
+
+def test_one_hip_runtime_per_process():
+    """The library needs only the HIP runtime (by SONAME) and the binding
+    loads PyTorch's runtime before it, so a process never holds two HSA
+    runtimes (the system one next to PyTorch's)."""
+    import subprocess
+    import sys
+    out = subprocess.run(["readelf", "-d", B.LIB_PATH], capture_output=True, text=True).stdout
+    needed = [l for l in out.splitlines() if "NEEDED" in l]
+    assert any("libamdhip64.so" in l for l in needed)
+    assert not any("libhsa-runtime64" in l for l in needed), needed
+    code = ("import sys; import diffusion_transformer_image_mm_amd.binding as b; "
+            "print('torch' in sys.modules)")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       cwd=__import__("os").path.dirname(__import__("os").path.dirname(__file__)))
+    assert r.stdout.strip() == "True", r.stderr

@@ -1,0 +1,329 @@
+"""Per-kernel parity of the HIP path against the CPU oracle, through the C ABI.
+
+Every case feeds both sides the same seeded bf16-exact inputs. Sizes span
+several tiles and ragged tails; the full-size cases check sampled outputs."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from diffusion_transformer_image_mm_amd import binding as B
+from diffusion_transformer_image_mm_amd import synth
+from gpu_helpers import (TOL, DeviceArena, rel_err, rel_err_bf16_out, rel_err_rounded_out, say, stream, sync,
+                         to_numpy_f32, within_one_bf16_ulp, within_one_ulp)
+
+pytestmark = pytest.mark.gpu
+CID = 700
+
+
+def rnd(tid, shape, std=1.0, cid=CID):
+    return synth.rand_array(cid, tid, shape, std)
+
+
+# ------------------------------------------------------------------ LN + modulate
+@pytest.mark.parametrize("rows,hidden,split", [(320, 256, 64), (7, 64, 3), (1000, 3072, 512), (4608, 3072, 512),
+                                               (33, 4096, 40)])
+def test_ln_modulate(rows, hidden, split):
+    say(f"ln_modulate rows={rows} hidden={hidden} split={split}")
+    A = DeviceArena()
+    x = rnd(1, (rows, hidden)) * 3 + rnd(2, (rows, 1))
+    sh = rnd(3, (2, hidden), 0.7)
+    sc = rnd(4, (2, hidden), 0.7)
+    dx, dsh, dsc = A.f32(x), A.f32(sh), A.f32(sc)
+    out = A.empty_f16(rows, hidden)
+    B.check(B.mmdit_k_ln_modulate(dx, rows, hidden, split, dsh[0], dsc[0], dsh[1], dsc[1], 1e-6, out, stream()))
+    sync()
+    g = to_numpy_f32(out)
+    ref = np.empty((rows, hidden))
+    s = min(split, rows)
+    ref[:s] = O.ln_modulate(x[:s], sh[0], sc[0], 1e-6)
+    ref[s:] = O.ln_modulate(x[s:], sh[1], sc[1], 1e-6)
+    assert rel_err(g, ref) <= TOL
+    assert rel_err_rounded_out(g, ref, "f16") <= 1e-4
+    assert within_one_ulp(g, ref, "f16") <= 1.0  # one rounding of an fp32 result
+
+
+# ------------------------------------------------------------------ RoPE table
+@pytest.mark.parametrize("shape", [synth.TINY, synth.QWEN_DOUBLE])
+def test_rope_table(shape):
+    say(f"rope_table {shape.name}")
+    A = DeviceArena()
+    from diffusion_transformer_image_mm_amd.device import dims_for
+    d = dims_for(shape)
+    ids = synth.position_ids(shape)
+    dids = A.i32(ids)
+    rope = A.empty_f32(shape.seq_len, shape.head_dim // 2, 2)
+    B.check(B.mmdit_rope_table(d, dids, rope, stream()))
+    sync()
+    g = rope.cpu().numpy()
+    phi = O.rope_angles(ids, shape.axes, shape.theta)
+    np.testing.assert_allclose(g[..., 0], np.cos(phi), rtol=0, atol=2e-7)
+    np.testing.assert_allclose(g[..., 1], np.sin(phi), rtol=0, atol=2e-7)
+
+
+# ------------------------------------------------------------------ QK norm + RoPE
+def _rope_host(ids, axes, theta):
+    phi = O.rope_angles(ids, axes, theta)
+    return np.stack([np.cos(phi), np.sin(phi)], axis=-1).astype(np.float32)
+
+
+@pytest.mark.parametrize("D,heads,txt,grid", [(64, 4, 64, (16, 16)), (128, 3, 5, (7, 9)), (128, 24, 512, (64, 64)),
+                                              (64, 2, 1, (1, 1))])
+def test_qknorm_rope(D, heads, txt, grid):
+    say(f"qknorm_rope D={D} heads={heads} txt={txt} grid={grid}")
+    A = DeviceArena()
+    shp = synth.custom_shape("qk", CID, heads * D, heads, 64, txt, grid)
+    L, H = shp.seq_len, shp.hidden
+    l_pad = (L + 127) // 128 * 128
+    qkv = rnd(10, (L, 3 * H))
+    norms = [synth.uniform(CID, 11 + i, (D,), 0.5, 1.5) for i in range(4)]  # q0 k0 q1 k1
+    ids = synth.position_ids(shp)
+    rope = _rope_host(ids, shp.axes, shp.theta)
+    dq = A.bf16(qkv)
+    dn = [A.bf16(n) for n in norms]
+    qo, ko, vo = (A.empty_bf16(heads, l_pad, D), A.empty_bf16(heads, l_pad, D), A.empty_bf16(heads, D, l_pad))
+    for t in (qo, ko, vo):
+        t.fill_(float("nan"))  # padding must be overwritten with zeros
+    B.check(B.mmdit_k_qknorm_rope(dq, 3 * H, L, heads, D, txt, dn[0], dn[1], dn[2], dn[3], A.f32(rope), 1e-6,
+                                  l_pad, qo, ko, vo, stream()))
+    sync()
+    gq, gk, gv = to_numpy_f32(qo), to_numpy_f32(ko), to_numpy_f32(vo)
+    phi = O.rope_angles(ids, shp.axes, shp.theta)
+    for which, g, n_t, n_i in (("q", gq, norms[0], norms[2]), ("k", gk, norms[1], norms[3])):
+        off = 0 if which == "q" else H
+        for h in range(heads):
+            u = qkv[:, off + h * D: off + (h + 1) * D]
+            ref = np.empty((L, D))
+            ref[:txt] = O.qk_norm_rope(u[:txt], n_t, phi[:txt], 1e-6)
+            ref[txt:] = O.qk_norm_rope(u[txt:], n_i, phi[txt:], 1e-6)
+            assert rel_err_bf16_out(g[h, :L], ref) <= TOL
+            # the fp32 rotation of an fp32-normalised value, rounded once; the
+            # fp32 cos/sin table adds < 1e-7 relative
+            assert within_one_bf16_ulp(g[h, :L], ref, abs_floor=1e-5) <= 1.0, (which, h)
+        assert np.all(g[:, L:] == 0)
+    v = qkv[:, 2 * H:].reshape(L, heads, D).transpose(1, 2, 0)
+    np.testing.assert_array_equal(gv[:, :, :L], v)
+    assert np.all(gv[:, :, L:] == 0)
+
+
+# ------------------------------------------------------------------ attention
+def _attention_case(D, heads, L, q_scale=1.0, rows=None, tid=20):
+    A = DeviceArena()
+    l_pad = (L + 127) // 128 * 128
+    q = rnd(tid, (heads, L, D)) * q_scale
+    k = rnd(tid + 1, (heads, L, D))
+    v = rnd(tid + 2, (heads, L, D))
+    qp = np.zeros((heads, l_pad, D), np.float32); qp[:, :L] = synth.bf16_exact(q)
+    kp = np.zeros((heads, l_pad, D), np.float32); kp[:, :L] = k
+    vt = np.zeros((heads, D, l_pad), np.float32); vt[:, :, :L] = v.transpose(0, 2, 1)
+    H = heads * D
+    out = A.empty_f16(L, H)
+    B.check(B.mmdit_k_attention(A.bf16(qp), A.bf16(kp), A.bf16(vt), heads, L, D, l_pad, out, H, stream()))
+    sync()
+    g = to_numpy_f32(out)
+    qe = synth.bf16_exact(q)
+    sel = np.arange(L) if rows is None else rows
+    worst = 0.0
+    for h in range(heads):
+        ref = O.attention_head(qe[h], k[h], v[h], rows=None if rows is None else rows)
+        worst = max(worst, rel_err_rounded_out(g[sel, h * D:(h + 1) * D], ref, "f16"))
+    return worst
+
+
+@pytest.mark.parametrize("D,heads,L", [(64, 4, 320), (128, 2, 333), (128, 3, 64), (64, 2, 1), (128, 1, 129),
+                                       (64, 1, 700)])
+def test_attention_small(D, heads, L):
+    say(f"attention D={D} heads={heads} L={L}")
+    err = _attention_case(D, heads, L)
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("D,heads,L", [(128, 2, 333), (64, 4, 320)])
+def test_attention_sharp(D, heads, L):
+    """Queries scaled x6: scores with std ~6, so a few keys dominate each row
+    and a wrong key/value pairing would show."""
+    say(f"attention sharp D={D} heads={heads} L={L}")
+    err = _attention_case(D, heads, L, q_scale=6.0, tid=30)
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("L", [4608, 7145])
+def test_attention_full_size_sampled_rows(L):
+    say(f"attention full heads=24 D=128 L={L}")
+    rng = np.random.default_rng(L)
+    rows = np.unique(np.r_[0, 1, 127, 128, L - 129, L - 1, rng.integers(0, L, 90)])
+    err = _attention_case(128, 24, L, rows=rows, tid=40)
+    assert err <= TOL, err
+
+
+# ------------------------------------------------------------------ GEMM
+def _lin(tid, n, k, int8):
+    w = rnd(tid, (n, k), 0.02)
+    b = rnd(tid + 1, (n,), 0.02)
+    if int8:
+        q, s = synth.quantize_int8(w)
+        return synth.Linear(None, b, q, s)
+    return synth.Linear(w, b)
+
+
+GEMM_CASES = [
+    # m, n, k, epilogue, int8
+    (320, 768, 256, B.MMDIT_EPI_BIAS, False),
+    (1000, 320, 1280, B.MMDIT_EPI_BIAS, False),
+    (513, 1024, 256, B.MMDIT_EPI_BIAS_GELU, False),
+    (700, 256, 1024, B.MMDIT_EPI_GATE_RESID, False),
+    (320, 1792, 256, B.MMDIT_EPI_SPLIT_GELU, False),
+    (4096, 3072, 64, B.MMDIT_EPI_BIAS_F32, False),
+    (4096, 64, 3072, B.MMDIT_EPI_EULER, False),
+    (1, 128, 64, B.MMDIT_EPI_BIAS, False),
+    (320, 768, 256, B.MMDIT_EPI_BIAS, True),
+    (700, 256, 1024, B.MMDIT_EPI_GATE_RESID, True),
+    (513, 1024, 256, B.MMDIT_EPI_BIAS_GELU, True),
+    (4096, 64, 3072, B.MMDIT_EPI_EULER, True),
+    (320, 1792, 256, B.MMDIT_EPI_SPLIT_GELU, True),
+]
+
+
+_RESID = [None]
+
+
+def _run_gemm(m, n, k, epi, int8, rows=None, tid=50):
+    A = DeviceArena()
+    a = synth.f16_exact(rnd(tid, (m, k)))  # the fp16 activation operand both sides read
+    lin = _lin(tid + 2, n, k, int8)
+    da = A.f16(a)
+    g = B.mmdit_gemm(m=m, n=n, k=k, weight_dtype=B.MMDIT_INT8 if int8 else B.MMDIT_BF16, a=da.data_ptr(),
+                     lda=k, w=A.linear(lin), epilogue=epi)
+    split = 3 * n // 7 // 64 * 64 if epi == B.MMDIT_EPI_SPLIT_GELU else n
+    _SPLIT[0] = split
+    gate = rnd(tid + 5, (n,), 0.7)
+    resid = rnd(tid + 6, (m, n))
+    f32out = epi in (B.MMDIT_EPI_GATE_RESID, B.MMDIT_EPI_BIAS_F32, B.MMDIT_EPI_EULER)
+    if f32out:
+        out = A.f32(resid) if epi == B.MMDIT_EPI_EULER else A.empty_f32(m, n)
+    else:
+        out = A.empty_bf16(m, split) if epi != B.MMDIT_EPI_BIAS_GELU else A.empty_f16(m, split)
+    g.out, g.ldo = out.data_ptr(), (n if f32out else split)
+    out2 = None
+    if epi == B.MMDIT_EPI_GATE_RESID:
+        g.gate, g.resid, g.ldr = A.f32(gate).data_ptr(), A.f32(resid).data_ptr(), n
+    if epi == B.MMDIT_EPI_SPLIT_GELU:
+        out2 = A.empty_f16(m, 64 + n - split)
+        g.split_n, g.out2, g.ldo2, g.out2_col = split, out2.data_ptr(), 64 + n - split, 64
+    if epi == B.MMDIT_EPI_EULER:
+        g.alpha = -1.0 / 28
+    B.check(B.mmdit_k_gemm(g, stream()))
+    sync()
+    sel = np.arange(m) if rows is None else rows
+    _RESID[0] = resid[sel]
+    y = O.linear(a[sel], lin)
+    if epi == B.MMDIT_EPI_BIAS:
+        return to_numpy_f32(out)[sel], y
+    if epi == B.MMDIT_EPI_BIAS_GELU:
+        return to_numpy_f32(out)[sel], O.gelu_tanh(y)
+    if epi == B.MMDIT_EPI_GATE_RESID:
+        return to_numpy_f32(out)[sel], resid[sel] + gate * y
+    if epi == B.MMDIT_EPI_BIAS_F32:
+        return to_numpy_f32(out)[sel], y
+    if epi == B.MMDIT_EPI_EULER:
+        return to_numpy_f32(out)[sel], O.euler(resid[sel], y, 1.0, 1.0 - 1.0 / 28)
+    # split: first columns plain, the rest GELU at column offset 64 of out2
+    g1 = to_numpy_f32(out)[sel]
+    g2 = to_numpy_f32(out2)[sel][:, 64:]
+    return np.concatenate([g1, g2], axis=1), np.concatenate([y[:, :split], O.gelu_tanh(y[:, split:])], axis=1)
+
+
+def _gemm_err(g, ref, epi, k):
+    """Output error over the output's own storage format: fp32 outputs are
+    compared as they are; bf16 (q, k, v) and fp16 (GELU hidden) outputs beyond
+    half a step of their format; a split output in two column blocks."""
+    if epi in (B.MMDIT_EPI_GATE_RESID, B.MMDIT_EPI_EULER, B.MMDIT_EPI_BIAS_F32):
+        return rel_err(g, ref)
+    if epi == B.MMDIT_EPI_BIAS:
+        return rel_err_rounded_out(g, ref, "bf16")
+    if epi == B.MMDIT_EPI_BIAS_GELU:
+        return rel_err_rounded_out(g, ref, "f16")
+    s = _SPLIT[0]
+    return max(rel_err_rounded_out(g[:, :s], ref[:, :s], "bf16"), rel_err_rounded_out(g[:, s:], ref[:, s:], "f16"))
+
+
+_SPLIT = [0]
+
+
+@pytest.mark.parametrize("m,n,k,epi,int8", GEMM_CASES)
+def test_gemm(m, n, k, epi, int8):
+    say(f"gemm m={m} n={n} k={k} epi={epi} int8={int8}")
+    g, ref = _run_gemm(m, n, k, epi, int8)
+    assert _gemm_err(g, ref, epi, k) <= TOL
+    if epi in (B.MMDIT_EPI_GATE_RESID, B.MMDIT_EPI_EULER, B.MMDIT_EPI_BIAS_F32):
+        # fp32 outputs: bf16 x bf16 products are exact in fp32 and the sums
+        # round in fp32, so the branch itself (output minus the residual the
+        # epilogue adds) matches far inside the bar
+        base = _RESID[0] if epi != B.MMDIT_EPI_BIAS_F32 else 0.0
+        assert rel_err(g - base, ref - base) <= 1e-3
+
+
+@pytest.mark.parametrize("m,n,k,epi", [(4608, 9216, 3072, B.MMDIT_EPI_BIAS), (4096, 3072, 12288, B.MMDIT_EPI_GATE_RESID),
+                                       (4608, 21504, 3072, B.MMDIT_EPI_SPLIT_GELU), (6889, 12288, 3072,
+                                                                                   B.MMDIT_EPI_BIAS_GELU)])
+def test_gemm_full_size_sampled_rows(m, n, k, epi):
+    say(f"gemm full m={m} n={n} k={k} epi={epi}")
+    rows = np.unique(np.r_[0, 255, 256, m - 1, np.random.default_rng(m).integers(0, m, 40)])
+    g, ref = _run_gemm(m, n, k, epi, False, rows=rows, tid=60)
+    assert _gemm_err(g, ref, epi, k) <= TOL
+
+
+def test_gemm_int8_rerun_bit_exact():
+    say("gemm int8 rerun")
+    a1, _ = _run_gemm(700, 256, 1024, B.MMDIT_EPI_GATE_RESID, True, tid=70)
+    a2, _ = _run_gemm(700, 256, 1024, B.MMDIT_EPI_GATE_RESID, True, tid=70)
+    np.testing.assert_array_equal(a1, a2)
+
+
+# ------------------------------------------------------------------ GEMV
+@pytest.mark.parametrize("n,k,int8,silu_in,acc", [(1536, 256, False, 1, 0), (18432, 3072, False, 1, 0),
+                                                   (18432, 3072, True, 1, 0), (3072, 256, True, 0, 1),
+                                                   (100, 64, False, 0, 1)])
+def test_gemv(n, k, int8, silu_in, acc):
+    say(f"gemv n={n} k={k} int8={int8}")
+    A = DeviceArena()
+    x = rnd(80, (k,))
+    lin = _lin(81, n, k, int8)
+    base = rnd(83, (n,))
+    out = A.f32(base)
+    B.check(B.mmdit_k_gemv(A.f32(x), k, A.linear(lin), n, B.MMDIT_INT8 if int8 else B.MMDIT_BF16, silu_in, acc,
+                           out, stream()))
+    sync()
+    xin = O.silu(x) if silu_in else x
+    ref = O.linear(xin[None, :], lin)[0] + (base if acc else 0)
+    assert rel_err(out.cpu().numpy(), ref) <= 1e-4
+
+
+# ------------------------------------------------------------------ time embedding / Euler
+@pytest.mark.parametrize("t,gd,int8", [(1.0, 3.5, False), (0.37, 3.5, True), (0.0, 1.0, False)])
+def test_time_embed(t, gd, int8):
+    say(f"time_embed t={t} g={gd} int8={int8}")
+    A = DeviceArena()
+    shp = synth.custom_shape("te", CID + 1, 256, 4, 1024, 8, (2, 2), n_double=0, n_single=0)
+    m = synth.model_weights(shp, int8=int8)
+    from diffusion_transformer_image_mm_amd.device import dims_for
+    d = dims_for(shp, int8)
+    mm = A.model(m)
+    vec = A.empty_f32(shp.hidden)
+    ws = A.workspace(4 * (512 + 2 * shp.hidden))
+    B.check(B.mmdit_k_time_embed(d, mm, t, gd, vec, ws, ws.numel(), stream()))
+    sync()
+    assert rel_err(vec.cpu().numpy(), O.conditioning(t, gd, m)) <= 1e-4
+
+
+def test_euler():
+    say("euler")
+    A = DeviceArena()
+    z = rnd(90, (4096, 64))
+    v = rnd(91, (4096, 64))
+    dz = A.f32(z)
+    B.check(B.mmdit_k_euler(dz, A.f32(v), z.size, -1.0 / 28, stream()))
+    sync()
+    np.testing.assert_allclose(dz.cpu().numpy(), O.euler(z, v, 1.0, 1.0 - 1.0 / 28), rtol=0, atol=1e-6)
