@@ -19,9 +19,13 @@
 // rates are equal on gfx950.
 //
 // Shape of the kernel (gfx950, 64-wide wavefronts):
-// * workgroup tile 256 (rows of A) x 256 (rows of W) x 64 (k), 4 wavefronts in
-//   a 2 x 2 arrangement, each owning a 128 x 128 sub-tile = 8 x 8 MFMA tiles
-//   of v_mfma_f32_16x16x32_f16 (256 fp32 accumulators per lane);
+// * workgroup tile 256 (rows of A) x 256 (rows of W) x 64 (k), 8 wavefronts
+//   (two per SIMD) in a 2 (m) x 4 (n) arrangement, each owning a 128 x 64
+//   sub-tile = 8 x 4 MFMA tiles of v_mfma_f32_16x16x32_f16 (128 fp32
+//   accumulators per lane). Two wavefronts per SIMD matter on gfx950: one
+//   wavefront per SIMD sustains only ~63 B/clk/CU of 16-byte LDS reads, two
+//   reach ~155 B/clk/CU (measured), and the MFMA pipe reaches 2.2 PFLOP/s
+//   only with at least two wavefronts per SIMD;
 // * W is the MFMA's first operand and A the second, so the hardware result
 //   is the transposed tile and each lane ends up with 4 consecutive output
 //   columns of one row: 8-byte 16-bit / 16-byte fp32 epilogue stores;
@@ -43,7 +47,7 @@ namespace mmdit {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int NTHREADS = 256;
+constexpr int NTHREADS = 512;
 constexpr int A_TILE_BYTES = BM * BK * 2;   // 32 KB
 constexpr int W_TILE_BYTES_BF16 = BN * BK * 2;  // 32 KB
 constexpr int W_TILE_BYTES_I8 = BN * BK;        // 16 KB
@@ -117,6 +121,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) 
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     constexpr int WT = INT8 ? W_TILE_BYTES_I8 : W_TILE_BYTES_BF16;
     constexpr int STAGE = A_TILE_BYTES + WT;
+    constexpr int TM = 8, TN = 4;   // MFMA sub-tiles per wavefront (m, n)
     // stage s: A tile at smem + s*STAGE, W tile right after it
 
     const TileCoord tc = tile_of(args, blockIdx.x);
@@ -124,66 +129,65 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) 
     const int M = G.m, N = args.n, K = args.k;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
 
-    const uint16_t* __restrict__ A = args.a + (size_t)G.row0 * args.lda;
-    const int lda = args.lda;
-
-    // ---- per-lane load descriptors. A tile: 256 rows x 8 chunks; each
-    // wavefront issues 8 loads of 8 rows. Lane i of load j covers row
-    // r = (wave*8 + j)*8 + i/8 at LDS position p = i%8, fetching chunk
-    // c = p ^ ((r >> 1) & 7).
+    // ---- load descriptors: a uniform base plus a 32-bit per-lane byte
+    // offset (so the loads use the scalar-base addressing form). A tile:
+    // 256 rows x 8 chunks; wavefront w issues loads j = 0..3 of 8 rows each:
+    // lane i covers row r = (4w + j)*8 + i/8 at LDS position p = i%8,
+    // fetching chunk c = p ^ ((r >> 1) & 7).
     const int lrow = lane >> 3, lpos = lane & 7;
-    const uint16_t* a_src[8];
+    const char* a_g = reinterpret_cast<const char*>(args.a + (size_t)G.row0 * args.lda);
+    uint32_t a_off_g[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int r = (wave * 8 + j) * 8 + lrow;
+    for (int j = 0; j < 4; ++j) {
+        const int r = (wave * 4 + j) * 8 + lrow;
         const int c = lpos ^ ((r >> 1) & 7);
         int gr = tc.m0 + r;
         gr = gr < M ? gr : M - 1;
-        a_src[j] = A + (size_t)gr * lda + c * 8;
+        a_off_g[j] = (uint32_t)gr * (uint32_t)args.lda * 2u + (uint32_t)c * 16u;
     }
     // W tile. bf16: same pattern as A over N rows. int8: 64 B per row = 4
-    // chunks of 16 codes; a load covers 16 rows; unit u of row r stored at
-    // position u ^ ((r >> 2) & 3).
-    const char* w_src[8];
+    // units of 16 codes; a load covers 16 rows (lane i: row (2w + j)*16 +
+    // i/4, position i%4); unit u of row r is stored at position u ^ ((r >> 2) & 3).
+    const char* w_g = static_cast<const char*>(G.w);
+    uint32_t w_off_g[4];
     if (!INT8) {
-        const uint16_t* W = static_cast<const uint16_t*>(G.w);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int r = (wave * 8 + j) * 8 + lrow;
+        for (int j = 0; j < 4; ++j) {
+            const int r = (wave * 4 + j) * 8 + lrow;
             const int c = lpos ^ ((r >> 1) & 7);
             int gn = tc.n0 + r;
             gn = gn < N ? gn : N - 1;
-            w_src[j] = reinterpret_cast<const char*>(W + (size_t)gn * K + c * 8);
+            w_off_g[j] = (uint32_t)gn * (uint32_t)K * 2u + (uint32_t)c * 16u;
         }
     } else {
-        const int8_t* W = static_cast<const int8_t*>(G.w);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = (wave * 4 + j) * 16 + (lane >> 2);
+        for (int j = 0; j < 2; ++j) {
+            const int r = (wave * 2 + j) * 16 + (lane >> 2);
             const int u = (lane & 3) ^ ((r >> 2) & 3);
             int gn = tc.n0 + r;
             gn = gn < N ? gn : N - 1;
-            w_src[j] = reinterpret_cast<const char*>(W + (size_t)gn * K + u * 16);
+            w_off_g[j] = (uint32_t)gn * (uint32_t)K + (uint32_t)u * 16u;
         }
     }
 
     auto issue_stage = [&](int kt, int s) {
         char* base = smem + s * STAGE;
-        const int k0 = kt * BK;
+        const uint32_t ka = (uint32_t)kt * (BK * 2);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            g2l_16(a_src[j] + k0, (lds_void*)(base + ((wave * 8 + j) * 8) * 128));
+        for (int j = 0; j < 4; ++j)
+            g2l_16(a_g + (a_off_g[j] + ka), (lds_void*)(base + ((wave * 4 + j) * 8) * 128));
         char* wb = base + A_TILE_BYTES;
         if (!INT8) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                g2l_16(w_src[j] + k0 * 2, (lds_void*)(wb + ((wave * 8 + j) * 8) * 128));
-        } else {
-#pragma unroll
             for (int j = 0; j < 4; ++j)
-                g2l_16(w_src[j] + k0, (lds_void*)(wb + ((wave * 4 + j) * 16) * 64));
+                g2l_16(w_g + (w_off_g[j] + ka), (lds_void*)(wb + ((wave * 4 + j) * 8) * 128));
+        } else {
+            const uint32_t kw = (uint32_t)kt * BK;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                g2l_16(w_g + (w_off_g[j] + kw), (lds_void*)(wb + ((wave * 2 + j) * 16) * 64));
         }
     };
 
@@ -196,16 +200,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) 
         const int c = ks * 4 + lg;
         a_off[ks] = (wm * 128 + lr) * 128 + ((c ^ ((lr >> 1) & 7)) * 16);
         if (!INT8)
-            w_off[ks] = (wn * 128 + lr) * 128 + ((c ^ ((lr >> 1) & 7)) * 16);
+            w_off[ks] = (wn * 64 + lr) * 128 + ((c ^ ((lr >> 1) & 7)) * 16);
         else
-            w_off[ks] = (wn * 128 + lr) * 64 + (((c >> 1) ^ ((lr >> 2) & 3)) * 16) + (c & 1) * 8;
+            w_off[ks] = (wn * 64 + lr) * 64 + (((c >> 1) ^ ((lr >> 2) & 3)) * 16) + (c & 1) * 8;
     }
 
-    f32x4_t acc[8][8];
+    f32x4_t acc[TN][TM];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < TN; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < TM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     const int nk = K / BK;
     issue_stage(0, 0);
@@ -216,13 +220,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) 
         const int s = kt & 1;
         const char* sa = smem + s * STAGE;
         const char* sw = sa + A_TILE_BYTES;
-        f16x8_t fa[2][8], fw[2][8];
+        f16x8_t fa[2][TM], fw[2][TN];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) fa[ks][i] = lds_frag_h(sa + a_off[ks] + i * 16 * 128);
+            for (int i = 0; i < TM; ++i) fa[ks][i] = lds_frag_h(sa + a_off[ks] + i * 16 * 128);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < TN; ++i) {
                 if (!INT8)
                     fw[ks][i] = bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(sw + w_off[ks] + i * 16 * 128));
                 else
@@ -233,9 +237,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) 
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int in = 0; in < 8; ++in)
+            for (int in = 0; in < TN; ++in)
 #pragma unroll
-                for (int im = 0; im < 8; ++im)
+                for (int im = 0; im < TM; ++im)
                     acc[in][im] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fw[ks][in], fa[ks][im],
                                                                          acc[in][im], 0, 0, 0);
         // keep the stage wait and the barrier behind the MFMAs (the compiler
@@ -246,11 +250,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) 
     }
 
     // ---- epilogue. acc[in][im] element j: output column
-    // n = n0 + wn*128 + in*16 + lg*4 + j, row m = m0 + wm*128 + im*16 + lr.
-    const int nb = tc.n0 + wn * 128 + lg * 4;
+    // n = n0 + wn*64 + in*16 + lg*4 + j, row m = m0 + wm*128 + im*16 + lr.
+    const int nb = tc.n0 + wn * 64 + lg * 4;
     const int mb = tc.m0 + wm * 128 + lr;
 #pragma unroll
-    for (int in = 0; in < 8; ++in) {
+    for (int in = 0; in < TN; ++in) {
         const int n = nb + in * 16;
         if (n >= N) continue;
         const uint2 braw = *reinterpret_cast<const uint2*>(G.bias + n);
@@ -267,7 +271,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) 
             gt[0] = g4.x; gt[1] = g4.y; gt[2] = g4.z; gt[3] = g4.w;
         }
 #pragma unroll
-        for (int im = 0; im < 8; ++im) {
+        for (int im = 0; im < TM; ++im) {
             const int m = mb + im * 16;
             if (m >= M) continue;
             const size_t grow = (size_t)(G.row0 + m);
