@@ -8,13 +8,16 @@
 //
 // gfx950 design:
 // * workgroup = 4 wavefronts x 32 query rows (128 rows of one head);
-//   key/value tiles of 64 keys;
+//   key/value tiles of 64 keys; at most 256 registers per lane so that two
+//   workgroups share a CU (two wavefronts per SIMD: one wavefront per SIMD
+//   sustains only about half the LDS read rate these tiles need);
 // * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K from LDS as the first
 //   operand, Q^T from registers as the second), so each lane holds 32 scores
 //   of ONE query row: the row max needs one cross-lane exchange (lane ^ 32)
 //   and the row sum none until the end;
 // * online softmax in fp32 with exp2: scores are scaled by log2(e)/sqrt(D)
-//   in one multiply-subtract; O is rescaled only by the lane's own factor;
+//   in one multiply-subtract; O is rescaled only by the lane's own factor,
+//   and only on tiles where some row's maximum grew by more than 2^8;
 // * O^T += V^T P^T: the probabilities are already in the second operand's
 //   register layout (the key order inside one MFMA is free as long as both
 //   operands agree), V^T comes from LDS as two 8-byte reads per fragment;
@@ -51,10 +54,10 @@ struct AttnTile {
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void attention_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ k,
                                                            const uint16_t* __restrict__ vt,
-                                                           int seq_len, int l_pad,
+                                                           int seq_len, int l_pad, int heads,
                                                            uint16_t* __restrict__ out, int ldo,
                                                            float c_log2) {
     using T = AttnTile<D>;
@@ -63,11 +66,18 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(const uint16_t* __res
     __shared__ __attribute__((aligned(1024))) char sK1[T::K_BYTES];
     __shared__ __attribute__((aligned(1024))) char sV1[T::V_BYTES];
 
-    const int h = blockIdx.y;
+    // Workgroups are dispatched round-robin over the 8 XCDs. Give each XCD a
+    // contiguous range of (head, query-tile) pairs, so that the keys and
+    // values of a head are read through one XCD's L2 (2.4 MB per head at
+    // 4608 tokens) instead of all eight.
+    const int nq = (seq_len + 127) / 128;
+    const int total = nq * heads;
+    int bid = blockIdx.x;
+    if (total % 8 == 0) bid = (bid % 8) * (total / 8) + bid / 8;
+    const int h = bid / nq, qt = bid % nq;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 5, r32 = lane & 31;
-    const int qrow = blockIdx.x * 128 + wave * 32 + r32;
-    const int H = gridDim.y * D;
+    const int qrow = qt * 128 + wave * 32 + r32;
 
     // ---- Q^T fragments (second MFMA operand): lane holds Q[qrow][ds*16 + 8g .. +7]
     const int qld = qrow < l_pad ? qrow : l_pad - 1;
@@ -169,8 +179,15 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(const uint16_t* __res
 #pragma unroll
             for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[st][i]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float m_new = fmaxf(m_run, tmax * c_log2);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        // Lazy rescaling: the running max only moves when a row's new max
+        // exceeds it by more than 8 (log2 units). O / l does not depend on
+        // which reference max is used; a stale one bounds P by 2^8.
+        const float cand = tmax * c_log2;
+        const bool move = cand > m_run + 8.0f;
+        const float m_new = move ? cand : m_run;
+        const bool any_move = __ballot(move) != 0ull;   // wave-uniform
+        float alpha = 1.0f;
+        if (any_move) alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
         float psum = 0.f;
         bf16x8_t pf[4];
@@ -183,10 +200,12 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(const uint16_t* __res
                 pf[st * 2 + (i >> 3)][i & 7] = static_cast<__bf16>(p);
             }
         l_run = l_run * alpha + psum;
+        if (any_move) {
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
+            for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+                for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+        }
         // O^T += V^T P^T
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
@@ -230,20 +249,19 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(const uint16_t* __res
                 *reinterpret_cast<uint2*>(op + dt * 32 + 8 * i4) = w;
             }
     }
-    (void)H;
 }
 
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int heads,
                             int seq_len, int head_dim, int l_pad, uint16_t* out, int ldo,
                             hipStream_t s) {
     if (seq_len <= 0) return hipSuccess;
-    dim3 grid((seq_len + 127) / 128, heads), block(256);
+    dim3 grid(((seq_len + 127) / 128) * heads), block(256);
     const float c_log2 = 1.4426950408889634f / sqrtf((float)head_dim);
     if (head_dim == 128)
-        hipLaunchKernelGGL(attention_kernel<128>, grid, block, 0, s, q, k, vt, seq_len, l_pad, out, ldo,
+        hipLaunchKernelGGL(attention_kernel<128>, grid, block, 0, s, q, k, vt, seq_len, l_pad, heads, out, ldo,
                            c_log2);
     else if (head_dim == 64)
-        hipLaunchKernelGGL(attention_kernel<64>, grid, block, 0, s, q, k, vt, seq_len, l_pad, out, ldo,
+        hipLaunchKernelGGL(attention_kernel<64>, grid, block, 0, s, q, k, vt, seq_len, l_pad, heads, out, ldo,
                            c_log2);
     else
         return hipErrorInvalidValue;

@@ -149,6 +149,32 @@ def test_attention_sharp(D, heads, L):
     assert err <= TOL, err
 
 
+@pytest.mark.parametrize("D,L,slope", [(64, 700, 0.5), (128, 333, 0.25), (128, 300, 0.01)])
+def test_attention_growing_scores(D, L, slope):
+    """Scores that grow along the key axis: with a large slope every key tile
+    raises the row maximum by far more than 2^8 (the rescaling path runs on
+    every tile); with a small one the running maximum stays stale for many
+    tiles. Both must give the exact softmax."""
+    say(f"attention growing scores D={D} L={L} slope={slope}")
+    A = DeviceArena()
+    heads, l_pad = 2, (L + 127) // 128 * 128
+    base = rnd(50, (heads, L, D), 0.3)
+    u = np.zeros(D, np.float32); u[0] = 1.0
+    q = synth.bf16_exact(base + 4.0 * u)
+    k = synth.bf16_exact(base[::-1] * 0.5 + (slope * np.arange(L, dtype=np.float32))[None, :, None] * u)
+    v = rnd(52, (heads, L, D))
+    qp = np.zeros((heads, l_pad, D), np.float32); qp[:, :L] = q
+    kp = np.zeros((heads, l_pad, D), np.float32); kp[:, :L] = k
+    vt = np.zeros((heads, D, l_pad), np.float32); vt[:, :, :L] = v.transpose(0, 2, 1)
+    out = A.empty_f16(L, heads * D)
+    B.check(B.mmdit_k_attention(A.bf16(qp), A.bf16(kp), A.bf16(vt), heads, L, D, l_pad, out, heads * D, stream()))
+    sync()
+    g = to_numpy_f32(out)
+    for h in range(heads):
+        ref = O.attention_head(q[h], k[h], v[h])
+        assert rel_err_rounded_out(g[:, h * D:(h + 1) * D], ref, "f16") <= TOL
+
+
 @pytest.mark.parametrize("L", [4608, 7145])
 def test_attention_full_size_sampled_rows(L):
     say(f"attention full heads=24 D=128 L={L}")
