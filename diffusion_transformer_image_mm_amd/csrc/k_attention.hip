@@ -20,7 +20,9 @@
 //   and only on tiles where some row's maximum grew by more than 2^8;
 // * O^T += V^T P^T: the probabilities are already in the second operand's
 //   register layout (the key order inside one MFMA is free as long as both
-//   operands agree), V^T comes from LDS as two 8-byte reads per fragment;
+//   operands agree); V^T is stored with the middle quads of every 16 keys
+//   swapped, so a lane's 8 keys are one 16-byte LDS read (the 16 lanes served
+//   together hit 16 distinct bank groups);
 // * K and V^T tiles go global -> LDS with 16-byte direct-to-LDS loads into
 //   two distinct LDS buffers (double buffering; distinct variables let the
 //   compiler see that the next tile's loads do not alias this tile's reads);
@@ -128,17 +130,17 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
             const int c = ds * 2 + g;
             k_off[st][ds] = row * T::RB + ((c ^ (row & (T::CPR - 1))) * 16);
         }
-    int v_off[D / 32][4][2];
+    // V^T fragment u of lane (r32, g): keys 16u + 4g + {0..3, 8..11}, which the
+    // quad-swapped layout stores as chunk 2u + g of row d
+    int v_off[D / 32][4];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int d = dt * 32 + r32;
-                const int c = 2 * u + half;
-                v_off[dt][u][half] = d * 128 + ((c ^ ((d >> 1) & 7)) * 16) + g * 8;
-            }
+        for (int u = 0; u < 4; ++u) {
+            const int d = dt * 32 + r32;
+            const int c = 2 * u + g;
+            v_off[dt][u] = d * 128 + ((c ^ ((d >> 1) & 7)) * 16);
+        }
 
     f32x16_t o[D / 32];
 #pragma unroll
@@ -211,9 +213,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const bf16x4_t lo = *reinterpret_cast<const bf16x4_t*>(sV + v_off[dt][u][0]);
-                const bf16x4_t hi = *reinterpret_cast<const bf16x4_t*>(sV + v_off[dt][u][1]);
-                const bf16x8_t vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(sV + v_off[dt][u]);
                 o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[u], o[dt], 0, 0, 0);
             }
     };

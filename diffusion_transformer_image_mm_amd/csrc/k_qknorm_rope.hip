@@ -7,7 +7,10 @@
 // to save memory round trips; here the fused kernel also writes the layout
 // the attention kernel reads, so no separate transpose pass exists:
 //   Q, K: [heads, l_pad, D]  (one contiguous D-row per token and head)
-//   V^T : [heads, D, l_pad]  (keys contiguous, the PV product's operand order)
+//   V^T : [heads, D, l_pad]  (keys along the row; inside each aligned group of
+//         16 keys the quads are stored 0, 2, 1, 3, so the 16-byte chunk 2i+j of
+//         a group holds keys 4j..4j+3 and 8+4j..8+4j+3 of it: the 8 keys that
+//         one lane of the 32x32x16 matrix-core product P V takes, in order)
 // Rows in [seq_len, l_pad) are written as zeros so the attention kernel never
 // reads past a buffer and padded keys stay finite.
 //
@@ -95,11 +98,14 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
         const int d = idx / (TILE / 8), tc = idx % (TILE / 8);
         const int tb = t0 + tc * 8;
         if (tb >= l_pad) continue;
+        // stored element e of chunk tc is key 16*(tc/2) + 4*(tc%2) + 8*(e/4) + e%4
+        const int kb = 16 * (tc >> 1) + 4 * (tc & 1);
         uint32_t w[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint16_t lo = vs[(tc * 8 + 2 * j) * LDV + d];
-            const uint16_t hi = vs[(tc * 8 + 2 * j + 1) * LDV + d];
+            const int key = kb + 8 * (j >> 1) + 2 * (j & 1);
+            const uint16_t lo = vs[key * LDV + d];
+            const uint16_t hi = vs[(key + 1) * LDV + d];
             w[j] = uint32_t(lo) | (uint32_t(hi) << 16);
         }
         *reinterpret_cast<uint4*>(vt_out + ((size_t)h * D + d) * l_pad + tb) =

@@ -254,7 +254,10 @@ int mmdit_k_ln_modulate(const float* x, int rows, int hidden, int split,
  *   qkv: bf16 [seq_len, ld]; q at columns [0, H), k at [H, 2H), v at [2H, 3H)
  *   rows < split use (q_norm0, k_norm0), the others (q_norm1, k_norm1): bf16 [D]
  *   rope: fp32 [seq_len, D/2, 2]
- *   q_out, k_out: bf16 [heads, l_pad, D]; vt_out: bf16 [heads, D, l_pad]
+ *   q_out, k_out: bf16 [heads, l_pad, D]; vt_out: bf16 [heads, D, l_pad], V
+ *   transposed (keys along the row) with the keys of every aligned group of 16
+ *   stored in the order 0-3, 8-11, 4-7, 12-15 (the two middle quads swapped),
+ *   so that each 16-byte chunk holds the 8 keys one matrix-core lane needs.
  *   l_pad: a multiple of 64, >= seq_len; rows [seq_len, l_pad) are written as 0.
  */
 int mmdit_k_qknorm_rope(const mmdit_bf16* qkv, int ld, int seq_len, int heads, int head_dim,
@@ -267,8 +270,9 @@ int mmdit_k_qknorm_rope(const mmdit_bf16* qkv, int ld, int seq_len, int heads, i
 /*
  * Softmax attention without a mask (Luminal blog, "What the compiler found on
  * its own" and "The AMD MI300X pipeline": fused, tiled softmax(QK^T)V).
- *   q, k: bf16 [heads, l_pad, D]; vt: bf16 [heads, D, l_pad], as written by
- *   mmdit_k_qknorm_rope (zero beyond seq_len); scale 1/sqrt(D).
+ *   q, k: bf16 [heads, l_pad, D]; vt: bf16 [heads, D, l_pad] in the
+ *   quad-swapped key order written by mmdit_k_qknorm_rope (zero beyond
+ *   seq_len); l_pad a multiple of 64; scale 1/sqrt(D).
  *   out: fp16 [seq_len, ldo], head h at columns [h*D, (h+1)*D).
  */
 int mmdit_k_attention(const mmdit_bf16* q, const mmdit_bf16* k, const mmdit_bf16* vt,

@@ -62,6 +62,19 @@ def within_one_bf16_ulp(gpu, ref, abs_floor=1e-6) -> float:
     return float(np.max(d / (bf16_ulp(ref) + abs_floor)))
 
 
+def vt_layout(vt):
+    """V^T [..., l_pad] rearranged into the attention kernel's key order: in
+    each aligned group of 16 keys the quads are stored 0, 2, 1, 3 (stored
+    position p holds key 16*(p//16) + 4*swap(p//4 % 4) + p%4, swap exchanging
+    quads 1 and 2)."""
+    n = vt.shape[-1]
+    assert n % 16 == 0
+    p = np.arange(n)
+    quad = (p >> 2) & 3
+    key = (p & ~15) | ((((quad & 1) << 1) | (quad >> 1)) << 2) | (p & 3)
+    return vt[..., key]
+
+
 def say(*a):
     """Print a progress line that names the case (flushed before GPU work)."""
     print(*a, file=sys.stderr, flush=True)

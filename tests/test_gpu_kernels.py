@@ -12,7 +12,7 @@ import oracle as O
 from diffusion_transformer_image_mm_amd import binding as B
 from diffusion_transformer_image_mm_amd import synth
 from gpu_helpers import (TOL, DeviceArena, rel_err, rel_err_bf16_out, rel_err_rounded_out, say, stream, sync,
-                         to_numpy_f32, within_one_bf16_ulp, within_one_ulp)
+                         to_numpy_f32, vt_layout, within_one_bf16_ulp, within_one_ulp)
 
 pytestmark = pytest.mark.gpu
 CID = 700
@@ -103,9 +103,9 @@ def test_qknorm_rope(D, heads, txt, grid):
             # fp32 cos/sin table adds < 1e-7 relative
             assert within_one_bf16_ulp(g[h, :L], ref, abs_floor=1e-5) <= 1.0, (which, h)
         assert np.all(g[:, L:] == 0)
-    v = qkv[:, 2 * H:].reshape(L, heads, D).transpose(1, 2, 0)
-    np.testing.assert_array_equal(gv[:, :, :L], v)
-    assert np.all(gv[:, :, L:] == 0)
+    v = np.zeros((heads, D, l_pad), np.float32)
+    v[:, :, :L] = qkv[:, 2 * H:].reshape(L, heads, D).transpose(1, 2, 0)
+    np.testing.assert_array_equal(gv, vt_layout(v))
 
 
 # ------------------------------------------------------------------ attention
@@ -118,6 +118,7 @@ def _attention_case(D, heads, L, q_scale=1.0, rows=None, tid=20):
     qp = np.zeros((heads, l_pad, D), np.float32); qp[:, :L] = synth.bf16_exact(q)
     kp = np.zeros((heads, l_pad, D), np.float32); kp[:, :L] = k
     vt = np.zeros((heads, D, l_pad), np.float32); vt[:, :, :L] = v.transpose(0, 2, 1)
+    vt = vt_layout(vt)
     H = heads * D
     out = A.empty_f16(L, H)
     B.check(B.mmdit_k_attention(A.bf16(qp), A.bf16(kp), A.bf16(vt), heads, L, D, l_pad, out, H, stream()))
@@ -166,6 +167,7 @@ def test_attention_growing_scores(D, L, slope):
     qp = np.zeros((heads, l_pad, D), np.float32); qp[:, :L] = q
     kp = np.zeros((heads, l_pad, D), np.float32); kp[:, :L] = k
     vt = np.zeros((heads, D, l_pad), np.float32); vt[:, :, :L] = v.transpose(0, 2, 1)
+    vt = vt_layout(vt)
     out = A.empty_f16(L, heads * D)
     B.check(B.mmdit_k_attention(A.bf16(qp), A.bf16(kp), A.bf16(vt), heads, L, D, l_pad, out, heads * D, stream()))
     sync()
