@@ -34,9 +34,10 @@ except ImportError:  # a process without PyTorch uses the system runtime
 lib = ctypes.CDLL(LIB_PATH)
 
 # ---------------------------------------------------------------- constants
+MMDIT_ABI_VERSION = 2
 MMDIT_OK, MMDIT_E_NULL, MMDIT_E_ALIGN, MMDIT_E_SHAPE = 0, 1, 2, 3
 MMDIT_E_DTYPE, MMDIT_E_WORKSPACE, MMDIT_E_HIP, MMDIT_E_ARG = 4, 5, 6, 7
-MMDIT_BF16, MMDIT_INT8 = 0, 1
+MMDIT_BF16, MMDIT_INT8, MMDIT_F16 = 0, 1, 2
 MMDIT_WS_DOUBLE, MMDIT_WS_SINGLE, MMDIT_WS_STEP = 0, 1, 2
 (MMDIT_EPI_BIAS, MMDIT_EPI_BIAS_GELU, MMDIT_EPI_GATE_RESID, MMDIT_EPI_SPLIT_GELU,
  MMDIT_EPI_BIAS_F32, MMDIT_EPI_EULER) = range(6)
@@ -122,6 +123,7 @@ _SIGS = {
     "mmdit_k_time_embed": (c_int, [POINTER(mmdit_dims), POINTER(mmdit_model), c_float, c_float, _P, _P,
                                    c_size_t, _P]),
     "mmdit_k_euler": (c_int, [_P, _P, c_int64, c_float, _P]),
+    "mmdit_weights_to_f16": (c_int, [_P, _P, c_size_t, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -214,3 +216,7 @@ def mmdit_k_time_embed(dims, model, t, guidance, vec, ws, ws_bytes, stream=None)
 
 def mmdit_k_euler(z, v, n, dt, stream=None) -> int:
     return lib.mmdit_k_euler(ptr(z), ptr(v), n, dt, stream_handle(stream))
+
+
+def mmdit_weights_to_f16(src, dst, count, stream=None) -> int:
+    return lib.mmdit_weights_to_f16(ptr(src), ptr(dst), count, stream_handle(stream))

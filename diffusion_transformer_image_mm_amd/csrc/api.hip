@@ -14,6 +14,8 @@ size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+bool dtype_ok(int dt) { return dt == MMDIT_BF16 || dt == MMDIT_INT8 || dt == MMDIT_F16; }
+
 // Validate the sizes of a model. Returns MMDIT_OK or the status.
 int check_dims(const mmdit_dims* d) {
     if (!d) return MMDIT_E_NULL;
@@ -30,7 +32,7 @@ int check_dims(const mmdit_dims* d) {
     }
     if (sum != d->head_dim) return MMDIT_E_SHAPE;
     if (!(d->ln_eps > 0.f) || !(d->rms_eps > 0.f) || !(d->rope_theta > 1.f)) return MMDIT_E_SHAPE;
-    if (d->weight_dtype != MMDIT_BF16 && d->weight_dtype != MMDIT_INT8) return MMDIT_E_DTYPE;
+    if (!dtype_ok(d->weight_dtype)) return MMDIT_E_DTYPE;
     return MMDIT_OK;
 }
 
@@ -189,7 +191,7 @@ StepWs carve_step(const mmdit_dims* d, Carver& c) {
 // ---------------------------------------------------------------- helpers
 hipError_t gemv(const float* x, int k, const mmdit_linear& l, int n, int dt, int silu_in, int acc,
                 float* out, hipStream_t s) {
-    return launch_gemv(x, k, l.w, l.scale, l.bias, n, dt == MMDIT_INT8, silu_in, acc, out, s);
+    return launch_gemv(x, k, l.w, l.scale, l.bias, n, dt, silu_in, acc, out, s);
 }
 
 GemmGroup group(int row0, int m, const mmdit_linear& l, const float* gate = nullptr) {
@@ -207,7 +209,7 @@ GemmArgs gemm_base(int n, int k, int dt, const uint16_t* a, int lda, int epi, vo
     GemmArgs g = {};
     g.n = n;
     g.k = k;
-    g.int8 = dt == MMDIT_INT8;
+    g.wtype = dt;
     g.a = a;
     g.lda = lda;
     g.epilogue = epi;
@@ -505,7 +507,7 @@ int mmdit_k_gemm(const mmdit_gemm* g, hipStream_t s) {
     if (!g) return MMDIT_E_NULL;
     if (g->m < 1 || g->n < 64 || g->n % 64 != 0 || g->k < 64 || g->k % 64 != 0) return MMDIT_E_SHAPE;
     if (g->lda < g->k || g->lda % 8 != 0) return MMDIT_E_SHAPE;
-    if (g->weight_dtype != MMDIT_BF16 && g->weight_dtype != MMDIT_INT8) return MMDIT_E_DTYPE;
+    if (!dtype_ok(g->weight_dtype)) return MMDIT_E_DTYPE;
     if (g->epilogue < MMDIT_EPI_BIAS || g->epilogue > MMDIT_EPI_EULER) return MMDIT_E_ARG;
     MMDIT_TRY(check_ptr(g->a));
     MMDIT_TRY(check_linear(g->w, g->weight_dtype));
@@ -542,7 +544,7 @@ int mmdit_k_gemv(const float* x, int k, const mmdit_linear* w, int n, int weight
                  int accumulate, float* out, hipStream_t s) {
     if (!w) return MMDIT_E_NULL;
     if (k < 64 || k % 64 != 0 || n < 1 || k > 16384) return MMDIT_E_SHAPE;
-    if (weight_dtype != MMDIT_BF16 && weight_dtype != MMDIT_INT8) return MMDIT_E_DTYPE;
+    if (!dtype_ok(weight_dtype)) return MMDIT_E_DTYPE;
     MMDIT_TRY(check_ptr(x));
     MMDIT_TRY(check_linear(*w, weight_dtype));
     MMDIT_TRY(check_ptr(out));
@@ -563,6 +565,15 @@ int mmdit_k_time_embed(const mmdit_dims* d, const mmdit_model* m, float t, float
     if (ws_bytes < 4 * (512 + 2 * (size_t)d->hidden)) return MMDIT_E_WORKSPACE;
     float* emb = static_cast<float*>(ws);
     return run_time_embed(d, m, t, guidance, vec, emb, emb + 512, s);
+}
+
+int mmdit_weights_to_f16(const mmdit_bf16* src, mmdit_f16* dst, size_t count, hipStream_t s) {
+    MMDIT_TRY(check_ptr(src));
+    MMDIT_TRY(check_ptr(dst));
+    const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+    if (count > 0 && a < b + 2 * count && b < a + 2 * count) return MMDIT_E_ARG;
+    MMDIT_HIP(launch_bf16_to_f16(src, dst, count, s));
+    return MMDIT_OK;
 }
 
 int mmdit_k_euler(float* z, const float* v, int64_t n, float dt, hipStream_t s) {

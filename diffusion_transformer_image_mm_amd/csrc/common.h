@@ -107,7 +107,7 @@ struct GemmGroup {
 
 struct GemmArgs {
     int n, k;
-    int int8;
+    int wtype;   // enum mmdit_weight_dtype
     const uint16_t* a;
     int lda;
     int epilogue;
@@ -127,8 +127,11 @@ struct GemmArgs {
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 
 hipError_t launch_gemv(const float* x, int k, const void* w, const float* scale,
-                       const uint16_t* bias, int n, int int8, int silu_input, int accumulate,
+                       const uint16_t* bias, int n, int wtype, int silu_input, int accumulate,
                        float* out, hipStream_t s);
+
+// bf16 -> fp16 (round to nearest even), count elements
+hipError_t launch_bf16_to_f16(const uint16_t* src, uint16_t* dst, size_t count, hipStream_t s);
 
 // out[0:256] = emb(t), out[256:512] = emb(g)
 hipError_t launch_time_and_guidance_embedding(float t, float g, float* out, hipStream_t s);

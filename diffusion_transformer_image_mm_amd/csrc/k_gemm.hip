@@ -8,10 +8,12 @@
 // (flux-amd-rocm benchmarks page) keep int8 codes in HBM and apply the
 // per-channel scale to the fp32 sum.
 //
-// Operand formats: the weights are bf16 (or int8 codes) in HBM and LDS; each
-// weight fragment is converted in registers to fp16, which is exact (bf16's
-// 8-bit significand fits fp16's 11 bits; int8 codes are small integers) for
-// every weight of magnitude >= 2^-14 (smaller ones round at 2^-24). The
+// Operand formats: the weights are bf16, fp16 or int8 codes in HBM and LDS;
+// bf16 and int8 weight fragments are converted in registers to fp16, which
+// is exact (bf16's 8-bit significand fits fp16's 11 bits; int8 codes are
+// small integers) for every weight of magnitude >= 2^-14 (smaller ones round
+// at 2^-24). fp16 weights (bf16 weights converted once, the same rounding)
+// skip that conversion: 12 VALU operations per 8 weights per use. The
 // activation operand A (LayerNorm outputs, attention output, GELU hidden) is
 // stored in fp16 by the kernel that produced it: at FLUX size, bf16 storage
 // of these activations alone puts the block output at ~2e-2 of its RMS away
@@ -37,7 +39,7 @@
 // * one barrier per k-step: all fragments of the current stage are read into
 //   registers before the next stage's loads are issued;
 // * grouped launch: up to two weight sets (text / image stream) over
-//   disjoint row ranges in one grid;
+//   disjoint row ranges in one grid; tiles are laid out per XCD (tile_of);
 // * M and N tails: loads clamp to the last valid row, stores are guarded;
 // * deterministic (no atomics, fixed k order).
 #include "common.h"
@@ -99,32 +101,50 @@ struct TileCoord {
     int n0;      // first output column
 };
 
-MMDIT_DEV TileCoord tile_of(const GemmArgs& a, int bid) {
+// Workgroup -> output tile. Workgroups are dispatched round-robin over the
+// 8 XCDs (workgroup b runs on XCD b % 8), and each XCD has its own L2. Each
+// XCD is therefore given one contiguous run of the tile list, and the list
+// walks the tiles of a group in bands of RASTER_ROWS tile rows, column by
+// column: the ~32 tiles an XCD runs at once then form a compact block that
+// shares A rows and W rows in its L2 (instead of ~6 rows and ~6 columns
+// spread over the whole output, or 18 rows x 3 columns for N = 3072).
+constexpr int RASTER_ROWS = 6;
+
+MMDIT_DEV TileCoord tile_of(const GemmArgs& a, int bid, int total) {
+    const int x = bid & 7, j = bid >> 3, q = total >> 3, r = total & 7;
+    int idx = x * q + (x < r ? x : r) + j;   // a bijection on [0, total)
     const int tn = (a.n + BN - 1) / BN;
-    const int t0 = ((a.g[0].m + BM - 1) / BM) * tn;
+    const int tm0 = (a.g[0].m + BM - 1) / BM;
     TileCoord c;
-    if (bid < t0 || a.ngroups == 1) {
+    int tm = tm0;
+    if (a.ngroups == 1 || idx < tm0 * tn) {
         c.g = 0;
     } else {
         c.g = 1;
-        bid -= t0;
+        idx -= tm0 * tn;
+        tm = (a.g[1].m + BM - 1) / BM;
     }
-    c.m0 = (bid / tn) * BM;
-    c.n0 = (bid % tn) * BN;
+    const int band = idx / (RASTER_ROWS * tn), rem = idx - band * RASTER_ROWS * tn;
+    const int r0 = band * RASTER_ROWS;
+    const int rows = (tm - r0) < RASTER_ROWS ? (tm - r0) : RASTER_ROWS;
+    c.m0 = (r0 + rem % rows) * BM;
+    c.n0 = (rem / rows) * BN;
     return c;
 }
 
 }  // namespace
 
-template <bool INT8, int EPI>
+template <int WT, int EPI>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) {
+    constexpr bool INT8 = WT == MMDIT_INT8;
+    constexpr bool F16W = WT == MMDIT_F16;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
-    constexpr int WT = INT8 ? W_TILE_BYTES_I8 : W_TILE_BYTES_BF16;
-    constexpr int STAGE = A_TILE_BYTES + WT;
+    constexpr int W_TILE = INT8 ? W_TILE_BYTES_I8 : W_TILE_BYTES_BF16;   // fp16: as bf16
+    constexpr int STAGE = A_TILE_BYTES + W_TILE;
     constexpr int TM = 8, TN = 4;   // MFMA sub-tiles per wavefront (m, n)
     // stage s: A tile at smem + s*STAGE, W tile right after it
 
-    const TileCoord tc = tile_of(args, blockIdx.x);
+    const TileCoord tc = tile_of(args, blockIdx.x, gridDim.x);
     const GemmGroup& G = args.g[tc.g];
     const int M = G.m, N = args.n, K = args.k;
     const int tid = threadIdx.x;
@@ -227,7 +247,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) 
             for (int i = 0; i < TM; ++i) fa[ks][i] = lds_frag_h(sa + a_off[ks] + i * 16 * 128);
 #pragma unroll
             for (int i = 0; i < TN; ++i) {
-                if (!INT8)
+                if (F16W)
+                    fw[ks][i] = lds_frag_h(sw + w_off[ks] + i * 16 * 128);
+                else if (!INT8)
                     fw[ks][i] = bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(sw + w_off[ks] + i * 16 * 128));
                 else
                     fw[ks][i] = i8x8_to_f16x8(*reinterpret_cast<const uint2*>(sw + w_off[ks] + i * 16 * 64));
@@ -313,8 +335,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) 
     }
 }
 
-template <bool INT8>
+template <int WT>
 static hipError_t launch_gemm_t(const GemmArgs& a, hipStream_t s) {
+    constexpr bool INT8 = WT == MMDIT_INT8;
     const int tn = (a.n + BN - 1) / BN;
     int tiles = 0;
     for (int g = 0; g < a.ngroups; ++g) tiles += ((a.g[g].m + BM - 1) / BM) * tn;
@@ -323,7 +346,7 @@ static hipError_t launch_gemm_t(const GemmArgs& a, hipStream_t s) {
     dim3 grid(tiles), block(NTHREADS);
 #define GEMM_CASE(E)                                                                        \
     case E: {                                                                               \
-        auto kfn = gemm_kernel<INT8, E>;                                                    \
+        auto kfn = gemm_kernel<WT, E>;                                                    \
         static bool attr_done = false;                                                      \
         if (!attr_done) {                                                                   \
             hipError_t e = hipFuncSetAttribute((const void*)kfn,                            \
@@ -350,7 +373,12 @@ static hipError_t launch_gemm_t(const GemmArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
-    return a.int8 ? launch_gemm_t<true>(a, s) : launch_gemm_t<false>(a, s);
+    switch (a.wtype) {
+        case MMDIT_BF16: return launch_gemm_t<MMDIT_BF16>(a, s);
+        case MMDIT_INT8: return launch_gemm_t<MMDIT_INT8>(a, s);
+        case MMDIT_F16: return launch_gemm_t<MMDIT_F16>(a, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace mmdit

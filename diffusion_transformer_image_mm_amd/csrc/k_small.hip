@@ -9,11 +9,11 @@ namespace mmdit {
 // out[n] (+)= sum_k W[n,k] act(x[k]) + b[n]
 //
 // The modulation layers read a [6H, H] weight for one conditioning vector:
-// pure weight streaming (HBM-bound, 2 B per weight in bf16, 1 B in int8).
+// pure weight streaming (HBM-bound, 2 B per weight in bf16/fp16, 1 B in int8).
 // act(x) is staged once per workgroup in LDS; each wavefront owns one output
 // row at a time and reads it with 16-byte loads, then reduces across lanes.
 // ---------------------------------------------------------------------------
-template <bool INT8>
+template <int WT>
 __global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ x, int k,
                                                    const void* __restrict__ w,
                                                    const float* __restrict__ scale,
@@ -29,6 +29,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ x, 
     const int lane = threadIdx.x & 63;
     const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int nwaves = gridDim.x * 4;
+    constexpr bool INT8 = WT == MMDIT_INT8;
     constexpr int EPL = INT8 ? 16 : 8;  // elements per 16-byte load
     for (int row = wave; row < n; row += nwaves) {
         float acc = 0.f;
@@ -46,7 +47,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ x, 
                 const uint4 raw = *reinterpret_cast<const uint4*>(wr + c);
                 const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc += bf2f(e[i]) * xs[c + i];
+                for (int i = 0; i < 8; ++i) acc += (WT == MMDIT_F16 ? h2f(e[i]) : bf2f(e[i])) * xs[c + i];
             }
         }
         acc = wave_sum(acc);
@@ -58,17 +59,51 @@ __global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ x, 
 }
 
 hipError_t launch_gemv(const float* x, int k, const void* w, const float* scale,
-                       const uint16_t* bias, int n, int int8, int silu_input, int accumulate,
+                       const uint16_t* bias, int n, int wtype, int silu_input, int accumulate,
                        float* out, hipStream_t s) {
     int blocks = (n + 3) / 4;
     if (blocks > 2048) blocks = 2048;
     const size_t lds = (size_t)k * sizeof(float);
-    if (int8)
-        hipLaunchKernelGGL(gemv_kernel<true>, dim3(blocks), dim3(256), lds, s, x, k, w, scale, bias, n,
-                           silu_input, accumulate, out);
-    else
-        hipLaunchKernelGGL(gemv_kernel<false>, dim3(blocks), dim3(256), lds, s, x, k, w, scale, bias,
-                           n, silu_input, accumulate, out);
+#define GEMV_CASE(T)                                                                               \
+    case T:                                                                                        \
+        hipLaunchKernelGGL(gemv_kernel<T>, dim3(blocks), dim3(256), lds, s, x, k, w, scale, bias, n, \
+                           silu_input, accumulate, out);                                           \
+        break;
+    switch (wtype) {
+        GEMV_CASE(MMDIT_BF16) GEMV_CASE(MMDIT_INT8) GEMV_CASE(MMDIT_F16)
+        default: return hipErrorInvalidValue;
+    }
+#undef GEMV_CASE
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// bf16 -> fp16, round to nearest even (the conversion the GEMM applies to
+// bf16 weight fragments), 8 values per 16-byte load and store.
+// ---------------------------------------------------------------------------
+__global__ void bf16_to_f16_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                   size_t count) {
+    const size_t n8 = count / 8;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
+        const uint4 v = reinterpret_cast<const uint4*>(src)[i];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            o[j] = pack2h(__uint_as_float(w[j] << 16), __uint_as_float(w[j] & 0xffff0000u));
+        reinterpret_cast<uint4*>(dst)[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    for (size_t i = n8 * 8 + (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride)
+        dst[i] = f2h(bf2f(src[i]));
+}
+
+hipError_t launch_bf16_to_f16(const uint16_t* src, uint16_t* dst, size_t count, hipStream_t s) {
+    if (count == 0) return hipSuccess;
+    size_t blocks = (count / 8 + 255) / 256;
+    if (blocks < 1) blocks = 1;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(bf16_to_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, count);
     return hipGetLastError();
 }
 

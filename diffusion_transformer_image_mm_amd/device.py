@@ -16,20 +16,25 @@ from . import synth
 
 
 class DeviceArena:
-    """Owns device tensors so that the addresses in ABI structs stay valid."""
+    """Owns device tensors so that the addresses in ABI structs stay valid.
+    With f16_weights, the bf16 weights of every non-int8 linear are uploaded
+    and re-encoded on the device by mmdit_weights_to_f16 (MMDIT_F16)."""
 
-    def __init__(self, device: str = "cuda"):
+    def __init__(self, device: str = "cuda", f16_weights: bool = False):
         self.device = torch.device(device)
         self.keep: List[torch.Tensor] = []
+        self.f16_weights = f16_weights
 
     def _hold(self, t: torch.Tensor) -> torch.Tensor:
         self.keep.append(t)
         return t
 
-    def bf16(self, a: np.ndarray) -> torch.Tensor:
+    def _upload_bf16(self, a: np.ndarray) -> torch.Tensor:
         bits = synth.bf16_bits(np.asarray(a, dtype=np.float32))
-        t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
-        return self._hold(t.to(self.device))
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(self.device)
+
+    def bf16(self, a: np.ndarray) -> torch.Tensor:
+        return self._hold(self._upload_bf16(a))
 
     def f16(self, a: np.ndarray) -> torch.Tensor:
         t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32).astype(np.float16))
@@ -64,7 +69,10 @@ class DeviceArena:
             q = self.i8(lin.q)
             s = self.f32(lin.s)
             return B.mmdit_linear(q.data_ptr(), s.data_ptr(), b.data_ptr())
-        w = self.bf16(lin.w)
+        if self.f16_weights:
+            w = self._hold(to_f16_weights(self._upload_bf16(lin.w)))
+        else:
+            w = self.bf16(lin.w)
         return B.mmdit_linear(w.data_ptr(), None, b.data_ptr())
 
     def stream_weights(self, s: Dict) -> B.mmdit_stream_weights:
@@ -97,6 +105,16 @@ class DeviceArena:
         return mm
 
 
+def to_f16_weights(w: torch.Tensor) -> torch.Tensor:
+    """bf16 device weights -> the fp16 copy that mmdit_weights_to_f16 makes on
+    the current stream (the torch allocator orders any reuse of w's memory
+    after that stream's work, so w may be dropped right away)."""
+    assert w.dtype == torch.bfloat16 and w.is_contiguous()
+    out = torch.empty(w.shape, dtype=torch.float16, device=w.device)
+    B.check(B.mmdit_weights_to_f16(w, out, w.numel(), torch.cuda.current_stream()))
+    return out
+
+
 class TimingModel:
     """A whole denoiser with random weights drawn directly in HBM (seeded torch
     device generator), for timing the full-depth step where host generation
@@ -106,11 +124,12 @@ class TimingModel:
     RMSNorm scales U(0.5, 1.5). Values are not checked against the oracle
     (the parity tests use the host generator)."""
 
-    def __init__(self, shp: synth.Shape, int8: bool, seed: int = 42, device: str = "cuda"):
+    def __init__(self, shp: synth.Shape, int8: bool, seed: int = 42, device: str = "cuda", f16: bool = False):
         self.dev = torch.device(device)
         self.gen = torch.Generator(device=self.dev)
         self.gen.manual_seed(seed)
         self.int8 = int8
+        self.f16 = f16 and not int8
         self.keep: List[torch.Tensor] = []
         H, M, C, D = shp.hidden, shp.mlp, shp.in_channels, shp.head_dim
         mk = self._linear
@@ -144,21 +163,23 @@ class TimingModel:
             q = self._hold(torch.randint(-127, 128, (n, k), generator=self.gen, device=self.dev, dtype=torch.int8))
             s = self._hold(torch.full((n,), 0.02 / 73.6, device=self.dev, dtype=torch.float32))
             return B.mmdit_linear(q, s, b)
-        w = self._hold((torch.randn(n, k, generator=self.gen, device=self.dev) * 0.02).to(torch.bfloat16))
-        return B.mmdit_linear(w, None, b)
+        w = (torch.randn(n, k, generator=self.gen, device=self.dev) * 0.02).to(torch.bfloat16)
+        if self.f16:
+            w = to_f16_weights(w)
+        return B.mmdit_linear(self._hold(w), None, b)
 
     def _norm(self, d: int) -> int:
         return self._hold((torch.rand(d, generator=self.gen, device=self.dev) + 0.5).to(torch.bfloat16))
 
 
-def dims_for(shp: synth.Shape, int8: bool = False) -> B.mmdit_dims:
+def dims_for(shp: synth.Shape, int8: bool = False, f16: bool = False) -> B.mmdit_dims:
     d = B.mmdit_dims()
     d.txt_len, d.img_len = shp.txt_len, shp.img_len
     d.hidden, d.heads, d.head_dim, d.mlp_hidden = shp.hidden, shp.heads, shp.head_dim, shp.mlp
     d.in_channels = shp.in_channels
     d.rope_axes[0], d.rope_axes[1], d.rope_axes[2] = shp.axes
     d.rope_theta, d.ln_eps, d.rms_eps = shp.theta, shp.ln_eps, shp.rms_eps
-    d.weight_dtype = B.MMDIT_INT8 if int8 else B.MMDIT_BF16
+    d.weight_dtype = B.MMDIT_INT8 if int8 else (B.MMDIT_F16 if f16 else B.MMDIT_BF16)
     d.n_double, d.n_single = shp.n_double, shp.n_single
     return d
 

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MMDIT_ABI_VERSION 1
+#define MMDIT_ABI_VERSION 2
 
 /* raw bfloat16 bits */
 typedef uint16_t mmdit_bf16;
@@ -70,9 +70,16 @@ enum mmdit_status {
 
 enum mmdit_weight_dtype {
     MMDIT_BF16 = 0, /* weights are bf16 [out, in] */
-    MMDIT_INT8 = 1  /* weights are int8 codes [out, in] with fp32 scale [out]:
+    MMDIT_INT8 = 1, /* weights are int8 codes [out, in] with fp32 scale [out]:
                        W = diag(scale) * codes (flux-amd-rocm benchmarks page:
                        int8 weight-only linears) */
+    MMDIT_F16 = 2   /* weights are fp16 [out, in]: bf16 weights re-encoded once
+                       by mmdit_weights_to_f16. The matrix cores take both
+                       operands in one format and the activation operands are
+                       fp16, so the bf16 path converts every weight fragment
+                       in registers on every use; this format does it once.
+                       Same rounding, so results are bit-identical to
+                       MMDIT_BF16 with the bf16 originals */
 };
 
 /* ------------------------------------------------------------------ sizes */
@@ -209,7 +216,7 @@ int mmdit_single_block_forward(const mmdit_dims* dims, const mmdit_single_weight
  *   latent: fp32 [img_len, in_channels], updated in place
  *   txt:    fp32 [txt_len, H] text states
  *   rope:   fp32 [L, D/2, 2]
- *   dims->weight_dtype selects bf16 or int8 weights for every linear.
+ *   dims->weight_dtype selects bf16, fp16 or int8 weights for every linear.
  */
 int mmdit_denoise_step(const mmdit_dims* dims, const mmdit_model* model,
                        float* latent, const float* txt, const float* rope,
@@ -228,6 +235,17 @@ int mmdit_rope_table(const mmdit_dims* dims, const int32_t* ids, float* rope,
 
 const char* mmdit_status_string(int status);
 int mmdit_abi_version(void);
+
+/*
+ * Re-encode bf16 weights as fp16 for MMDIT_F16 (a load-time step, like the
+ * upload of the weights). Each value is rounded to nearest-even fp16: exact
+ * for magnitudes in [2^-14, 65504]; smaller ones round to fp16 subnormals
+ * (steps of 2^-24); magnitudes >= 65520 become infinities. These are the
+ * values the bf16 path feeds its matrix cores.
+ *   src: bf16 [count]; dst: fp16 [count]; both 16-byte aligned, may not overlap.
+ * Errors: E_NULL, E_ALIGN; count 0 enqueues nothing.
+ */
+int mmdit_weights_to_f16(const mmdit_bf16* src, mmdit_f16* dst, size_t count, hipStream_t stream);
 
 /* ------------------------------------------------------------------ kernels */
 /*
@@ -292,9 +310,10 @@ enum mmdit_epilogue {
 };
 
 /*
- * out = epilogue(A W^T): A fp16 [m, k] (row stride lda), W = w.w [n, k] bf16
- * or int8 (weight_dtype). k a multiple of 64, n a multiple of 64, m >= 1.
- * Weight fragments are converted to fp16 in registers (exact, see above);
+ * out = epilogue(A W^T): A fp16 [m, k] (row stride lda), W = w.w [n, k] bf16,
+ * fp16 or int8 (weight_dtype). k a multiple of 64, n a multiple of 64, m >= 1.
+ * bf16 and int8 weight fragments are converted to fp16 in registers (see
+ * above);
  * accumulation in fp32; the int8 per-channel scale multiplies the fp32 sum.
  */
 typedef struct mmdit_gemm {

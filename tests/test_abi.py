@@ -21,7 +21,7 @@ def test_exports_every_header_function():
 
 
 def test_abi_version_and_status_strings():
-    assert B.mmdit_abi_version() == 1
+    assert B.mmdit_abi_version() == B.MMDIT_ABI_VERSION == 2
     for st in range(8):
         assert B.mmdit_status_string(st)
     assert B.mmdit_status_string(99) == "unknown status"
@@ -117,9 +117,22 @@ def test_kernel_entry_validation():
     assert B.mmdit_k_gemm(g) == B.MMDIT_E_NULL  # gate / resid missing
     g.epilogue, g.weight_dtype = 0, B.MMDIT_INT8
     assert B.mmdit_k_gemm(g) == B.MMDIT_E_DTYPE  # int8 without scales
+    g.weight_dtype = 3
+    assert B.mmdit_k_gemm(g) == B.MMDIT_E_DTYPE
     lin = _linear()
     assert B.mmdit_k_gemv(FAKE, 100, lin, 10, 0, 1, 0, FAKE) == B.MMDIT_E_SHAPE
+    assert B.mmdit_k_gemv(FAKE, 128, lin, 10, 3, 1, 0, FAKE) == B.MMDIT_E_DTYPE
     assert B.mmdit_k_euler(FAKE + 8, FAKE, 10, 0.1) == B.MMDIT_E_ALIGN
+
+
+def test_weight_conversion_validation():
+    assert B.mmdit_weights_to_f16(0, FAKE, 8) == B.MMDIT_E_NULL
+    assert B.mmdit_weights_to_f16(FAKE, FAKE + 2, 8) == B.MMDIT_E_ALIGN
+    assert B.mmdit_weights_to_f16(FAKE, FAKE + 16, 64) == B.MMDIT_E_ARG   # overlapping ranges
+    assert B.mmdit_weights_to_f16(FAKE, FAKE + 128, 0) == B.MMDIT_OK      # nothing to do
+    d = _dims(weight_dtype=B.MMDIT_F16)
+    assert B.mmdit_workspace_bytes(d, B.MMDIT_WS_DOUBLE) > 0
+    assert B.mmdit_workspace_bytes(_dims(weight_dtype=3), B.MMDIT_WS_DOUBLE) == 0
 
 
 def test_one_hip_runtime_per_process():

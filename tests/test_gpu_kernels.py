@@ -217,13 +217,13 @@ GEMM_CASES = [
 _RESID = [None]
 
 
-def _run_gemm(m, n, k, epi, int8, rows=None, tid=50):
-    A = DeviceArena()
+def _run_gemm(m, n, k, epi, int8, rows=None, tid=50, f16=False):
+    A = DeviceArena(f16_weights=f16)
     a = synth.f16_exact(rnd(tid, (m, k)))  # the fp16 activation operand both sides read
     lin = _lin(tid + 2, n, k, int8)
     da = A.f16(a)
-    g = B.mmdit_gemm(m=m, n=n, k=k, weight_dtype=B.MMDIT_INT8 if int8 else B.MMDIT_BF16, a=da.data_ptr(),
-                     lda=k, w=A.linear(lin), epilogue=epi)
+    wt = B.MMDIT_INT8 if int8 else (B.MMDIT_F16 if f16 else B.MMDIT_BF16)
+    g = B.mmdit_gemm(m=m, n=n, k=k, weight_dtype=wt, a=da.data_ptr(), lda=k, w=A.linear(lin), epilogue=epi)
     split = 3 * n // 7 // 64 * 64 if epi == B.MMDIT_EPI_SPLIT_GELU else n
     _SPLIT[0] = split
     gate = rnd(tid + 5, (n,), 0.7)
@@ -310,19 +310,54 @@ def test_gemm_int8_rerun_bit_exact():
     np.testing.assert_array_equal(a1, a2)
 
 
+@pytest.mark.parametrize("m,n,k,epi", [(513, 1024, 256, B.MMDIT_EPI_BIAS_GELU), (700, 256, 1024, B.MMDIT_EPI_GATE_RESID),
+                                       (320, 1792, 256, B.MMDIT_EPI_SPLIT_GELU), (1, 128, 64, B.MMDIT_EPI_BIAS),
+                                       (4608, 3072, 12288, B.MMDIT_EPI_GATE_RESID)])
+def test_gemm_f16_weights_bit_identical(m, n, k, epi):
+    """Weights re-encoded once by mmdit_weights_to_f16 give the bf16 path's
+    results bit for bit (same fp16 values reach the matrix cores)."""
+    say(f"gemm f16 weights m={m} n={n} k={k} epi={epi}")
+    rows = None if m < 4096 else np.unique(np.r_[0, 255, 256, m - 1, np.arange(0, m, 97)])
+    a, ref = _run_gemm(m, n, k, epi, False, rows=rows, tid=90)
+    b, _ = _run_gemm(m, n, k, epi, False, rows=rows, tid=90, f16=True)
+    np.testing.assert_array_equal(a, b)
+    assert _gemm_err(b, ref, epi, k) <= TOL
+
+
+def test_weights_to_f16_exhaustive():
+    """Every bf16 bit pattern (plus a ragged tail) against numpy's
+    round-to-nearest-even float32 -> float16 conversion: subnormal results,
+    overflow to infinity, signed zeros; NaN stays NaN."""
+    say("weights_to_f16 all bf16 patterns")
+    bits = np.r_[np.arange(65536, dtype=np.uint32), np.array([0x3f80, 0x0001, 0x8001, 0x477f, 0x4780], np.uint32)]
+    bits = bits.astype(np.uint16)
+    src = torch.from_numpy(bits.view(np.int16)).cuda()
+    dst = torch.empty(bits.size, dtype=torch.int16, device="cuda")
+    B.check(B.mmdit_weights_to_f16(src, dst, bits.size, stream()))
+    sync()
+    got = dst.cpu().numpy().view(np.uint16)
+    with np.errstate(over="ignore", invalid="ignore"):
+        ref = synth.bits_to_f32(bits).astype(np.float16).view(np.uint16)
+    nan = np.isnan(synth.bits_to_f32(bits))
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+    assert np.all(np.isnan(got[nan].view(np.float16)))
+
+
 # ------------------------------------------------------------------ GEMV
-@pytest.mark.parametrize("n,k,int8,silu_in,acc", [(1536, 256, False, 1, 0), (18432, 3072, False, 1, 0),
-                                                   (18432, 3072, True, 1, 0), (3072, 256, True, 0, 1),
-                                                   (100, 64, False, 0, 1)])
-def test_gemv(n, k, int8, silu_in, acc):
-    say(f"gemv n={n} k={k} int8={int8}")
-    A = DeviceArena()
+@pytest.mark.parametrize("n,k,wt,silu_in,acc", [(1536, 256, "bf16", 1, 0), (18432, 3072, "bf16", 1, 0),
+                                                (18432, 3072, "int8", 1, 0), (3072, 256, "int8", 0, 1),
+                                                (100, 64, "bf16", 0, 1), (18432, 3072, "f16", 1, 0),
+                                                (100, 64, "f16", 0, 1)])
+def test_gemv(n, k, wt, silu_in, acc):
+    say(f"gemv n={n} k={k} weights={wt}")
+    int8, f16 = wt == "int8", wt == "f16"
+    A = DeviceArena(f16_weights=f16)
     x = rnd(80, (k,))
     lin = _lin(81, n, k, int8)
     base = rnd(83, (n,))
     out = A.f32(base)
-    B.check(B.mmdit_k_gemv(A.f32(x), k, A.linear(lin), n, B.MMDIT_INT8 if int8 else B.MMDIT_BF16, silu_in, acc,
-                           out, stream()))
+    dt = B.MMDIT_INT8 if int8 else (B.MMDIT_F16 if f16 else B.MMDIT_BF16)
+    B.check(B.mmdit_k_gemv(A.f32(x), k, A.linear(lin), n, dt, silu_in, acc, out, stream()))
     sync()
     xin = O.silu(x) if silu_in else x
     ref = O.linear(xin[None, :], lin)[0] + (base if acc else 0)
