@@ -54,6 +54,38 @@ def step_flops(shp) -> float:
     return shp.n_double * block_flops(shp) + shp.n_single * single_flops(shp) + extra
 
 
+def probe(shp, stream, log) -> int:
+    """The dominant kernel alone, as bench.py times it (fp16-encoded MLP-in
+    weights of the FLUX block, fp16 activations, BIAS_GELU epilogue), then a
+    plain 1 GiB device-to-device copy of known size, to calibrate the HBM
+    byte counters (FETCH_SIZE / WRITE_SIZE) of rocprofv3 --pmc runs."""
+    import torch
+
+    from diffusion_transformer_image_mm_amd import binding as B
+    from diffusion_transformer_image_mm_amd.device import to_f16_weights
+
+    L, H, M = shp.seq_len, shp.hidden, shp.mlp
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(42)
+    w = to_f16_weights((torch.randn(M, H, generator=gen, device="cuda") * 0.02).to(torch.bfloat16))
+    bias = (torch.randn(M, generator=gen, device="cuda") * 0.02).to(torch.bfloat16)
+    a = torch.randn(L, H, generator=gen, device="cuda").to(torch.float16)
+    out = torch.empty(L, M, dtype=torch.float16, device="cuda")
+    g = B.mmdit_gemm(m=L, n=M, k=H, weight_dtype=B.MMDIT_F16, a=a.data_ptr(), lda=H,
+                     w=B.mmdit_linear(w.data_ptr(), None, bias.data_ptr()), epilogue=B.MMDIT_EPI_BIAS_GELU,
+                     out=out.data_ptr(), ldo=M)
+    for _ in range(10):
+        B.check(B.mmdit_k_gemm(g, stream), "gemm")
+    torch.cuda.synchronize()
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"probe: 10 x gemm {L}x{M}x{H} (fp16 weights, BIAS_GELU), 3 x copy of {src.numel() * 4} bytes")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -62,6 +94,9 @@ def main() -> int:
     ap.add_argument("--no-step", action="store_true", help="skip the full denoise-step timing")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--probe", action="store_true",
+                    help="only launch the dominant kernel (MLP-in GEMM, 10x) and a 1 GiB device copy (3x), "
+                         "for hardware-counter runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -82,6 +117,9 @@ def main() -> int:
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     shp = synth.FLUX_DOUBLE
+
+    if args.probe:
+        return probe(shp, stream, log)
 
     # ------------------------------------------------------------ block
     log("bench: generating FLUX double-block inputs")
@@ -154,6 +192,11 @@ def main() -> int:
     gemm_tflops = gemm_flops / (ms_gemm * 1e-3) / 1e12
     log(f"bench: fc1 GEMM {L}x{M}x{H} {ms_gemm * 1e3:.1f} us -> {gemm_tflops:.1f} TFLOP/s")
 
+    from diffusion_transformer_image_mm_amd.traffic import load_traffic
+    traffic = load_traffic()   # HBM bytes per launch from the committed counter summary, None if stale
+    if traffic is not None:
+        traffic = round(traffic)
+
     result = {
         "metric": "MM-DiT block TFLOP/s + ms/denoise step (bf16, FLUX-shaped 1024^2, 1 GPU)",
         "value": round(tflops, 2),
@@ -177,7 +220,7 @@ def main() -> int:
                    "tflops_bf16_weights": round(flops / (ms_block_bf16 * 1e-3) / 1e12, 2)},
         "roofline": {"kernel": "gemm_kernel<f16 weights, BIAS_GELU> (MLP-in, 4608x12288x3072)", "bound": "mfma",
                      "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "avg_us": round(ms_gemm * 1e3, 2)},
     }
 

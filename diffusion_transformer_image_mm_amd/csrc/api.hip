@@ -189,9 +189,31 @@ StepWs carve_step(const mmdit_dims* d, Carver& c) {
 }
 
 // ---------------------------------------------------------------- helpers
+GemvSet gemv_set(const mmdit_linear& l, float* out) {
+    GemvSet g;
+    g.w = l.w;
+    g.scale = l.scale;
+    g.bias = l.bias;
+    g.out = out;
+    return g;
+}
+
 hipError_t gemv(const float* x, int k, const mmdit_linear& l, int n, int dt, int silu_in, int acc,
                 float* out, hipStream_t s) {
-    return launch_gemv(x, k, l.w, l.scale, l.bias, n, dt, silu_in, acc, out, s);
+    GemvSets g = {};
+    g.count = 1;
+    g.s[0] = gemv_set(l, out);
+    return launch_gemv(x, k, n, dt, silu_in, acc, g, s);
+}
+
+// two weight sets of the same shape over the same input, one launch
+hipError_t gemv_2(const float* x, int k, const mmdit_linear& l0, float* out0, const mmdit_linear& l1,
+                  float* out1, int n, int dt, int silu_in, hipStream_t s) {
+    GemvSets g = {};
+    g.count = 2;
+    g.s[0] = gemv_set(l0, out0);
+    g.s[1] = gemv_set(l1, out1);
+    return launch_gemv(x, k, n, dt, silu_in, 0, g, s);
 }
 
 GemmGroup group(int row0, int m, const mmdit_linear& l, const float* gate = nullptr) {
@@ -245,8 +267,7 @@ int run_double(const mmdit_dims* d, const mmdit_double_weights* w, const float* 
     float* mt = ws.mod;
     float* mi = ws.mod + 6 * H;
     // a1: modulation of each stream
-    MMDIT_HIP(gemv(vec, H, w->txt.mod, 6 * H, dt, 1, 0, mt, s));
-    MMDIT_HIP(gemv(vec, H, w->img.mod, 6 * H, dt, 1, 0, mi, s));
+    MMDIT_HIP(gemv_2(vec, H, w->txt.mod, mt, w->img.mod, mi, 6 * H, dt, 1, s));
     // a2: LN1 + modulate
     MMDIT_HIP(launch_ln_modulate(x_in, L, H, Lt, mt, mt + H, mi, mi + H, d->ln_eps, ws.h, s));
     // a3: QKV
@@ -543,7 +564,7 @@ int mmdit_k_gemm(const mmdit_gemm* g, hipStream_t s) {
 int mmdit_k_gemv(const float* x, int k, const mmdit_linear* w, int n, int weight_dtype, int silu_input,
                  int accumulate, float* out, hipStream_t s) {
     if (!w) return MMDIT_E_NULL;
-    if (k < 64 || k % 64 != 0 || n < 1 || k > 16384) return MMDIT_E_SHAPE;
+    if (k < 64 || k % 64 != 0 || n < 1 || k > 4096) return MMDIT_E_SHAPE;
     if (!dtype_ok(weight_dtype)) return MMDIT_E_DTYPE;
     MMDIT_TRY(check_ptr(x));
     MMDIT_TRY(check_linear(*w, weight_dtype));

@@ -126,9 +126,20 @@ struct GemmArgs {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 
-hipError_t launch_gemv(const float* x, int k, const void* w, const float* scale,
-                       const uint16_t* bias, int n, int wtype, int silu_input, int accumulate,
-                       float* out, hipStream_t s);
+struct GemvSet {
+    const void* w;          // [n, k] bf16 / fp16 / int8 codes
+    const float* scale;     // [n], int8 only
+    const uint16_t* bias;   // [n] bf16
+    float* out;             // [n] fp32
+};
+struct GemvSets {
+    int count;              // 1 or 2
+    GemvSet s[2];
+};
+
+// k <= 4096 and a multiple of 16
+hipError_t launch_gemv(const float* x, int k, int n, int wtype, int silu_input, int accumulate,
+                       const GemvSets& sets, hipStream_t s);
 
 // bf16 -> fp16 (round to nearest even), count elements
 hipError_t launch_bf16_to_f16(const uint16_t* src, uint16_t* dst, size_t count, hipStream_t s);

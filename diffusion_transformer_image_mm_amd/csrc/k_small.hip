@@ -6,75 +6,97 @@
 namespace mmdit {
 
 // ---------------------------------------------------------------------------
-// out[n] (+)= sum_k W[n,k] act(x[k]) + b[n]
+// out_g[r] (+)= sum_k W_g[r,k] act(x[k]) + b_g[r], r < n, for one or two
+// weight sets g that share the input x (the text and image stream
+// modulations of a double block share the conditioning vector).
 //
-// The modulation layers read a [6H, H] weight for one conditioning vector:
-// pure weight streaming (HBM-bound, 2 B per weight in bf16/fp16, 1 B in int8).
-// act(x) is staged once per workgroup in LDS; each wavefront owns one output
-// row at a time and reads it with 16-byte loads, then reduces across lanes.
+// Pure weight streaming (HBM-bound: 2 B per weight in bf16/fp16, 1 B in
+// int8). Lane l owns the columns l*E + i*64*E (E = 8 16-bit or 16 int8
+// weights = one 16-byte load, i < NL) of every row; it keeps act(x) of those
+// columns in registers, and each wavefront issues the loads of RPW rows
+// before it reduces any of them, so ~RPW*NL*1 KB per wavefront is in flight.
 // ---------------------------------------------------------------------------
-template <int WT>
-__global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ x, int k,
-                                                   const void* __restrict__ w,
-                                                   const float* __restrict__ scale,
-                                                   const uint16_t* __restrict__ bias, int n,
-                                                   int silu_input, int accumulate,
-                                                   float* __restrict__ out) {
-    extern __shared__ float xs[];
-    for (int i = threadIdx.x; i < k; i += 256) {
-        float v = x[i];
-        xs[i] = silu_input ? silu(v) : v;
-    }
-    __syncthreads();
-    const int lane = threadIdx.x & 63;
-    const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int nwaves = gridDim.x * 4;
+constexpr int GEMV_RPW = 4;
+
+template <int WT, int NL>
+__global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ x, int k, int n,
+                                                   int silu_input, int accumulate, const GemvSets sets) {
     constexpr bool INT8 = WT == MMDIT_INT8;
-    constexpr int EPL = INT8 ? 16 : 8;  // elements per 16-byte load
-    for (int row = wave; row < n; row += nwaves) {
+    constexpr int E = INT8 ? 16 : 8;
+    const int lane = threadIdx.x & 63;
+    const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * GEMV_RPW;
+    const int rows = sets.count * n;
+    if (row0 >= rows) return;
+    float xs[NL][E];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int c = lane * E + i * 64 * E;
+#pragma unroll
+        for (int q = 0; q < E / 4; ++q) {
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (c < k) v = *reinterpret_cast<const float4*>(x + c + 4 * q);
+            if (silu_input) { v.x = silu(v.x); v.y = silu(v.y); v.z = silu(v.z); v.w = silu(v.w); }
+            xs[i][4 * q] = v.x; xs[i][4 * q + 1] = v.y; xs[i][4 * q + 2] = v.z; xs[i][4 * q + 3] = v.w;
+        }
+    }
+    uint4 raw[GEMV_RPW][NL];
+#pragma unroll
+    for (int rr = 0; rr < GEMV_RPW; ++rr) {
+        const int row = row0 + rr;
+        const int g = row < n ? 0 : 1;
+        const char* wr = static_cast<const char*>(sets.s[g].w) + (size_t)(row - g * n) * k * (INT8 ? 1 : 2);
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int c = lane * E + i * 64 * E;
+            raw[rr][i] = (row < rows && c < k) ? *reinterpret_cast<const uint4*>(wr + c * (INT8 ? 1 : 2))
+                                               : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+#pragma unroll
+    for (int rr = 0; rr < GEMV_RPW; ++rr) {
         float acc = 0.f;
-        if (INT8) {
-            const int8_t* wr = static_cast<const int8_t*>(w) + (size_t)row * k;
-            for (int c = lane * EPL; c < k; c += 64 * EPL) {
-                const int4 raw = *reinterpret_cast<const int4*>(wr + c);
-                const int8_t* e = reinterpret_cast<const int8_t*>(&raw);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) acc += (float)e[i] * xs[c + i];
-            }
-        } else {
-            const uint16_t* wr = static_cast<const uint16_t*>(w) + (size_t)row * k;
-            for (int c = lane * EPL; c < k; c += 64 * EPL) {
-                const uint4 raw = *reinterpret_cast<const uint4*>(wr + c);
-                const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw);
+        for (int i = 0; i < NL; ++i) {
+            if (INT8) {
+                const int8_t* e = reinterpret_cast<const int8_t*>(&raw[rr][i]);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc += (WT == MMDIT_F16 ? h2f(e[i]) : bf2f(e[i])) * xs[c + i];
+                for (int j = 0; j < 16; ++j) acc += (float)e[j] * xs[i][j];
+            } else {
+                const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw[rr][i]);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc += (WT == MMDIT_F16 ? h2f(e[j]) : bf2f(e[j])) * xs[i][j];
             }
         }
         acc = wave_sum(acc);
-        if (lane == 0) {
-            float y = (INT8 ? acc * scale[row] : acc) + bf2f(bias[row]);
-            out[row] = accumulate ? out[row] + y : y;
+        const int row = row0 + rr;
+        if (lane == 0 && row < rows) {
+            const int g = row < n ? 0 : 1, r = row - g * n;
+            const GemvSet& st = sets.s[g];
+            const float y = (INT8 ? acc * st.scale[r] : acc) + bf2f(st.bias[r]);
+            st.out[r] = accumulate ? st.out[r] + y : y;
         }
     }
 }
 
-hipError_t launch_gemv(const float* x, int k, const void* w, const float* scale,
-                       const uint16_t* bias, int n, int wtype, int silu_input, int accumulate,
-                       float* out, hipStream_t s) {
-    int blocks = (n + 3) / 4;
-    if (blocks > 2048) blocks = 2048;
-    const size_t lds = (size_t)k * sizeof(float);
-#define GEMV_CASE(T)                                                                               \
-    case T:                                                                                        \
-        hipLaunchKernelGGL(gemv_kernel<T>, dim3(blocks), dim3(256), lds, s, x, k, w, scale, bias, n, \
-                           silu_input, accumulate, out);                                           \
-        break;
-    switch (wtype) {
-        GEMV_CASE(MMDIT_BF16) GEMV_CASE(MMDIT_INT8) GEMV_CASE(MMDIT_F16)
-        default: return hipErrorInvalidValue;
+hipError_t launch_gemv(const float* x, int k, int n, int wtype, int silu_input, int accumulate,
+                       const GemvSets& sets, hipStream_t s) {
+    if (n <= 0 || sets.count < 1) return hipSuccess;
+    const int E = wtype == MMDIT_INT8 ? 16 : 8;
+    const int nl = (k + 64 * E - 1) / (64 * E);
+    const int waves = (sets.count * n + GEMV_RPW - 1) / GEMV_RPW;
+    const dim3 grid((waves + 3) / 4), block(256);
+#define GEMV_CASE(T, L)                                                                                  \
+    if (wtype == T && nl == L) {                                                                         \
+        hipLaunchKernelGGL((gemv_kernel<T, L>), grid, block, 0, s, x, k, n, silu_input, accumulate, sets); \
+        return hipGetLastError();                                                                        \
     }
+    GEMV_CASE(MMDIT_BF16, 1) GEMV_CASE(MMDIT_BF16, 2) GEMV_CASE(MMDIT_BF16, 3) GEMV_CASE(MMDIT_BF16, 4)
+    GEMV_CASE(MMDIT_BF16, 5) GEMV_CASE(MMDIT_BF16, 6) GEMV_CASE(MMDIT_BF16, 7) GEMV_CASE(MMDIT_BF16, 8)
+    GEMV_CASE(MMDIT_F16, 1) GEMV_CASE(MMDIT_F16, 2) GEMV_CASE(MMDIT_F16, 3) GEMV_CASE(MMDIT_F16, 4)
+    GEMV_CASE(MMDIT_F16, 5) GEMV_CASE(MMDIT_F16, 6) GEMV_CASE(MMDIT_F16, 7) GEMV_CASE(MMDIT_F16, 8)
+    GEMV_CASE(MMDIT_INT8, 1) GEMV_CASE(MMDIT_INT8, 2) GEMV_CASE(MMDIT_INT8, 3) GEMV_CASE(MMDIT_INT8, 4)
 #undef GEMV_CASE
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------------------

@@ -339,7 +339,8 @@ int mmdit_k_gemm(const mmdit_gemm* g, hipStream_t stream);
 
 /*
  * out[n] (+)= W act(x) + b for one vector (modulation and embedder layers):
- *   x fp32 [k]; act = SiLU if silu_input else identity; W [n, k] bf16 or int8;
+ *   x fp32 [k], k a multiple of 64 and <= 4096; act = SiLU if silu_input else
+ *   identity; W [n, k] bf16, fp16 or int8 (weight_dtype);
  *   accumulate: 0 writes out, 1 adds to it. out fp32 [n].
  */
 int mmdit_k_gemv(const float* x, int k, const mmdit_linear* w, int n, int weight_dtype,

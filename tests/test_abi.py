@@ -122,6 +122,7 @@ def test_kernel_entry_validation():
     lin = _linear()
     assert B.mmdit_k_gemv(FAKE, 100, lin, 10, 0, 1, 0, FAKE) == B.MMDIT_E_SHAPE
     assert B.mmdit_k_gemv(FAKE, 128, lin, 10, 3, 1, 0, FAKE) == B.MMDIT_E_DTYPE
+    assert B.mmdit_k_gemv(FAKE, 4160, lin, 10, 0, 1, 0, FAKE) == B.MMDIT_E_SHAPE  # k > 4096
     assert B.mmdit_k_euler(FAKE + 8, FAKE, 10, 0.1) == B.MMDIT_E_ALIGN
 
 

@@ -347,7 +347,8 @@ def test_weights_to_f16_exhaustive():
 @pytest.mark.parametrize("n,k,wt,silu_in,acc", [(1536, 256, "bf16", 1, 0), (18432, 3072, "bf16", 1, 0),
                                                 (18432, 3072, "int8", 1, 0), (3072, 256, "int8", 0, 1),
                                                 (100, 64, "bf16", 0, 1), (18432, 3072, "f16", 1, 0),
-                                                (100, 64, "f16", 0, 1)])
+                                                (100, 64, "f16", 0, 1), (101, 4096, "bf16", 1, 0),
+                                                (7, 1024, "int8", 1, 1), (9, 4096, "int8", 0, 0)])
 def test_gemv(n, k, wt, silu_in, acc):
     say(f"gemv n={n} k={k} weights={wt}")
     int8, f16 = wt == "int8", wt == "f16"
