@@ -102,33 +102,39 @@ struct TileCoord {
 };
 
 // Workgroup -> output tile. Workgroups are dispatched round-robin over the
-// 8 XCDs (workgroup b runs on XCD b % 8), and each XCD has its own L2. Each
-// XCD is therefore given one contiguous run of the tile list, and the list
-// walks the tiles of a group in bands of RASTER_ROWS tile rows, column by
-// column: the ~32 tiles an XCD runs at once then form a compact block that
-// shares A rows and W rows in its L2 (instead of ~6 rows and ~6 columns
-// spread over the whole output, or 18 rows x 3 columns for N = 3072).
+// 8 XCDs (workgroup b runs on XCD b % 8) and each XCD has its own L2, so each
+// XCD is given one contiguous run of a tile order in which such runs are
+// compact rectangles: the tile grid (the row tiles of both groups stacked,
+// text rows first) is cut into CS column strips (8, 4 or 2 when the column
+// count divides evenly, else 1), each strip walked in bands of RASTER_ROWS
+// tile rows, column by column. An XCD then holds e.g. all 18 row tiles x 6
+// columns of the MLP-in projection, or 9 rows x 9 columns of QKV, and its
+// ~32 concurrent tiles share A and W rows in its L2. Both weight groups share
+// the strips, so no XCD streams a whole text-stream weight matrix alone.
 constexpr int RASTER_ROWS = 6;
 
 MMDIT_DEV TileCoord tile_of(const GemmArgs& a, int bid, int total) {
     const int x = bid & 7, j = bid >> 3, q = total >> 3, r = total & 7;
-    int idx = x * q + (x < r ? x : r) + j;   // a bijection on [0, total)
+    const int idx = x * q + (x < r ? x : r) + j;   // a bijection on [0, total)
     const int tn = (a.n + BN - 1) / BN;
     const int tm0 = (a.g[0].m + BM - 1) / BM;
+    const int tmt = a.ngroups == 2 ? tm0 + (a.g[1].m + BM - 1) / BM : tm0;
+    const int cs = (tn % 8 == 0) ? 8 : (tn % 4 == 0) ? 4 : (tn % 2 == 0) ? 2 : 1;
+    const int cols = tn / cs;
+    const int strip = idx / (tmt * cols), in_strip = idx - strip * tmt * cols;
+    const int band = in_strip / (RASTER_ROWS * cols), rem = in_strip - band * RASTER_ROWS * cols;
+    const int r0 = band * RASTER_ROWS;
+    const int rows = (tmt - r0) < RASTER_ROWS ? (tmt - r0) : RASTER_ROWS;
+    int mt = r0 + rem % rows;
     TileCoord c;
-    int tm = tm0;
-    if (a.ngroups == 1 || idx < tm0 * tn) {
+    c.n0 = (strip * cols + rem / rows) * BN;
+    if (a.ngroups == 1 || mt < tm0) {
         c.g = 0;
     } else {
         c.g = 1;
-        idx -= tm0 * tn;
-        tm = (a.g[1].m + BM - 1) / BM;
+        mt -= tm0;
     }
-    const int band = idx / (RASTER_ROWS * tn), rem = idx - band * RASTER_ROWS * tn;
-    const int r0 = band * RASTER_ROWS;
-    const int rows = (tm - r0) < RASTER_ROWS ? (tm - r0) : RASTER_ROWS;
-    c.m0 = (r0 + rem % rows) * BM;
-    c.n0 = (rem / rows) * BN;
+    c.m0 = mt * BM;
     return c;
 }
 
