@@ -24,6 +24,7 @@ def rnd(tid, shape, std=1.0, cid=CID):
 
 # ------------------------------------------------------------------ LN + modulate
 @pytest.mark.parametrize("rows,hidden,split", [(320, 256, 64), (7, 64, 3), (1000, 3072, 512), (4608, 3072, 512),
+                                               (9, 960, 4), (257, 1536, 100), (5, 2048, 2),
                                                (33, 4096, 40)])
 def test_ln_modulate(rows, hidden, split):
     say(f"ln_modulate rows={rows} hidden={hidden} split={split}")
