@@ -34,13 +34,14 @@ except ImportError:  # a process without PyTorch uses the system runtime
 lib = ctypes.CDLL(LIB_PATH)
 
 # ---------------------------------------------------------------- constants
-MMDIT_ABI_VERSION = 2
+MMDIT_ABI_VERSION = 3
 MMDIT_OK, MMDIT_E_NULL, MMDIT_E_ALIGN, MMDIT_E_SHAPE = 0, 1, 2, 3
 MMDIT_E_DTYPE, MMDIT_E_WORKSPACE, MMDIT_E_HIP, MMDIT_E_ARG = 4, 5, 6, 7
 MMDIT_BF16, MMDIT_INT8, MMDIT_F16 = 0, 1, 2
 MMDIT_WS_DOUBLE, MMDIT_WS_SINGLE, MMDIT_WS_STEP = 0, 1, 2
 (MMDIT_EPI_BIAS, MMDIT_EPI_BIAS_GELU, MMDIT_EPI_GATE_RESID, MMDIT_EPI_SPLIT_GELU,
- MMDIT_EPI_BIAS_F32, MMDIT_EPI_EULER) = range(6)
+ MMDIT_EPI_BIAS_F32, MMDIT_EPI_EULER, MMDIT_EPI_SWIGLU, MMDIT_EPI_SPLIT_SWIGLU) = range(8)
+MMDIT_ACT_GELU_TANH, MMDIT_ACT_SWIGLU = 0, 1
 
 
 # ---------------------------------------------------------------- structs
@@ -49,7 +50,8 @@ class mmdit_dims(Structure):
                 ("head_dim", c_int32), ("mlp_hidden", c_int32), ("in_channels", c_int32),
                 ("rope_axes", c_int32 * 3), ("rope_theta", c_float), ("ln_eps", c_float),
                 ("rms_eps", c_float), ("weight_dtype", c_int32), ("n_double", c_int32),
-                ("n_single", c_int32)]
+                ("n_single", c_int32), ("mlp_act", c_int32), ("guidance_embed", c_int32),
+                ("ref_len", c_int32)]
 
 
 class mmdit_linear(Structure):

@@ -33,7 +33,19 @@ int check_dims(const mmdit_dims* d) {
     if (sum != d->head_dim) return MMDIT_E_SHAPE;
     if (!(d->ln_eps > 0.f) || !(d->rms_eps > 0.f) || !(d->rope_theta > 1.f)) return MMDIT_E_SHAPE;
     if (!dtype_ok(d->weight_dtype)) return MMDIT_E_DTYPE;
+    if (d->mlp_act != MMDIT_ACT_GELU_TANH && d->mlp_act != MMDIT_ACT_SWIGLU) return MMDIT_E_ARG;
+    // SwiGLU GEMM tiles hold 128 features and never straddle the q|k|v / MLP
+    // split of the single-stream linear1 (at 3H)
+    if (d->mlp_act == MMDIT_ACT_SWIGLU && (d->hidden % 256 != 0 || d->mlp_hidden % 128 != 0))
+        return MMDIT_E_SHAPE;
+    if (d->guidance_embed != 0 && d->guidance_embed != 1) return MMDIT_E_ARG;
+    if (d->ref_len < 0 || d->ref_len >= d->img_len) return MMDIT_E_SHAPE;
     return MMDIT_OK;
+}
+
+// fc1 / MLP-part output columns of linear1: M (GELU) or [gate | up] = 2M (SwiGLU)
+int mlp_cols(const mmdit_dims* d) {
+    return d->mlp_act == MMDIT_ACT_SWIGLU ? 2 * d->mlp_hidden : d->mlp_hidden;
 }
 
 int check_ptr(const void* p) {
@@ -289,9 +301,12 @@ int run_double(const mmdit_dims* d, const mmdit_double_weights* w, const float* 
     // a7: LN2 + modulate
     MMDIT_HIP(launch_ln_modulate(x_out, L, H, Lt, mt + 3 * H, mt + 4 * H, mi + 3 * H, mi + 4 * H,
                                  d->ln_eps, ws.h, s));
-    // a8: fc1 + GELU
-    MMDIT_HIP(gemm_2(gemm_base(M, H, dt, ws.h, H, MMDIT_EPI_BIAS_GELU, ws.a, M),
-                     group(0, Lt, w->txt.fc1), group(Lt, Li, w->img.fc1), s));
+    // a8: fc1 + GELU (or SwiGLU: fc1 rows [gate | up], hidden = SiLU(gate) * up)
+    {
+        const int epi = d->mlp_act == MMDIT_ACT_SWIGLU ? MMDIT_EPI_SWIGLU : MMDIT_EPI_BIAS_GELU;
+        MMDIT_HIP(gemm_2(gemm_base(mlp_cols(d), H, dt, ws.h, H, epi, ws.a, M),
+                         group(0, Lt, w->txt.fc1), group(Lt, Li, w->img.fc1), s));
+    }
     // a9: fc2 + gated residual
     {
         GemmArgs g = gemm_base(H, M, dt, ws.a, M, MMDIT_EPI_GATE_RESID, x_out, H);
@@ -310,7 +325,8 @@ int run_single(const mmdit_dims* d, const mmdit_single_weights* w, const float* 
     MMDIT_HIP(gemv(vec, H, w->mod, 3 * H, dt, 1, 0, m, s));
     MMDIT_HIP(launch_ln_modulate(x_in, L, H, 0, m, m + H, m, m + H, d->ln_eps, ws.h, s));
     {
-        GemmArgs g = gemm_base(3 * H + M, H, dt, ws.h, H, MMDIT_EPI_SPLIT_GELU, ws.qkv, 3 * H);
+        const int epi = d->mlp_act == MMDIT_ACT_SWIGLU ? MMDIT_EPI_SPLIT_SWIGLU : MMDIT_EPI_SPLIT_GELU;
+        GemmArgs g = gemm_base(3 * H + mlp_cols(d), H, dt, ws.h, H, epi, ws.qkv, 3 * H);
         g.split_n = 3 * H;
         g.out2 = ws.cat;
         g.ldo2 = H + M;
@@ -334,9 +350,11 @@ int run_time_embed(const mmdit_dims* d, const mmdit_model* m, float t, float gui
     const int H = d->hidden, dt = d->weight_dtype;
     MMDIT_HIP(launch_time_and_guidance_embedding(t, guidance, emb, s));
     MMDIT_HIP(gemv(emb, 256, m->time_in[0], H, dt, 0, 0, tmp, s));
-    MMDIT_HIP(gemv(emb + 256, 256, m->guid_in[0], H, dt, 0, 0, tmp + H, s));
     MMDIT_HIP(gemv(tmp, H, m->time_in[1], H, dt, 1, 0, vec, s));
-    MMDIT_HIP(gemv(tmp + H, H, m->guid_in[1], H, dt, 1, 1, vec, s));
+    if (d->guidance_embed) {
+        MMDIT_HIP(gemv(emb + 256, 256, m->guid_in[0], H, dt, 0, 0, tmp + H, s));
+        MMDIT_HIP(gemv(tmp + H, H, m->guid_in[1], H, dt, 1, 1, vec, s));
+    }
     return MMDIT_OK;
 }
 
@@ -414,7 +432,7 @@ int mmdit_denoise_step(const mmdit_dims* d, const mmdit_model* m, float* latent,
     MMDIT_TRY(check_linear(m->img_in, dt));
     for (int i = 0; i < 2; ++i) {
         MMDIT_TRY(check_linear(m->time_in[i], dt));
-        MMDIT_TRY(check_linear(m->guid_in[i], dt));
+        if (d->guidance_embed) MMDIT_TRY(check_linear(m->guid_in[i], dt));
     }
     MMDIT_TRY(check_linear(m->final_mod, dt));
     MMDIT_TRY(check_linear(m->final_out, dt));
@@ -432,8 +450,9 @@ int mmdit_denoise_step(const mmdit_dims* d, const mmdit_model* m, float* latent,
     if (ws_bytes < c.off) return MMDIT_E_WORKSPACE;
 
     const int Lt = d->txt_len, Li = d->img_len, L = Lt + Li, H = d->hidden, C = d->in_channels;
+    const int Ln = Li - d->ref_len;   // noisy image rows; the rest is the reference latent
     MMDIT_TRY(run_time_embed(d, m, t_cur, guidance, sw.vec, sw.emb, sw.tmp, s));
-    // x = [txt | img_in(latent)]
+    // x = [txt | img_in(latent)] (reference rows included)
     MMDIT_HIP(launch_copy_f32(sw.x, txt, (int64_t)Lt * H, s));
     {
         const int64_t n = (int64_t)Li * C;
@@ -452,14 +471,14 @@ int mmdit_denoise_step(const mmdit_dims* d, const mmdit_model* m, float* latent,
         MMDIT_TRY(run_double(d, &m->doubles[i], sw.vec, rope, sw.x, sw.x, dws, s));
     for (int i = 0; i < d->n_single; ++i)
         MMDIT_TRY(run_single(d, &m->singles[i], sw.vec, rope, sw.x, sw.x, sws, s));
-    // final layer on the image rows, fused with the Euler update
+    // final layer on the noisy image rows, fused with the Euler update
     MMDIT_HIP(gemv(sw.vec, H, m->final_mod, 2 * H, dt, 1, 0, sw.fmod, s));
-    MMDIT_HIP(launch_ln_modulate(sw.x + (size_t)Lt * H, Li, H, 0, sw.fmod, sw.fmod + H, sw.fmod,
+    MMDIT_HIP(launch_ln_modulate(sw.x + (size_t)Lt * H, Ln, H, 0, sw.fmod, sw.fmod + H, sw.fmod,
                                  sw.fmod + H, d->ln_eps, dws.h, s));
     {
         GemmArgs g = gemm_base(C, H, dt, dws.h, H, MMDIT_EPI_EULER, latent, C);
         g.alpha = t_next - t_cur;
-        MMDIT_HIP(gemm_1(g, group(0, Li, m->final_out), s));
+        MMDIT_HIP(gemm_1(g, group(0, Ln, m->final_out), s));
     }
     (void)L;
     return MMDIT_OK;
@@ -529,24 +548,28 @@ int mmdit_k_gemm(const mmdit_gemm* g, hipStream_t s) {
     if (g->m < 1 || g->n < 64 || g->n % 64 != 0 || g->k < 64 || g->k % 64 != 0) return MMDIT_E_SHAPE;
     if (g->lda < g->k || g->lda % 8 != 0) return MMDIT_E_SHAPE;
     if (!dtype_ok(g->weight_dtype)) return MMDIT_E_DTYPE;
-    if (g->epilogue < MMDIT_EPI_BIAS || g->epilogue > MMDIT_EPI_EULER) return MMDIT_E_ARG;
+    if (g->epilogue < MMDIT_EPI_BIAS || g->epilogue > MMDIT_EPI_SPLIT_SWIGLU) return MMDIT_E_ARG;
     MMDIT_TRY(check_ptr(g->a));
     MMDIT_TRY(check_linear(g->w, g->weight_dtype));
     MMDIT_TRY(check_ptr(g->out));
     const bool f32out = g->epilogue == MMDIT_EPI_GATE_RESID || g->epilogue == MMDIT_EPI_BIAS_F32 ||
                         g->epilogue == MMDIT_EPI_EULER;
-    const int ncols = g->epilogue == MMDIT_EPI_SPLIT_GELU ? g->split_n : g->n;
+    const bool split = g->epilogue == MMDIT_EPI_SPLIT_GELU || g->epilogue == MMDIT_EPI_SPLIT_SWIGLU;
+    const int ncols = split ? g->split_n : g->epilogue == MMDIT_EPI_SWIGLU ? g->n / 2 : g->n;
     if (g->ldo < ncols || g->ldo % (f32out ? 4 : 8) != 0) return MMDIT_E_SHAPE;
     if (g->epilogue == MMDIT_EPI_GATE_RESID) {
         MMDIT_TRY(check_ptr(g->gate));
         MMDIT_TRY(check_ptr(g->resid));
         if (g->ldr < g->n || g->ldr % 4 != 0) return MMDIT_E_SHAPE;
     }
-    if (g->epilogue == MMDIT_EPI_SPLIT_GELU) {
-        if (g->split_n < 0 || g->split_n > g->n || g->split_n % 64 != 0) return MMDIT_E_SHAPE;
+    if (g->epilogue == MMDIT_EPI_SWIGLU && g->n % 256 != 0) return MMDIT_E_SHAPE;
+    if (split) {
+        const int q = g->epilogue == MMDIT_EPI_SPLIT_SWIGLU ? 256 : 64;   // SwiGLU tiles never straddle
+        if (g->split_n < 0 || g->split_n > g->n || g->split_n % q != 0 || (g->n - g->split_n) % q != 0)
+            return MMDIT_E_SHAPE;
+        const int n2 = g->epilogue == MMDIT_EPI_SPLIT_SWIGLU ? (g->n - g->split_n) / 2 : g->n - g->split_n;
         MMDIT_TRY(check_ptr(g->out2));
-        if (g->out2_col < 0 || g->out2_col % 8 != 0 || g->ldo2 % 8 != 0 ||
-            g->ldo2 < g->out2_col + (g->n - g->split_n))
+        if (g->out2_col < 0 || g->out2_col % 8 != 0 || g->ldo2 % 8 != 0 || g->ldo2 < g->out2_col + n2)
             return MMDIT_E_SHAPE;
     }
     GemmArgs a = gemm_base(g->n, g->k, g->weight_dtype, g->a, g->lda, g->epilogue, g->out, g->ldo);
@@ -579,7 +602,7 @@ int mmdit_k_time_embed(const mmdit_dims* d, const mmdit_model* m, float t, float
     if (!m) return MMDIT_E_NULL;
     for (int i = 0; i < 2; ++i) {
         MMDIT_TRY(check_linear(m->time_in[i], d->weight_dtype));
-        MMDIT_TRY(check_linear(m->guid_in[i], d->weight_dtype));
+        if (d->guidance_embed) MMDIT_TRY(check_linear(m->guid_in[i], d->weight_dtype));
     }
     MMDIT_TRY(check_ptr(vec));
     MMDIT_TRY(check_ptr(ws));

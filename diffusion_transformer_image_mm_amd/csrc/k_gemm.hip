@@ -40,6 +40,13 @@
 //   registers before the next stage's loads are issued;
 // * grouped launch: up to two weight sets (text / image stream) over
 //   disjoint row ranges in one grid; tiles are laid out per XCD (tile_of);
+// * SwiGLU epilogues (a gated MLP, Luminal blog section "What the compiler
+//   found on its own": the fused SwiGLU activation of Flux.2 Klein): the
+//   weight keeps its natural layout, rows [gate (M) | up (M)]. A tile covers
+//   128 features: tile row r loads gate row f or up row M + f of feature
+//   f = 32 * (r / 64) + r % 32 (up when bit 5 of r is set), so each wavefront
+//   holds gate and up of the same 32 features and the epilogue pairs its
+//   accumulators in registers;
 // * M and N tails: loads clamp to the last valid row, stores are guarded;
 // * deterministic (no atomics, fixed k order).
 #include "common.h"
@@ -138,6 +145,17 @@ MMDIT_DEV TileCoord tile_of(const GemmArgs& a, int bid, int total) {
     return c;
 }
 
+// Weight row loaded into tile row position v = n0 + r (a column of the
+// product's output). Plain epilogues: row v. SwiGLU columns (v >= swiglu_from,
+// a multiple of 256): 128 features per tile, gate and up rows interleaved in
+// runs of 32 (see the header).
+MMDIT_DEV int weight_row(int v, int swiglu_from, int half) {
+    if (v < swiglu_from) return v;
+    const int u = v - swiglu_from;
+    const int f = ((u >> 6) << 5) + (u & 31);
+    return swiglu_from + ((u & 32) ? half : 0) + f;
+}
+
 }  // namespace
 
 template <int WT, int EPI>
@@ -156,6 +174,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;
+    constexpr bool SWIGLU = EPI == MMDIT_EPI_SWIGLU || EPI == MMDIT_EPI_SPLIT_SWIGLU;
+    // SwiGLU columns start at sw_from (0, or split_n for the split epilogue);
+    // sw_half = M, the number of features
+    const int sw_from = EPI == MMDIT_EPI_SPLIT_SWIGLU ? args.split_n : 0;
+    const int sw_half = (N - sw_from) >> 1;
 
     // ---- load descriptors: a uniform base plus a 32-bit per-lane byte
     // offset (so the loads use the scalar-base addressing form). A tile:
@@ -185,6 +208,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) 
             const int c = lpos ^ ((r >> 1) & 7);
             int gn = tc.n0 + r;
             gn = gn < N ? gn : N - 1;
+            if (SWIGLU) gn = weight_row(gn, sw_from, sw_half);
             w_off_g[j] = (uint32_t)gn * (uint32_t)K * 2u + (uint32_t)c * 16u;
         }
     } else {
@@ -194,6 +218,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) 
             const int u = (lane & 3) ^ ((r >> 2) & 3);
             int gn = tc.n0 + r;
             gn = gn < N ? gn : N - 1;
+            if (SWIGLU) gn = weight_row(gn, sw_from, sw_half);
             w_off_g[j] = (uint32_t)gn * (uint32_t)K + (uint32_t)u * 16u;
         }
     }
@@ -281,6 +306,45 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) 
     // n = n0 + wn*64 + in*16 + lg*4 + j, row m = m0 + wm*128 + im*16 + lr.
     const int nb = tc.n0 + wn * 64 + lg * 4;
     const int mb = tc.m0 + wm * 128 + lr;
+    if (SWIGLU && tc.n0 >= sw_from) {
+        // accumulators in = 0, 1 hold gate, in = 2, 3 up of the same features
+        // f = (n0 - sw_from) / 2 + 32 wn + 16 in + 4 lg + j: out fp16 = SiLU(gate) * up
+        const int fb = ((tc.n0 - sw_from) >> 1) + wn * 32 + lg * 4;
+        uint16_t* obase = static_cast<uint16_t*>(EPI == MMDIT_EPI_SPLIT_SWIGLU ? args.out2 : args.out);
+        const int ld = EPI == MMDIT_EPI_SPLIT_SWIGLU ? args.ldo2 : args.ldo;
+        const int ocol = EPI == MMDIT_EPI_SPLIT_SWIGLU ? args.out2_col : 0;
+#pragma unroll
+        for (int in = 0; in < 2; ++in) {
+            const int f = fb + in * 16;
+            const int ng = sw_from + f, nu = sw_from + sw_half + f;
+            const uint2 bg = *reinterpret_cast<const uint2*>(G.bias + ng);
+            const uint2 bu = *reinterpret_cast<const uint2*>(G.bias + nu);
+            const float b_g[4] = {bf2f(bg.x & 0xffff), bf2f(bg.x >> 16), bf2f(bg.y & 0xffff), bf2f(bg.y >> 16)};
+            const float b_u[4] = {bf2f(bu.x & 0xffff), bf2f(bu.x >> 16), bf2f(bu.y & 0xffff), bf2f(bu.y >> 16)};
+            float s_g[4] = {1.f, 1.f, 1.f, 1.f}, s_u[4] = {1.f, 1.f, 1.f, 1.f};
+            if (INT8) {
+                const float4 a4 = *reinterpret_cast<const float4*>(G.scale + ng);
+                const float4 c4 = *reinterpret_cast<const float4*>(G.scale + nu);
+                s_g[0] = a4.x; s_g[1] = a4.y; s_g[2] = a4.z; s_g[3] = a4.w;
+                s_u[0] = c4.x; s_u[1] = c4.y; s_u[2] = c4.z; s_u[3] = c4.w;
+            }
+#pragma unroll
+            for (int im = 0; im < TM; ++im) {
+                const int m = mb + im * 16;
+                if (m >= M) continue;
+                float y[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float g = acc[in][im][j] * s_g[j] + b_g[j];
+                    const float u = acc[in + 2][im][j] * s_u[j] + b_u[j];
+                    y[j] = silu(g) * u;
+                }
+                uint16_t* o = obase + (size_t)(G.row0 + m) * ld + ocol + f;
+                *reinterpret_cast<uint2*>(o) = make_uint2(pack2h(y[0], y[1]), pack2h(y[2], y[3]));
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int in = 0; in < TN; ++in) {
         const int n = nb + in * 16;
@@ -306,7 +370,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) 
             float y[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) y[j] = acc[in][im][j] * sc[j] + b[j];
-            if (EPI == MMDIT_EPI_BIAS || (EPI == MMDIT_EPI_SPLIT_GELU && n < args.split_n)) {
+            if (EPI == MMDIT_EPI_BIAS || EPI == MMDIT_EPI_SPLIT_SWIGLU ||
+                (EPI == MMDIT_EPI_SPLIT_GELU && n < args.split_n)) {
                 // attention-side operands (q, k, v): bf16
                 uint16_t* o = static_cast<uint16_t*>(args.out) + grow * args.ldo + n;
                 *reinterpret_cast<uint2*>(o) = make_uint2(pack2bf(y[0], y[1]), pack2bf(y[2], y[3]));
@@ -371,6 +436,8 @@ static hipError_t launch_gemm_t(const GemmArgs& a, hipStream_t s) {
         GEMM_CASE(MMDIT_EPI_SPLIT_GELU)
         GEMM_CASE(MMDIT_EPI_BIAS_F32)
         GEMM_CASE(MMDIT_EPI_EULER)
+        GEMM_CASE(MMDIT_EPI_SWIGLU)
+        GEMM_CASE(MMDIT_EPI_SPLIT_SWIGLU)
         default:
             return hipErrorInvalidValue;
     }

@@ -96,8 +96,9 @@ class DeviceArena:
         mm.img_in = self.linear(m["img_in"])
         mm.time_in[0] = self.linear(m["time_in"][0])
         mm.time_in[1] = self.linear(m["time_in"][1])
-        mm.guid_in[0] = self.linear(m["guid_in"][0])
-        mm.guid_in[1] = self.linear(m["guid_in"][1])
+        if m.get("guid_in") is not None:
+            mm.guid_in[0] = self.linear(m["guid_in"][0])
+            mm.guid_in[1] = self.linear(m["guid_in"][1])
         mm.final_mod = self.linear(m["final_mod"])
         mm.final_out = self.linear(m["final_out"])
         mm.doubles = doubles
@@ -132,21 +133,33 @@ class TimingModel:
         self.f16 = f16 and not int8
         self.keep: List[torch.Tensor] = []
         H, M, C, D = shp.hidden, shp.mlp, shp.in_channels, shp.head_dim
+        MO = shp.mlp_out
         mk = self._linear
         norm = self._norm
+        shared = {}
 
-        def stream_w():
-            return B.mmdit_stream_weights(mk(6 * H, H), mk(3 * H, H), mk(H, H), mk(M, H), mk(H, M), norm(D), norm(D))
+        def mod(key, n):
+            # one modulation linear per block type when the shape shares them
+            if not shp.shared_mod:
+                return mk(n, H)
+            if key not in shared:
+                shared[key] = mk(n, H)
+            return shared[key]
+
+        def stream_w(key):
+            return B.mmdit_stream_weights(mod(key, 6 * H), mk(3 * H, H), mk(H, H), mk(MO, H), mk(H, M), norm(D),
+                                          norm(D))
 
         self.doubles = (B.mmdit_double_weights * max(shp.n_double, 1))(
-            *[B.mmdit_double_weights(stream_w(), stream_w()) for _ in range(shp.n_double)])
+            *[B.mmdit_double_weights(stream_w("txt"), stream_w("img")) for _ in range(shp.n_double)])
         self.singles = (B.mmdit_single_weights * max(shp.n_single, 1))(
-            *[B.mmdit_single_weights(mk(3 * H, H), mk(3 * H + M, H), mk(H, H + M), norm(D), norm(D))
+            *[B.mmdit_single_weights(mod("single", 3 * H), mk(3 * H + MO, H), mk(H, H + M), norm(D), norm(D))
               for _ in range(shp.n_single)])
         m = B.mmdit_model()
         m.img_in = mk(H, C)
         m.time_in[0], m.time_in[1] = mk(H, 256), mk(H, H)
-        m.guid_in[0], m.guid_in[1] = mk(H, 256), mk(H, H)
+        if shp.guidance_embed:
+            m.guid_in[0], m.guid_in[1] = mk(H, 256), mk(H, H)
         m.final_mod = mk(2 * H, H)
         m.final_out = mk(C, H)
         m.doubles = self.doubles
@@ -181,6 +194,9 @@ def dims_for(shp: synth.Shape, int8: bool = False, f16: bool = False) -> B.mmdit
     d.rope_theta, d.ln_eps, d.rms_eps = shp.theta, shp.ln_eps, shp.rms_eps
     d.weight_dtype = B.MMDIT_INT8 if int8 else (B.MMDIT_F16 if f16 else B.MMDIT_BF16)
     d.n_double, d.n_single = shp.n_double, shp.n_single
+    d.mlp_act = B.MMDIT_ACT_SWIGLU if shp.mlp_act == "swiglu" else B.MMDIT_ACT_GELU_TANH
+    d.guidance_embed = 1 if shp.guidance_embed else 0
+    d.ref_len = shp.ref_len
     return d
 
 

@@ -60,10 +60,24 @@ class Shape:
     theta: float = 10000.0
     ln_eps: float = 1e-6
     rms_eps: float = 1e-6
+    mlp_act: str = "gelu"        # "gelu" (tanh form) or "swiglu" (fc1 rows [gate | up])
+    guidance_embed: bool = True  # False: guidance-free conditioning (step-distilled)
+    ref: bool = False            # image editing: a reference image of the same grid
+    shared_mod: bool = False     # one set of modulation weights per block type
+
+    @property
+    def ref_len(self) -> int:
+        return self.grid[0] * self.grid[1] if self.ref else 0
 
     @property
     def img_len(self) -> int:
-        return self.grid[0] * self.grid[1]
+        """Image-stream tokens: the output image, then the reference image."""
+        return self.grid[0] * self.grid[1] + self.ref_len
+
+    @property
+    def mlp_out(self) -> int:
+        """Output width of fc1 (and of linear1's MLP part)."""
+        return 2 * self.mlp if self.mlp_act == "swiglu" else self.mlp
 
     @property
     def seq_len(self) -> int:
@@ -87,7 +101,27 @@ QWEN_DOUBLE = Shape("qwen-double-h3072-L7145", 4, 3072, 24, 128, 12288, 256, (83
 FLUX_STEP = Shape("flux-dev-step-19d38s-int8", 5, 3072, 24, 128, 12288, 512, (64, 64), _axes_for(128),
                   n_double=19, n_single=38)
 
-SHAPES = {s.name: s for s in (TINY, FLUX_DOUBLE, FLUX_SINGLE, QWEN_DOUBLE, FLUX_STEP)}
+# Flux.2 Klein 9B-shaped (Luminal blog, "Flux.2 Klein 9B"): H 4096, 32 heads,
+# 8 double + 24 single blocks, SwiGLU MLP, 4 guidance-free steps, image-to-
+# image editing with a 512-token prompt; the latent is 1/16 of the image per
+# side with 128 channels, and the encoded input image (same size as the
+# output) is appended to the image stream. MLP width 3H and modulation
+# shared by the blocks of one type are readings (with them the parameter
+# count comes to ~9 B).
+KLEIN_KW = dict(mlp_act="swiglu", guidance_embed=False, ref=True, shared_mod=True, in_channels=128)
+KLEIN_TINY = Shape("klein-tiny-h256-L192", 6, 256, 4, 64, 768, 64, (8, 8), _axes_for(64), n_double=1,
+                   **KLEIN_KW)
+KLEIN_512 = Shape("klein-double-h4096-512x512-L2560", 7, 4096, 32, 128, 12288, 512, (32, 32), _axes_for(128),
+                  **KLEIN_KW)
+KLEIN_704x864 = Shape("klein-double-h4096-704x864-L5264", 8, 4096, 32, 128, 12288, 512, (54, 44),
+                      _axes_for(128), **KLEIN_KW)
+KLEIN_1200x800 = Shape("klein-double-h4096-1200x800-L8012", 9, 4096, 32, 128, 12288, 512, (50, 75),
+                       _axes_for(128), **KLEIN_KW)
+KLEIN_STEP_512 = Shape("klein-step-8d24s-512x512", 10, 4096, 32, 128, 12288, 512, (32, 32), _axes_for(128),
+                       n_double=8, n_single=24, **KLEIN_KW)
+
+SHAPES = {s.name: s for s in (TINY, FLUX_DOUBLE, FLUX_SINGLE, QWEN_DOUBLE, FLUX_STEP, KLEIN_TINY, KLEIN_512,
+                              KLEIN_704x864, KLEIN_1200x800, KLEIN_STEP_512)}
 
 
 def custom_shape(name: str, cid: int, hidden: int, heads: int, mlp: int, txt_len: int,
@@ -227,7 +261,7 @@ def stream_weights(cid: int, ids: _Ids, shp: Shape, int8: bool = False) -> Dict[
         "mod": make_linear(cid, ids, 6 * H, H, int8),
         "qkv": make_linear(cid, ids, 3 * H, H, int8),
         "proj": make_linear(cid, ids, H, H, int8),
-        "fc1": make_linear(cid, ids, M, H, int8),
+        "fc1": make_linear(cid, ids, shp.mlp_out, H, int8),
         "fc2": make_linear(cid, ids, H, M, int8),
         "q_norm": uniform(cid, ids(), (D,), 0.5, 1.5),
         "k_norm": uniform(cid, ids(), (D,), 0.5, 1.5),
@@ -242,7 +276,7 @@ def single_weights(cid: int, ids: _Ids, shp: Shape, int8: bool = False) -> Dict[
     H, M, D = shp.hidden, shp.mlp, shp.head_dim
     return {
         "mod": make_linear(cid, ids, 3 * H, H, int8),
-        "linear1": make_linear(cid, ids, 3 * H + M, H, int8),
+        "linear1": make_linear(cid, ids, 3 * H + shp.mlp_out, H, int8),
         "linear2": make_linear(cid, ids, H, H + M, int8),
         "q_norm": uniform(cid, ids(), (D,), 0.5, 1.5),
         "k_norm": uniform(cid, ids(), (D,), 0.5, 1.5),
@@ -250,12 +284,17 @@ def single_weights(cid: int, ids: _Ids, shp: Shape, int8: bool = False) -> Dict[
 
 
 def position_ids(shp: Shape) -> np.ndarray:
-    """int32 [L, 3] axial (t, h, w) ids: text at (0,0,0), image cell (r,c) at (0,r,c)."""
+    """int32 [L, 3] axial (t, h, w) ids: text at (0,0,0), image cell (r,c) at
+    (0,r,c); the cells of a reference image (editing) at (1,r,c)."""
     rows, cols = shp.grid
     ids = np.zeros((shp.seq_len, 3), dtype=np.int32)
     r, c = np.meshgrid(np.arange(rows, dtype=np.int32), np.arange(cols, dtype=np.int32), indexing="ij")
-    ids[shp.txt_len:, 1] = r.reshape(-1)
-    ids[shp.txt_len:, 2] = c.reshape(-1)
+    n = rows * cols
+    for k in range(2 if shp.ref else 1):
+        sl = slice(shp.txt_len + k * n, shp.txt_len + (k + 1) * n)
+        ids[sl, 0] = k
+        ids[sl, 1] = r.reshape(-1)
+        ids[sl, 2] = c.reshape(-1)
     return ids
 
 
@@ -286,17 +325,25 @@ def model_weights(shp: Shape, int8: bool = True, variant: int = 0) -> Dict[str, 
     m = {
         "img_in": make_linear(cid, ids, H, C, int8),
         "time_in": [make_linear(cid, ids, H, 256, int8), make_linear(cid, ids, H, H, int8)],
-        "guid_in": [make_linear(cid, ids, H, 256, int8), make_linear(cid, ids, H, H, int8)],
+        "guid_in": ([make_linear(cid, ids, H, 256, int8), make_linear(cid, ids, H, H, int8)]
+                    if shp.guidance_embed else None),
         "final_mod": make_linear(cid, ids, 2 * H, H, int8),
         "final_out": make_linear(cid, ids, C, H, int8),
         "double": [double_weights(cid, ids, shp, int8) for _ in range(shp.n_double)],
         "single": [single_weights(cid, ids, shp, int8) for _ in range(shp.n_single)],
     }
+    if shp.shared_mod:
+        # every block of a type uses the first block's modulation weights
+        for w in m["double"][1:]:
+            w["txt"]["mod"], w["img"]["mod"] = m["double"][0]["txt"]["mod"], m["double"][0]["img"]["mod"]
+        for w in m["single"][1:]:
+            w["mod"] = m["single"][0]["mod"]
     return m
 
 
 def step_inputs(shp: Shape, variant: int = 0) -> Dict[str, object]:
-    """Latent z0 [L_i, C] and text states [L_t, H] of a denoise step."""
+    """Latent z0 [L_i, C] (with the reference rows last when editing) and
+    text states [L_t, H] of a denoise step."""
     cid = shp.cid * 16 + variant
     ids = _Ids(90)
     z = normal(cid, ids(), (shp.img_len, shp.in_channels))

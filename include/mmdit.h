@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MMDIT_ABI_VERSION 2
+#define MMDIT_ABI_VERSION 3
 
 /* raw bfloat16 bits */
 typedef uint16_t mmdit_bf16;
@@ -106,7 +106,25 @@ typedef struct mmdit_dims {
     int32_t weight_dtype; /* enum mmdit_weight_dtype */
     int32_t n_double;
     int32_t n_single;
+    int32_t mlp_act;        /* enum mmdit_mlp_act */
+    int32_t guidance_embed; /* 1: vec = MLP_t(emb(t)) + MLP_g(emb(guidance)) (FLUX.1-dev);
+                               0: vec = MLP_t(emb(t)), guid_in unused (guidance-free,
+                               step-distilled Flux.2 Klein, "Flux.2 Klein 9B" section) */
+    int32_t ref_len;        /* image editing ("Flux.2 Klein 9B" section: the image-to-image
+                               pipeline): the last ref_len of the img_len image-stream
+                               tokens are the encoded reference image. They take part in
+                               every block; the denoise step reads them and updates only
+                               the first img_len - ref_len rows. 0 <= ref_len < img_len */
 } mmdit_dims;
+
+/* Activation of the MLP (double-stream fc1, single-stream linear1 MLP part) */
+enum mmdit_mlp_act {
+    MMDIT_ACT_GELU_TANH = 0, /* fc1 [M, H]; hidden = GELU_tanh(fc1(h)) */
+    MMDIT_ACT_SWIGLU = 1     /* fc1 [2M, H] rows [gate | up]; hidden = SiLU(gate) * up
+                                (Luminal blog, "What the compiler found on its own":
+                                the fused SwiGLU activation of Flux.2 Klein). Needs
+                                hidden % 256 == 0 and mlp_hidden % 128 == 0 */
+};
 
 /* ------------------------------------------------------------------ weights */
 /*
@@ -125,7 +143,7 @@ typedef struct mmdit_linear {
  * has its own projections, norm and feed-forward network).
  *   mod  [6H, H]: SiLU(vec) -> [shift1 | scale1 | gate1 | shift2 | scale2 | gate2]
  *   qkv  [3H, H]: columns [q | k | v], each head-major (column h*D + d)
- *   proj [H, H], fc1 [M, H], fc2 [H, M]
+ *   proj [H, H], fc1 [M, H] (SwiGLU: [2M, H], rows [gate | up]), fc2 [H, M]
  *   q_norm, k_norm: bf16 [D] RMSNorm scales of this stream
  */
 typedef struct mmdit_stream_weights {
@@ -142,7 +160,8 @@ typedef struct mmdit_double_weights {
  * Single-stream block: one set of weights over the joint sequence.
  *   mod     [3H, H]:   [shift | scale | gate]
  *   linear1 [3H+M, H]: columns [q | k | v | mlp]
- *   linear2 [H, H+M]:  input [attention | GELU(mlp)]
+ *           (SwiGLU: [3H+2M, H], columns [q | k | v | gate | up])
+ *   linear2 [H, H+M]:  input [attention | GELU(mlp)] (SwiGLU: [attention | SiLU(gate) * up])
  */
 typedef struct mmdit_single_weights {
     mmdit_linear mod, linear1, linear2;
@@ -152,7 +171,8 @@ typedef struct mmdit_single_weights {
 
 /*
  * A whole denoiser. img_in [H, C]; time_in / guid_in: Linear(256 -> H), SiLU,
- * Linear(H -> H) of the sinusoidal embedding; final_mod [2H, H] ->
+ * Linear(H -> H) of the sinusoidal embedding (guid_in is not read when
+ * dims->guidance_embed is 0); final_mod [2H, H] ->
  * [shift | scale]; final_out [C, H]. doubles / singles: HOST arrays of
  * n_double / n_single block weight structs.
  */
@@ -182,7 +202,7 @@ size_t mmdit_workspace_bytes(const mmdit_dims* dims, int kind);
  * LayerNorm + modulate, QKV projection, per-head RMSNorm of q and k; over the
  * joint sequence, axial RoPE and softmax attention without a mask; per
  * stream, output projection with gated residual, LayerNorm + modulate, GELU
- * MLP with gated residual.
+ * (or SwiGLU, dims->mlp_act) MLP with gated residual.
  *   vec:   fp32 [H] conditioning vector
  *   rope:  fp32 [L, D/2, 2] (cos, sin) per rotated pair (mmdit_rope_table)
  *   x_in:  fp32 [L, H] joint residual stream, text rows first
@@ -197,7 +217,8 @@ int mmdit_block_forward(const mmdit_dims* dims, const mmdit_double_weights* w,
 /*
  * Single-stream block forward: modulation, LayerNorm + modulate, linear1
  * (q|k|v|mlp), RMSNorm + RoPE on q and k, attention, linear2 over
- * [attention | GELU(mlp)], gated residual. Arguments as mmdit_block_forward.
+ * [attention | GELU(mlp)] (or [attention | SiLU(gate) * up]), gated residual.
+ * Arguments as mmdit_block_forward.
  */
 int mmdit_single_block_forward(const mmdit_dims* dims, const mmdit_single_weights* w,
                                const float* vec, const float* rope,
@@ -209,11 +230,14 @@ int mmdit_single_block_forward(const mmdit_dims* dims, const mmdit_single_weight
  * FLUX.1-dev, guidance 3.5; Luminal blog, "The AMD MI300X pipeline": the
  * latent is integrated in fp32):
  *   vec = MLP_t(emb(t_cur)) + MLP_g(emb(guidance)), emb = [cos | sin] of
- *   1000*t times 128 geometric frequencies (max period 1e4);
+ *   1000*t times 128 geometric frequencies (max period 1e4); without the
+ *   guidance term when dims->guidance_embed is 0 (guidance is then unused);
  *   x = [txt | img_in(latent)]; n_double double blocks; n_single single
- *   blocks; v = final_out(LayerNorm(x_img) * (1 + scale) + shift);
- *   latent += (t_next - t_cur) * v.
- *   latent: fp32 [img_len, in_channels], updated in place
+ *   blocks; v = final_out(LayerNorm(x_img) * (1 + scale) + shift) on the
+ *   first img_len - ref_len image rows; latent += (t_next - t_cur) * v there.
+ *   latent: fp32 [img_len, in_channels]; the first img_len - ref_len rows are
+ *           updated in place, the last ref_len rows (the reference image of
+ *           an edit) are only read
  *   txt:    fp32 [txt_len, H] text states
  *   rope:   fp32 [L, D/2, 2]
  *   dims->weight_dtype selects bf16, fp16 or int8 weights for every linear.
@@ -306,7 +330,15 @@ enum mmdit_epilogue {
                                  n >= split_n: out2 fp16 [m, ldo2] col
                                  out2_col + n - split_n = GELU_tanh(y) */
     MMDIT_EPI_BIAS_F32 = 4,   /* out fp32 [m, ldo] = y */
-    MMDIT_EPI_EULER = 5       /* out fp32 [m, ldo] += alpha * y (the Euler update) */
+    MMDIT_EPI_EULER = 5,      /* out fp32 [m, ldo] += alpha * y (the Euler update) */
+    MMDIT_EPI_SWIGLU = 6,     /* gated MLP (Luminal blog, "What the compiler found on
+                                 its own": fused SwiGLU of Flux.2 Klein). W rows are
+                                 [gate (n/2) | up (n/2)]; out fp16 [m, ldo] col f =
+                                 SiLU(y_f) * y_{n/2+f}, f < n/2. n a multiple of 256 */
+    MMDIT_EPI_SPLIT_SWIGLU = 7 /* columns n < split_n: out bf16 [m, ldo] col n = y;
+                                 the rest, [gate (M) | up (M)] with M = (n - split_n)/2:
+                                 out2 fp16 [m, ldo2] col out2_col + f = SiLU(gate_f) * up_f.
+                                 split_n and n - split_n multiples of 256 */
 };
 
 /*

@@ -78,6 +78,20 @@ def gelu_tanh(x):
 # --------------------------------------------------------------------------
 # linear layers ("What the compiler found on its own": multiply then sum)
 # --------------------------------------------------------------------------
+def swiglu(u) -> np.ndarray:
+    """Gated linear unit with SiLU (the fused SwiGLU activation that the
+    Luminal blog's section "What the compiler found on its own" names for
+    Flux.2 Klein): u = [gate | up] (two halves of the columns) ->
+    SiLU(gate) * up."""
+    u = _f64(u)
+    m = u.shape[-1] // 2
+    return silu(u[..., :m]) * u[..., m:]
+
+
+def mlp_activation(u, act: str) -> np.ndarray:
+    return swiglu(u) if act == "swiglu" else gelu_tanh(u)
+
+
 def weight_matrix(lin) -> np.ndarray:
     """The layer's weight as fp64: W itself, or diag(s) Q for an int8 layer
     (flux-amd-rocm benchmarks page: int8 weight-only linears)."""
@@ -260,7 +274,7 @@ def double_block(x, vec, ids, w, shp, rows: Optional[np.ndarray] = None,
         sh1, sc1, g1, sh2, sc2, g2 = mods[s]
         xs = xo[mask] + g1 * linear(o[mask], w[s]["proj"])
         h2 = ln_modulate(xs, sh2, sc2, shp.ln_eps)
-        a = gelu_tanh(linear(h2, w[s]["fc1"]))
+        a = mlp_activation(linear(h2, w[s]["fc1"]), shp.mlp_act)
         xs = xs + g2 * linear(a, w[s]["fc2"])
         xo[mask] = xs
     if return_stages:
@@ -289,7 +303,7 @@ def single_block(x, vec, ids, w, shp, rows: Optional[np.ndarray] = None,
     k = norm_rope_heads(k, w["k_norm"], phi, heads, shp.rms_eps)
     out_rows = np.arange(L) if rows is None else np.asarray(rows)
     o = attention(q, k, v, heads, out_rows)
-    cat = np.concatenate([o, gelu_tanh(m[out_rows])], axis=1)
+    cat = np.concatenate([o, mlp_activation(m[out_rows], shp.mlp_act)], axis=1)
     xo = x[out_rows] + g * linear(cat, w["linear2"])
     if return_stages:
         return xo, {"h": h, "u": u, "q": q, "k": k, "v": v, "attn": o, "mod": (sh, sc, g)}
@@ -315,9 +329,13 @@ def mlp_embedder(e, lins) -> np.ndarray:
 
 
 def conditioning(t: float, guidance: float, m) -> np.ndarray:
-    """vec = MLP_t(emb(t)) + MLP_g(emb(guidance))."""
-    return mlp_embedder(timestep_embedding(t), m["time_in"]) + \
-        mlp_embedder(timestep_embedding(guidance), m["guid_in"])
+    """vec = MLP_t(emb(t)) + MLP_g(emb(guidance)); a guidance-free model
+    (m["guid_in"] None: the step-distilled Flux.2 Klein of the Luminal blog)
+    has only the time term."""
+    vec = mlp_embedder(timestep_embedding(t), m["time_in"])
+    if m.get("guid_in") is not None:
+        vec = vec + mlp_embedder(timestep_embedding(guidance), m["guid_in"])
+    return vec
 
 
 def euler(z, v, t_cur: float, t_next: float) -> np.ndarray:
@@ -328,7 +346,10 @@ def euler(z, v, t_cur: float, t_next: float) -> np.ndarray:
 def velocity(z, txt, ids, m, shp, t_cur: float, guidance: float) -> np.ndarray:
     """The denoiser's prediction v for latent z [L_i, C] and text states
     txt [L_t, H]: embed, run the double then the single blocks, and apply the
-    final modulated LayerNorm and projection to the image rows."""
+    final modulated LayerNorm and projection to the image rows. When editing,
+    the last ``shp.ref_len`` rows of z are the encoded reference image: they
+    are embedded and attended to like the others, and v covers only the rows
+    before them."""
     vec = conditioning(t_cur, guidance, m)
     x = np.concatenate([_f64(txt), linear(z, m["img_in"])], axis=0)
     for wd in m["double"]:
@@ -336,11 +357,16 @@ def velocity(z, txt, ids, m, shp, t_cur: float, guidance: float) -> np.ndarray:
     for ws in m["single"]:
         x = single_block(x, vec, ids, ws, shp)
     sh, sc = modulation(vec, m["final_mod"], 2)
-    h = ln_modulate(x[shp.txt_len:], sh, sc, shp.ln_eps)
+    n = shp.img_len - shp.ref_len
+    h = ln_modulate(x[shp.txt_len:shp.txt_len + n], sh, sc, shp.ln_eps)
     return linear(h, m["final_out"])
 
 
 def denoise_step(z, txt, ids, m, shp, t_cur: float, t_next: float, guidance: float):
-    """One flow-matching Euler step of the latent; returns (z_next, v)."""
+    """One flow-matching Euler step of the latent; returns (z_next, v). The
+    reference rows of an edit (the last shp.ref_len) are carried unchanged."""
     v = velocity(z, txt, ids, m, shp, t_cur, guidance)
-    return euler(z, v, t_cur, t_next), v
+    z_next = _f64(z).copy()
+    n = shp.img_len - shp.ref_len
+    z_next[:n] = euler(z[:n], v, t_cur, t_next)
+    return z_next, v

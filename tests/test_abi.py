@@ -21,7 +21,7 @@ def test_exports_every_header_function():
 
 
 def test_abi_version_and_status_strings():
-    assert B.mmdit_abi_version() == B.MMDIT_ABI_VERSION == 2
+    assert B.mmdit_abi_version() == B.MMDIT_ABI_VERSION == 3
     for st in range(8):
         assert B.mmdit_status_string(st)
     assert B.mmdit_status_string(99) == "unknown status"
@@ -56,6 +56,12 @@ def _double():
     ({"img_len": 0}, B.MMDIT_E_SHAPE),
     ({"mlp_hidden": 1000}, B.MMDIT_E_SHAPE),
     ({"weight_dtype": 5}, B.MMDIT_E_DTYPE),
+    ({"mlp_act": 2}, B.MMDIT_E_ARG),
+    ({"guidance_embed": 2}, B.MMDIT_E_ARG),
+    ({"ref_len": 256}, B.MMDIT_E_SHAPE),             # ref_len must be < img_len (256)
+    ({"ref_len": -1}, B.MMDIT_E_SHAPE),
+    ({"mlp_act": B.MMDIT_ACT_SWIGLU, "mlp_hidden": 1088}, B.MMDIT_E_SHAPE),   # SwiGLU: M % 128
+    ({"mlp_act": B.MMDIT_ACT_SWIGLU, "hidden": 192, "heads": 3}, B.MMDIT_E_SHAPE),  # SwiGLU: H % 256
 ])
 def test_block_rejects_bad_dims(kw, status):
     d = _dims(**kw)
@@ -99,6 +105,12 @@ def test_single_and_step_validation():
     assert B.mmdit_denoise_step(d, m, FAKE, FAKE, FAKE, float("nan"), 0.9, 3.5, FAKE, need) == B.MMDIT_E_ARG
     d.in_channels = 48
     assert B.mmdit_denoise_step(d, m, FAKE, FAKE, FAKE, 1.0, 0.9, 3.5, FAKE, need) == B.MMDIT_E_SHAPE
+    d.in_channels = 64
+    m.guid_in[1] = B.mmdit_linear(0, 0, FAKE)
+    assert B.mmdit_denoise_step(d, m, FAKE, FAKE, FAKE, 1.0, 0.9, 3.5, FAKE, need) == B.MMDIT_E_NULL
+    d.guidance_embed = 0   # a guidance-free model does not read guid_in
+    need = B.mmdit_workspace_bytes(d, B.MMDIT_WS_STEP)
+    assert B.mmdit_denoise_step(d, m, FAKE, FAKE, FAKE, 1.0, 0.9, 3.5, FAKE, need - 1) == B.MMDIT_E_WORKSPACE
 
 
 def test_kernel_entry_validation():
@@ -119,6 +131,12 @@ def test_kernel_entry_validation():
     assert B.mmdit_k_gemm(g) == B.MMDIT_E_DTYPE  # int8 without scales
     g.weight_dtype = 3
     assert B.mmdit_k_gemm(g) == B.MMDIT_E_DTYPE
+    g.weight_dtype, g.epilogue, g.ldo = 0, B.MMDIT_EPI_SWIGLU, 64
+    assert B.mmdit_k_gemm(g) == B.MMDIT_E_SHAPE  # SwiGLU: n (2M) a multiple of 256
+    g.n, g.ldo = 256, 120
+    assert B.mmdit_k_gemm(g) == B.MMDIT_E_SHAPE  # ldo < n / 2
+    g.epilogue, g.n, g.ldo, g.split_n, g.out2, g.ldo2, g.out2_col = B.MMDIT_EPI_SPLIT_SWIGLU, 768, 256, 192, FAKE, 512, 256
+    assert B.mmdit_k_gemm(g) == B.MMDIT_E_SHAPE  # split at 192: a SwiGLU tile would straddle it
     lin = _linear()
     assert B.mmdit_k_gemv(FAKE, 100, lin, 10, 0, 1, 0, FAKE) == B.MMDIT_E_SHAPE
     assert B.mmdit_k_gemv(FAKE, 128, lin, 10, 3, 1, 0, FAKE) == B.MMDIT_E_DTYPE

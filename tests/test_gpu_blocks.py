@@ -14,6 +14,9 @@ pytestmark = pytest.mark.gpu
 
 RAGGED = synth.custom_shape("ragged-h128-L68", 710, 128, 2, 256, 5, (7, 9))
 RAGGED_D128 = synth.custom_shape("ragged-h256-d128-L203", 711, 256, 2, 512, 3, (10, 20))
+# SwiGLU with ragged lengths: 5 text tokens, a 7x9 image and its 7x9 reference
+RAGGED_SWIGLU = synth.custom_shape("ragged-swiglu-h256-d128-L131", 712, 256, 2, 384, 5, (7, 9),
+                                   **synth.KLEIN_KW)
 
 
 def _rope(A, d, shp):
@@ -66,6 +69,11 @@ def _check(g, ref, x, label):
     (RAGGED_D128, "single", "int8"),
     (RAGGED, "double", "f16"),
     (RAGGED_D128, "single", "f16"),
+    (synth.KLEIN_TINY, "double", "bf16"),
+    (synth.KLEIN_TINY, "single", "bf16"),
+    (synth.KLEIN_TINY, "double", "int8"),
+    (RAGGED_SWIGLU, "double", "f16"),
+    (RAGGED_SWIGLU, "single", "int8"),
 ])
 def test_block_small_full_compare(shape, kind, wt):
     say(f"block {kind} {shape.name} weights={wt}")
@@ -112,7 +120,9 @@ def test_block_zero_gate_identity(kind):
 
 @pytest.mark.parametrize("shape,kind,f16", [(synth.FLUX_DOUBLE, "double", False), (synth.FLUX_SINGLE, "single", False),
                                             (synth.QWEN_DOUBLE, "double", False), (synth.FLUX_DOUBLE, "double", True),
-                                            (synth.FLUX_SINGLE, "single", True)])
+                                            (synth.FLUX_SINGLE, "single", True), (synth.KLEIN_512, "double", True),
+                                            (synth.KLEIN_512, "single", True),
+                                            (synth.KLEIN_1200x800, "double", True)])
 def test_block_full_size_sampled_rows(shape, kind, f16):
     say(f"block full {kind} {shape.name} f16_weights={f16}")
     inp = synth.block_inputs(shape, kind)
@@ -175,3 +185,39 @@ def test_denoise_step_tiny(wt):
     B.check(B.mmdit_denoise_step(d, mm, z2, txt, rope, t0, t1, 3.5, ws, ws.numel(), stream()), "step")
     sync()
     np.testing.assert_array_equal(z2.cpu().numpy(), g)
+
+
+KLEIN_STEP = synth.custom_shape("klein-step-h256-2d2s", 721, 256, 4, 768, 64, (8, 8), n_double=2, n_single=2,
+                                **synth.KLEIN_KW)
+
+
+@pytest.mark.parametrize("wt", ["bf16", "f16"])
+def test_denoise_step_klein_tiny(wt):
+    """Flux.2 Klein-shaped step: SwiGLU MLPs, guidance-free conditioning,
+    modulation shared by the blocks of a type, 128 latent channels, and the
+    reference image appended to the image stream (editing). The reference
+    rows of the latent are read, never written."""
+    say(f"denoise step klein tiny weights={wt}")
+    shp, f16 = KLEIN_STEP, wt == "f16"
+    m = synth.model_weights(shp, int8=False)
+    s = synth.step_inputs(shp)
+    A = DeviceArena(f16_weights=f16)
+    d = dims_for(shp, False, f16)
+    mm = A.model(m)
+    rope = _rope(A, d, shp)
+    z = A.f32(s["z"])
+    txt = A.f32(s["txt"])
+    ws = A.workspace(B.mmdit_workspace_bytes(d, B.MMDIT_WS_STEP))
+    t0, t1 = 1.0, 0.75   # four steps
+    # the guidance argument is unused by a guidance-free model
+    B.check(B.mmdit_denoise_step(d, mm, z, txt, rope, t0, t1, 123.0, ws, ws.numel(), stream()), "step")
+    sync()
+    g = z.cpu().numpy()
+    z_ref, v_ref = O.denoise_step(s["z"], s["txt"], s["ids"], m, shp, t0, t1, 0.0)
+    n = shp.img_len - shp.ref_len
+    np.testing.assert_array_equal(g[n:], s["z"][n:].astype(np.float32))
+    assert rel_err(g, z_ref) <= TOL
+    v_gpu = (g[:n].astype(np.float64) - s["z"][:n]) / (t1 - t0)
+    ev = rel_err(v_gpu, v_ref)
+    say(f"  klein step: rel_err(z)={rel_err(g, z_ref):.3e} rel_err(v)={ev:.3e}")
+    assert ev <= TOL, ev

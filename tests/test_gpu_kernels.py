@@ -225,7 +225,15 @@ def _run_gemm(m, n, k, epi, int8, rows=None, tid=50, f16=False):
     da = A.f16(a)
     wt = B.MMDIT_INT8 if int8 else (B.MMDIT_F16 if f16 else B.MMDIT_BF16)
     g = B.mmdit_gemm(m=m, n=n, k=k, weight_dtype=wt, a=da.data_ptr(), lda=k, w=A.linear(lin), epilogue=epi)
-    split = 3 * n // 7 // 64 * 64 if epi == B.MMDIT_EPI_SPLIT_GELU else n
+    swiglu = epi in (B.MMDIT_EPI_SWIGLU, B.MMDIT_EPI_SPLIT_SWIGLU)
+    if epi == B.MMDIT_EPI_SPLIT_GELU:
+        split = 3 * n // 7 // 64 * 64
+    elif epi == B.MMDIT_EPI_SPLIT_SWIGLU:
+        split = (n // 3) // 256 * 256       # q|k|v part; the rest is [gate | up]
+    elif epi == B.MMDIT_EPI_SWIGLU:
+        split = n // 2                      # output width M
+    else:
+        split = n
     _SPLIT[0] = split
     gate = rnd(tid + 5, (n,), 0.7)
     resid = rnd(tid + 6, (m, n))
@@ -233,14 +241,16 @@ def _run_gemm(m, n, k, epi, int8, rows=None, tid=50, f16=False):
     if f32out:
         out = A.f32(resid) if epi == B.MMDIT_EPI_EULER else A.empty_f32(m, n)
     else:
-        out = A.empty_bf16(m, split) if epi != B.MMDIT_EPI_BIAS_GELU else A.empty_f16(m, split)
+        f16out = epi in (B.MMDIT_EPI_BIAS_GELU, B.MMDIT_EPI_SWIGLU)
+        out = A.empty_f16(m, split) if f16out else A.empty_bf16(m, split)
     g.out, g.ldo = out.data_ptr(), (n if f32out else split)
     out2 = None
     if epi == B.MMDIT_EPI_GATE_RESID:
         g.gate, g.resid, g.ldr = A.f32(gate).data_ptr(), A.f32(resid).data_ptr(), n
-    if epi == B.MMDIT_EPI_SPLIT_GELU:
-        out2 = A.empty_f16(m, 64 + n - split)
-        g.split_n, g.out2, g.ldo2, g.out2_col = split, out2.data_ptr(), 64 + n - split, 64
+    if epi in (B.MMDIT_EPI_SPLIT_GELU, B.MMDIT_EPI_SPLIT_SWIGLU):
+        w2 = (n - split) // 2 if swiglu else n - split
+        out2 = A.empty_f16(m, 64 + w2)
+        g.split_n, g.out2, g.ldo2, g.out2_col = split, out2.data_ptr(), 64 + w2, 64
     if epi == B.MMDIT_EPI_EULER:
         g.alpha = -1.0 / 28
     B.check(B.mmdit_k_gemm(g, stream()))
@@ -258,10 +268,13 @@ def _run_gemm(m, n, k, epi, int8, rows=None, tid=50, f16=False):
         return to_numpy_f32(out)[sel], y
     if epi == B.MMDIT_EPI_EULER:
         return to_numpy_f32(out)[sel], O.euler(resid[sel], y, 1.0, 1.0 - 1.0 / 28)
-    # split: first columns plain, the rest GELU at column offset 64 of out2
+    if epi == B.MMDIT_EPI_SWIGLU:
+        return to_numpy_f32(out)[sel], O.swiglu(y)
+    # split: first columns plain, the rest GELU (or SwiGLU) at column offset 64 of out2
     g1 = to_numpy_f32(out)[sel]
     g2 = to_numpy_f32(out2)[sel][:, 64:]
-    return np.concatenate([g1, g2], axis=1), np.concatenate([y[:, :split], O.gelu_tanh(y[:, split:])], axis=1)
+    act = O.swiglu if swiglu else O.gelu_tanh
+    return np.concatenate([g1, g2], axis=1), np.concatenate([y[:, :split], act(y[:, split:])], axis=1)
 
 
 def _gemm_err(g, ref, epi, k):
@@ -272,7 +285,7 @@ def _gemm_err(g, ref, epi, k):
         return rel_err(g, ref)
     if epi == B.MMDIT_EPI_BIAS:
         return rel_err_rounded_out(g, ref, "bf16")
-    if epi == B.MMDIT_EPI_BIAS_GELU:
+    if epi in (B.MMDIT_EPI_BIAS_GELU, B.MMDIT_EPI_SWIGLU):
         return rel_err_rounded_out(g, ref, "f16")
     s = _SPLIT[0]
     return max(rel_err_rounded_out(g[:, :s], ref[:, :s], "bf16"), rel_err_rounded_out(g[:, s:], ref[:, s:], "f16"))
@@ -301,6 +314,32 @@ def test_gemm_full_size_sampled_rows(m, n, k, epi):
     say(f"gemm full m={m} n={n} k={k} epi={epi}")
     rows = np.unique(np.r_[0, 255, 256, m - 1, np.random.default_rng(m).integers(0, m, 40)])
     g, ref = _run_gemm(m, n, k, epi, False, rows=rows, tid=60)
+    assert _gemm_err(g, ref, epi, k) <= TOL
+
+
+@pytest.mark.parametrize("m,n,k,epi,wt", [
+    (513, 1024, 256, B.MMDIT_EPI_SWIGLU, "bf16"), (300, 512, 448, B.MMDIT_EPI_SWIGLU, "int8"),
+    (77, 2048, 320, B.MMDIT_EPI_SWIGLU, "f16"), (1, 256, 64, B.MMDIT_EPI_SWIGLU, "bf16"),
+    (320, 1280, 256, B.MMDIT_EPI_SPLIT_SWIGLU, "bf16"), (257, 2816, 512, B.MMDIT_EPI_SPLIT_SWIGLU, "int8"),
+    (130, 1280, 256, B.MMDIT_EPI_SPLIT_SWIGLU, "f16")])
+def test_gemm_swiglu(m, n, k, epi, wt):
+    """SwiGLU epilogues: W rows [gate | up] in their natural layout; the
+    kernel pairs them per feature in registers."""
+    say(f"gemm swiglu m={m} n={n} k={k} epi={epi} weights={wt}")
+    g, ref = _run_gemm(m, n, k, epi, wt == "int8", tid=110, f16=wt == "f16")
+    assert _gemm_err(g, ref, epi, k) <= TOL
+    assert within_one_ulp(g[:, _SPLIT[0]:] if epi == B.MMDIT_EPI_SPLIT_SWIGLU else g,
+                          ref[:, _SPLIT[0]:] if epi == B.MMDIT_EPI_SPLIT_SWIGLU else ref, "f16", 1e-3) <= 8
+
+
+@pytest.mark.parametrize("m,n,k,epi", [(2560, 24576, 4096, B.MMDIT_EPI_SWIGLU),
+                                       (2560, 36864, 4096, B.MMDIT_EPI_SPLIT_SWIGLU)])
+def test_gemm_swiglu_klein_size_sampled_rows(m, n, k, epi):
+    """Flux.2 Klein-shaped MLP-in (fc1, 4096 -> 2 x 12288) and single-block
+    linear1 (4096 -> 3 x 4096 + 2 x 12288) at 512x512 editing (2560 tokens)."""
+    say(f"gemm swiglu full m={m} n={n} k={k} epi={epi}")
+    rows = np.unique(np.r_[0, 255, 256, m - 1, np.random.default_rng(n).integers(0, m, 40)])
+    g, ref = _run_gemm(m, n, k, epi, False, rows=rows, tid=120)
     assert _gemm_err(g, ref, epi, k) <= TOL
 
 

@@ -218,6 +218,23 @@ def test_silu_against_logistic():
     np.testing.assert_allclose(O.silu(x) - O.silu(-x), x, atol=1e-12)
 
 
+def test_swiglu_closed_forms_and_operand_order():
+    """SwiGLU (the gated MLP activation of Flux.2 Klein): the first half of
+    the columns is the gate, the second the value."""
+    g = np.linspace(-20, 20, 81)
+    u = rng.standard_normal(81)
+    np.testing.assert_allclose(O.swiglu(np.c_[g, np.ones(81)]), (g * expit(g))[:, None],
+                               rtol=1e-14, atol=1e-300)
+    np.testing.assert_array_equal(O.swiglu(np.c_[np.zeros(81), u]), np.zeros((81, 1)))
+    # hand value: SiLU(1) * 2 = 2 / (1 + e^-1)
+    assert abs(O.swiglu(np.array([[1.0, 2.0]]))[0, 0] - 2.0 / (1.0 + math.exp(-1.0))) < 1e-15
+    # gate first: swapping the halves changes the result
+    assert abs(O.swiglu(np.array([[2.0, 1.0]]))[0, 0] - 2.0 / (1.0 + math.exp(-2.0))) < 1e-15
+    # several features: column f pairs gate f with value M + f
+    x = rng.standard_normal((3, 8))
+    np.testing.assert_allclose(O.swiglu(x), x[:, :4] * expit(x[:, :4]) * x[:, 4:], rtol=1e-13)
+
+
 # ---------------------------------------------------------------- linear
 def test_linear_brute_force_tiny_rectangular():
     x = rng.standard_normal((3, 5))
@@ -439,3 +456,82 @@ def test_int8_step_matches_dequantised_bf16_step():
     v8 = O.velocity(s["z"], s["txt"], s["ids"], m8, shp, 0.8, 3.5)
     vf = O.velocity(s["z"], s["txt"], s["ids"], mf, shp, 0.8, 3.5)
     np.testing.assert_array_equal(v8, vf)
+
+
+def _param_count(shp) -> int:
+    """Parameters of a model of this shape, from the layer sizes that
+    synth.model_weights draws (biases and norm scales included)."""
+    H, D, C = shp.hidden, shp.head_dim, shp.in_channels
+
+    def lin(o, i):
+        return o * i + o
+    dbl = 2 * (lin(3 * H, H) + lin(H, H) + lin(shp.mlp_out, H) + lin(H, shp.mlp) + 2 * D)
+    sgl = lin(3 * H + shp.mlp_out, H) + lin(H, H + shp.mlp) + 2 * D
+    mod_d, mod_s = 2 * lin(6 * H, H), lin(3 * H, H)
+    emb = lin(H, C) + lin(H, 256) + lin(H, H) + lin(2 * H, H) + lin(C, H)
+    if shp.guidance_embed:
+        emb += lin(H, 256) + lin(H, H)
+    if shp.shared_mod:
+        return shp.n_double * dbl + shp.n_single * sgl + mod_d + mod_s + emb
+    return shp.n_double * (dbl + mod_d) + shp.n_single * (sgl + mod_s) + emb
+
+
+def test_klein_shape_readings_give_nine_billion_parameters():
+    """The Luminal blog names the model Flux.2 Klein 9B and gives H 4096, 32
+    heads, 8 double and 24 single blocks, SwiGLU. The pages leave the MLP width
+    and the modulation layout open; the readings taken (MLP width 3H, one
+    modulation per block type) give 9.03 B parameters. The alternatives miss
+    the name: width 4H gives 11.0 B, per-block modulation 11.6 B, width 8H/3
+    8.3 B."""
+    shp = synth.KLEIN_STEP_512
+    assert (shp.hidden, shp.heads, shp.n_double, shp.n_single, shp.mlp_act) == (4096, 32, 8, 24, "swiglu")
+    n = _param_count(shp)
+    assert abs(n - 9.0e9) < 0.02 * 9.0e9, n
+    import dataclasses
+    for alt in (dataclasses.replace(shp, mlp=4 * 4096), dataclasses.replace(shp, shared_mod=False),
+                dataclasses.replace(shp, mlp=10880)):
+        assert abs(_param_count(alt) - 9.0e9) > 0.05 * 9.0e9
+
+
+def test_klein_step_structure_matches_reported_launch_counts():
+    """The Klein-shaped step (SwiGLU, guidance-free, reference image appended,
+    shared modulation) runs the per-step fused-kernel counts of the Luminal
+    blog too: the editing tokens change lengths, not the block structure."""
+    with open(os.path.join(GOLDEN, "klein_structure.json")) as f:
+        g = json.load(f)
+    shp = synth.custom_shape("pin-klein-edit", 904, 64, 2, 128, 4, (2, 2), n_double=g["double_blocks"],
+                             n_single=g["single_blocks"], **synth.KLEIN_KW)
+    m = synth.model_weights(shp, int8=False)
+    s = synth.step_inputs(shp)
+    O.SITE_COUNTS.clear()
+    O.velocity(s["z"], s["txt"], s["ids"], m, shp, 0.5, 0.0)
+    assert O.SITE_COUNTS["rmsnorm_rope"] == g["rmsnorm_rope_per_step"]
+    assert O.SITE_COUNTS["ln_modulate"] == g["ln_modulate_per_step"]
+    assert O.SITE_COUNTS["attention"] == g["attention_sites_per_step"]
+
+
+def test_edit_step_reference_rows_and_guidance_free_conditioning():
+    """Editing: the reference latent rows ride along unchanged, sit at time
+    index 1 of the position ids, and are attended to (changing them changes
+    the prediction). Guidance-free: the guidance value has no effect."""
+    shp = synth.custom_shape("pin-edit", 905, 64, 2, 128, 4, (3, 3), n_double=1, n_single=1, **synth.KLEIN_KW)
+    m = synth.model_weights(shp, int8=False)
+    s = synth.step_inputs(shp)
+    n, r = shp.img_len - shp.ref_len, shp.ref_len
+    assert (n, r) == (9, 9)
+    ids = s["ids"]
+    np.testing.assert_array_equal(ids[shp.txt_len:shp.txt_len + n, 0], 0)
+    np.testing.assert_array_equal(ids[shp.txt_len + n:, 0], 1)
+    np.testing.assert_array_equal(ids[shp.txt_len:shp.txt_len + n, 1:], ids[shp.txt_len + n:, 1:])
+    z1, v = O.denoise_step(s["z"], s["txt"], ids, m, shp, 1.0, 0.75, 3.5)
+    assert v.shape == (n, shp.in_channels)
+    np.testing.assert_array_equal(z1[n:], s["z"][n:])
+    np.testing.assert_allclose(z1[:n], s["z"][:n] - 0.25 * v, atol=1e-14)
+    z2, v2 = O.denoise_step(s["z"], s["txt"], ids, m, shp, 1.0, 0.75, -7.0)
+    np.testing.assert_array_equal(v2, v)
+    zr = s["z"].copy()
+    zr[n:] = rng.standard_normal((r, shp.in_channels))
+    _, v3 = O.denoise_step(zr, s["txt"], ids, m, shp, 1.0, 0.75, 3.5)
+    assert np.max(np.abs(v3 - v)) > 1e-6
+    # shared modulation: every block of a type holds the same weights
+    assert m["single"][0]["mod"] is m["single"][-1]["mod"]
