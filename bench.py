@@ -37,7 +37,7 @@ def block_flops(shp) -> float:
     """Algorithmic FLOPs of one double block: 2*M*N*K per projection (both
     streams) plus 4*L^2*H for QK^T and PV; modulation GEMVs included."""
     L, H, M = shp.seq_len, shp.hidden, shp.mlp
-    lin = 2 * L * H * (3 * H + H + M + M)
+    lin = 2 * L * H * (3 * H + H + shp.mlp_out + M)   # fc1 has 2M outputs with SwiGLU
     attn = 4 * L * L * H
     mod = 2 * 2 * 6 * H * H
     return float(lin + attn + mod)
@@ -45,12 +45,14 @@ def block_flops(shp) -> float:
 
 def single_flops(shp) -> float:
     L, H, M = shp.seq_len, shp.hidden, shp.mlp
-    return float(2 * L * H * (3 * H + M) + 2 * L * (H + M) * H + 4 * L * L * H + 2 * 3 * H * H)
+    return float(2 * L * H * (3 * H + shp.mlp_out) + 2 * L * (H + M) * H + 4 * L * L * H + 2 * 3 * H * H)
 
 
 def step_flops(shp) -> float:
     L, H, C = shp.seq_len, shp.hidden, shp.in_channels
-    extra = 2 * shp.img_len * C * H * 2 + 2 * 2 * (256 * H + H * H) + 2 * 2 * H * H
+    n_emb = 2 if shp.guidance_embed else 1
+    extra = (2 * shp.img_len * C * H + 2 * (shp.img_len - shp.ref_len) * H * C
+             + n_emb * 2 * (256 * H + H * H) + 2 * 2 * H * H)
     return shp.n_double * block_flops(shp) + shp.n_single * single_flops(shp) + extra
 
 
@@ -93,7 +95,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-step", action="store_true", help="skip the full denoise-step timing")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="rows of the block the CPU oracle computes (0: all rows, the whole block)")
+    ap.add_argument("--no-klein", action="store_true", help="skip the Flux.2 Klein-shaped edit timing")
     ap.add_argument("--probe", action="store_true",
                     help="only launch the dominant kernel (MLP-in GEMM, 10x) and a 1 GiB device copy (3x), "
                          "for hardware-counter runs")
@@ -262,13 +266,86 @@ def main() -> int:
             del S, mm, tm
             torch.cuda.empty_cache()
 
+    # ------------------------------------------------------------ Flux.2 Klein-shaped image edit
+    if not args.no_klein:
+        import dataclasses
+        torch.cuda.empty_cache()
+        kshp = synth.KLEIN_STEP_512
+        log("bench: generating Flux.2 Klein-shaped weights on the device (fp16-encoded, ~9 B parameters)")
+        tm = TimingModel(kshp, int8=False, seed=43, f16=True)
+        klein = {"workload": "Flux.2 Klein 9B-shaped image edit: H4096 32x128 SwiGLU MLP 12288, 8 double + 24 "
+                             "single blocks, 512 text tokens + output image + reference image tokens, 4 "
+                             "guidance-free Euler steps, fp16-encoded weights"}
+        # one double block at the largest edit size (1200x800: 512 + 2 x 3750 tokens)
+        big = dataclasses.replace(kshp, name="klein-1200x800", grid=(50, 75), n_double=1, n_single=0)
+        K = DeviceArena()
+        kd = dims_for(big, f16=True)
+        krope = K.empty_f32(big.seq_len, big.head_dim // 2, 2)
+        B.check(B.mmdit_rope_table(kd, K.i32(synth.position_ids(big)), krope, stream), "rope")
+        kx = K.empty_f32(big.seq_len, big.hidden)
+        kx.normal_()
+        kvec = K.empty_f32(big.hidden)
+        kvec.normal_()
+        kws = K.workspace(B.mmdit_workspace_bytes(kd, B.MMDIT_WS_DOUBLE))
+        kout = K.empty_f32(big.seq_len, big.hidden)
+        for _ in range(2):
+            B.check(B.mmdit_block_forward(kd, tm.doubles[0], kvec, krope, kx, kout, kws, kws.numel(), stream))
+        torch.cuda.synchronize()
+        k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n_k = 10
+        k0.record(stream)
+        for _ in range(n_k):
+            B.check(B.mmdit_block_forward(kd, tm.doubles[0], kvec, krope, kx, kout, kws, kws.numel(), stream))
+        k1.record(stream)
+        torch.cuda.synchronize()
+        ms_kb = k0.elapsed_time(k1) / n_k
+        klein["double_block_1200x800_ms"] = round(ms_kb, 3)
+        klein["double_block_1200x800_tflops"] = round(block_flops(big) / (ms_kb * 1e-3) / 1e12, 2)
+        log(f"bench: Klein double block 1200x800 (L={big.seq_len}) {ms_kb:.3f} ms -> "
+            f"{klein['double_block_1200x800_tflops']:.1f} TFLOP/s")
+        del K
+        torch.cuda.empty_cache()
+        # the 4-step edit at the three sizes of the Luminal blog's setup
+        for label, grid in (("512x512", (32, 32)), ("704x864", (54, 44)), ("1200x800", (50, 75))):
+            es = dataclasses.replace(kshp, name=f"klein-{label}", grid=grid)
+            E = DeviceArena()
+            ed = dims_for(es, f16=True)
+            erope = E.empty_f32(es.seq_len, es.head_dim // 2, 2)
+            B.check(B.mmdit_rope_table(ed, E.i32(synth.position_ids(es)), erope, stream), "rope")
+            z = E.empty_f32(es.img_len, es.in_channels)
+            z.normal_()
+            txt = E.empty_f32(es.txt_len, es.hidden)
+            txt.normal_()
+            ews = E.workspace(B.mmdit_workspace_bytes(ed, B.MMDIT_WS_STEP))
+            ts = synth.sigma_schedule(4)
+            B.check(B.mmdit_denoise_step(ed, tm.model, z, txt, erope, ts[0], ts[1], 0.0, ews, ews.numel(), stream))
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(4):
+                B.check(B.mmdit_denoise_step(ed, tm.model, z, txt, erope, ts[i], ts[i + 1], 0.0, ews, ews.numel(),
+                                             stream))
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms_edit = e0.elapsed_time(e1)
+            tf = 4 * step_flops(es) / (ms_edit * 1e-3) / 1e12
+            klein[f"ms_per_edit_{label}"] = round(ms_edit, 2)
+            klein[f"tflops_{label}"] = round(tf, 1)
+            log(f"bench: Klein edit {label} (L={es.seq_len}) 4 steps {ms_edit:.1f} ms -> {tf:.1f} TFLOP/s")
+            del E
+            torch.cuda.empty_cache()
+        result["klein_edit"] = klein
+        del tm
+        torch.cuda.empty_cache()
+
     # ------------------------------------------------------------ CPU oracle baseline
     if not args.no_cpu:
         import oracle as O
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
         rng = np.random.default_rng(7)
-        rows = np.sort(rng.choice(shp.seq_len, size=min(args.cpu_rows, shp.seq_len), replace=False))
+        n_rows = shp.seq_len if args.cpu_rows <= 0 else min(args.cpu_rows, shp.seq_len)
+        rows = np.sort(rng.choice(shp.seq_len, size=n_rows, replace=False))
         log(f"bench: CPU oracle on {len(rows)} sampled rows of the block ({threads} BLAS threads)")
         c0 = time.perf_counter()
         O.double_block(inp["x"], inp["vec"], inp["ids"], inp["w"], shp, rows=rows)
@@ -278,8 +355,11 @@ def main() -> int:
         result["cpu_baseline"] = {
             "value": round(sample_flops / cdt / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"numpy fp64 oracle of the FLUX double block: QKV for all {L} tokens, attention, "
-                      f"projections and MLP for {r} sampled rows; {sample_flops / 1e9:.0f} GFLOP in {cdt:.1f} s",
+            "sample": (f"numpy fp64 oracle of the whole FLUX double block ({L} tokens); "
+                       if r == L else
+                       f"numpy fp64 oracle of the FLUX double block: QKV for all {L} tokens, attention, "
+                       f"projections and MLP for {r} sampled rows; ") +
+                      f"{sample_flops / 1e9:.0f} GFLOP in {cdt:.1f} s",
             "seconds": round(cdt, 2)}
         log(f"bench: CPU oracle {cdt:.1f} s")
 
