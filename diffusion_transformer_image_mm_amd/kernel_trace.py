@@ -17,12 +17,13 @@ import statistics as st
 import sys
 from collections import defaultdict
 
-DOMINANT = "mmdit::gemm_kernel<2, 1>"
+DOMINANT = "mmdit::gemm_kernel<2, 1, 0>"
 FLOPS = 2 * 4608 * 12288 * 3072
 LABELS = [("gemv_kernel", "modulation GEMV (both streams)"), ("ln_modulate", "LN + modulate"),
-          ("gemm_kernel<2, 0>", "QKV GEMM"), ("qknorm", "QK-RMSNorm + RoPE + relayout"),
-          ("attention", "attention"), ("gemm_kernel<2, 2>", "gated projection GEMM"),
-          ("gemm_kernel<2, 1>", "MLP-in GEMM + GELU")]
+          ("gemm_kernel<2, 0, 0>", "QKV GEMM"), ("qknorm", "QK-RMSNorm + RoPE + relayout"),
+          ("attention", "attention"), ("gemm_kernel<2, 2, 0>", "gated projection GEMM"),
+          ("gemm_kernel<2, 2, 1>", "gated projection GEMM, pipelined"),
+          ("gemm_kernel<2, 1, 0>", "MLP-in GEMM + GELU")]
 KERNELS_PER_BLOCK = 9
 
 

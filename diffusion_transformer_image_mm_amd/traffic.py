@@ -25,7 +25,7 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCE = os.path.join(ROOT, "diffusion_transformer_image_mm_amd", "csrc", "k_gemm.hip")
 SUMMARY = os.path.join(ROOT, "profiles", "gemm_mlp_in_flux_traffic.txt")
-KERNEL_MATCH = "gemm_kernel<2, 1>"          # fp16 weights, bias + GELU epilogue
+KERNEL_MATCH = "gemm_kernel<2, 1, 0>"       # fp16 weights, bias + GELU epilogue, plain loop
 COPY_MATCH = "__amd_rocclr_copyBuffer"
 COPY_KIB = 1 << 20                            # the probe copies 1 GiB
 

@@ -352,10 +352,14 @@ def test_gemm_int8_rerun_bit_exact():
 
 @pytest.mark.parametrize("m,n,k,epi", [(513, 1024, 256, B.MMDIT_EPI_BIAS_GELU), (700, 256, 1024, B.MMDIT_EPI_GATE_RESID),
                                        (320, 1792, 256, B.MMDIT_EPI_SPLIT_GELU), (1, 128, 64, B.MMDIT_EPI_BIAS),
-                                       (4608, 3072, 12288, B.MMDIT_EPI_GATE_RESID)])
+                                       (4608, 3072, 12288, B.MMDIT_EPI_GATE_RESID),
+                                       (300, 320, 8256, B.MMDIT_EPI_BIAS_GELU), (77, 512, 8192, B.MMDIT_EPI_SWIGLU),
+                                       (513, 256, 8320, B.MMDIT_EPI_GATE_RESID)])
 def test_gemm_f16_weights_bit_identical(m, n, k, epi):
     """Weights re-encoded once by mmdit_weights_to_f16 give the bf16 path's
-    results bit for bit (same fp16 values reach the matrix cores)."""
+    results bit for bit (same fp16 values reach the matrix cores). With
+    K >= 8192 the fp16-weight GEMM runs its pipelined main loop (odd and even
+    k-step counts here), so this also pins that loop to the plain one."""
     say(f"gemm f16 weights m={m} n={n} k={k} epi={epi}")
     rows = None if m < 4096 else np.unique(np.r_[0, 255, 256, m - 1, np.arange(0, m, 97)])
     a, ref = _run_gemm(m, n, k, epi, False, rows=rows, tid=90)
