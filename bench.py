@@ -263,6 +263,42 @@ def main() -> int:
             result[f"denoise_step_tflops_{key}"] = round(step_flops(sshp) / (ms_step * 1e-3) / 1e12, 2)
             log(f"bench: denoise step ({key}) {ms_step:.2f} ms -> "
                 f"{result[f'denoise_step_tflops_{key}']:.1f} TFLOP/s; 28 steps = {28 * ms_step / 1e3:.2f} s")
+            if key == "f16":
+                # a whole 28-step sampling run: per-step conditioning + modulation GEMVs,
+                # against all modulations computed up front (one GEMM per modulation
+                # linear over the 28 steps) and premodulated steps
+                z0 = S.f32(st["z"])
+                nf = B.mmdit_modulation_floats(sd)
+                mod = S.empty_f32(28, nf)
+                mws = S.workspace(B.mmdit_modulation_workspace_bytes(sd, 28))
+                r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                z.copy_(z0)
+                torch.cuda.synchronize()
+                r0.record(stream)
+                for i in range(28):
+                    B.check(B.mmdit_denoise_step(sd, mm, z, txt, srope, ts[i], ts[i + 1], 3.5, sws, sws.numel(),
+                                                 stream))
+                r1.record(stream)
+                torch.cuda.synchronize()
+                ms_run = r0.elapsed_time(r1)
+                z.copy_(z0)
+                torch.cuda.synchronize()
+                r0.record(stream)
+                B.check(B.mmdit_modulation_batch(sd, mm, ts[:28], 3.5, mod, mws, mws.numel(), stream))
+                r2 = torch.cuda.Event(enable_timing=True)
+                r2.record(stream)
+                for i in range(28):
+                    B.check(B.mmdit_denoise_step_premod(sd, mm, mod[i], z, txt, srope, ts[i], ts[i + 1], sws,
+                                                        sws.numel(), stream))
+                r1.record(stream)
+                torch.cuda.synchronize()
+                ms_hoist, ms_mod = r0.elapsed_time(r1), r0.elapsed_time(r2)
+                result["sampling_28_steps_f16"] = {
+                    "s_per_image_step_by_step": round(ms_run / 1e3, 3),
+                    "s_per_image_hoisted_modulation": round(ms_hoist / 1e3, 3),
+                    "ms_modulation_batch_28_steps": round(ms_mod, 2)}
+                log(f"bench: 28 steps (f16) step by step {ms_run / 1e3:.3f} s; modulation hoisted "
+                    f"{ms_hoist / 1e3:.3f} s (of which the 28-step modulation batch {ms_mod:.1f} ms)")
             del S, mm, tm
             torch.cuda.empty_cache()
 

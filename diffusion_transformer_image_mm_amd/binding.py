@@ -116,6 +116,12 @@ _SIGS = {
     "mmdit_denoise_step": (c_int, [POINTER(mmdit_dims), POINTER(mmdit_model), _P, _P, _P, c_float,
                                    c_float, c_float, _P, c_size_t, _P]),
     "mmdit_rope_table": (c_int, [POINTER(mmdit_dims), _P, _P, _P]),
+    "mmdit_modulation_floats": (c_size_t, [POINTER(mmdit_dims)]),
+    "mmdit_modulation_workspace_bytes": (c_size_t, [POINTER(mmdit_dims), c_int]),
+    "mmdit_modulation_batch": (c_int, [POINTER(mmdit_dims), POINTER(mmdit_model), POINTER(c_float), c_int, c_float,
+                                       _P, _P, c_size_t, _P]),
+    "mmdit_denoise_step_premod": (c_int, [POINTER(mmdit_dims), POINTER(mmdit_model), _P, _P, _P, _P, c_float,
+                                          c_float, _P, c_size_t, _P]),
     "mmdit_k_ln_modulate": (c_int, [_P, c_int, c_int, c_int, _P, _P, _P, _P, c_float, _P, _P]),
     "mmdit_k_qknorm_rope": (c_int, [_P, c_int, c_int, c_int, c_int, c_int, _P, _P, _P, _P, _P, c_float,
                                     c_int, _P, _P, _P, _P]),
@@ -172,6 +178,28 @@ def mmdit_block_forward(dims, w, vec, rope, x_in, x_out, ws, ws_bytes, stream=No
 def mmdit_single_block_forward(dims, w, vec, rope, x_in, x_out, ws, ws_bytes, stream=None) -> int:
     return lib.mmdit_single_block_forward(ctypes.byref(dims), ctypes.byref(w), ptr(vec), ptr(rope),
                                           ptr(x_in), ptr(x_out), ptr(ws), ws_bytes, stream_handle(stream))
+
+
+def mmdit_modulation_floats(dims) -> int:
+    return lib.mmdit_modulation_floats(ctypes.byref(dims))
+
+
+def mmdit_modulation_workspace_bytes(dims, n_steps: int) -> int:
+    return lib.mmdit_modulation_workspace_bytes(ctypes.byref(dims), n_steps)
+
+
+def mmdit_modulation_batch(dims, model, t, guidance, mod, ws, ws_bytes, stream=None) -> int:
+    """t: a sequence of step times (host); marshalled to a float32 array."""
+    n = len(t)
+    arr = (c_float * max(n, 1))(*[float(v) for v in t])
+    return lib.mmdit_modulation_batch(ctypes.byref(dims), ctypes.byref(model), arr, n, guidance, ptr(mod),
+                                      ptr(ws), ws_bytes, stream_handle(stream))
+
+
+def mmdit_denoise_step_premod(dims, model, mod, latent, txt, rope, t_cur, t_next, ws, ws_bytes,
+                              stream=None) -> int:
+    return lib.mmdit_denoise_step_premod(ctypes.byref(dims), ctypes.byref(model), ptr(mod), ptr(latent), ptr(txt),
+                                         ptr(rope), t_cur, t_next, ptr(ws), ws_bytes, stream_handle(stream))
 
 
 def mmdit_denoise_step(dims, model, latent, txt, rope, t_cur, t_next, guidance, ws, ws_bytes,

@@ -272,14 +272,17 @@ __global__ void f32_to_f16_kernel(const float* __restrict__ x, uint16_t* __restr
 }
 
 // ---------------------------------------------------------------- blocks
+// premod: the block's modulation [txt 6H | img 6H] computed beforehand
+// (mmdit_modulation_batch), or null to compute it here from vec
 int run_double(const mmdit_dims* d, const mmdit_double_weights* w, const float* vec, const float* rope,
-               const float* x_in, float* x_out, const DoubleWs& ws, hipStream_t s) {
+               const float* x_in, float* x_out, const DoubleWs& ws, hipStream_t s,
+               const float* premod = nullptr) {
     const int Lt = d->txt_len, Li = d->img_len, L = Lt + Li, H = d->hidden, M = d->mlp_hidden;
     const int dt = d->weight_dtype, LP = padded_len(d);
-    float* mt = ws.mod;
-    float* mi = ws.mod + 6 * H;
+    const float* mt = premod ? premod : ws.mod;
+    const float* mi = mt + 6 * H;
     // a1: modulation of each stream
-    MMDIT_HIP(gemv_2(vec, H, w->txt.mod, mt, w->img.mod, mi, 6 * H, dt, 1, s));
+    if (!premod) MMDIT_HIP(gemv_2(vec, H, w->txt.mod, ws.mod, w->img.mod, ws.mod + 6 * H, 6 * H, dt, 1, s));
     // a2: LN1 + modulate
     MMDIT_HIP(launch_ln_modulate(x_in, L, H, Lt, mt, mt + H, mi, mi + H, d->ln_eps, ws.h, s));
     // a3: QKV
@@ -318,11 +321,12 @@ int run_double(const mmdit_dims* d, const mmdit_double_weights* w, const float* 
 }
 
 int run_single(const mmdit_dims* d, const mmdit_single_weights* w, const float* vec, const float* rope,
-               const float* x_in, float* x_out, const SingleWs& ws, hipStream_t s) {
+               const float* x_in, float* x_out, const SingleWs& ws, hipStream_t s,
+               const float* premod = nullptr) {
     const int L = seq_len(d), H = d->hidden, M = d->mlp_hidden;
     const int dt = d->weight_dtype, LP = padded_len(d);
-    float* m = ws.mod;
-    MMDIT_HIP(gemv(vec, H, w->mod, 3 * H, dt, 1, 0, m, s));
+    const float* m = premod ? premod : ws.mod;
+    if (!premod) MMDIT_HIP(gemv(vec, H, w->mod, 3 * H, dt, 1, 0, ws.mod, s));
     MMDIT_HIP(launch_ln_modulate(x_in, L, H, 0, m, m + H, m, m + H, d->ln_eps, ws.h, s));
     {
         const int epi = d->mlp_act == MMDIT_ACT_SWIGLU ? MMDIT_EPI_SPLIT_SWIGLU : MMDIT_EPI_SPLIT_GELU;
@@ -354,6 +358,95 @@ int run_time_embed(const mmdit_dims* d, const mmdit_model* m, float t, float gui
     if (d->guidance_embed) {
         MMDIT_HIP(gemv(emb + 256, 256, m->guid_in[0], H, dt, 0, 0, tmp + H, s));
         MMDIT_HIP(gemv(tmp + H, H, m->guid_in[1], H, dt, 1, 1, vec, s));
+    }
+    return MMDIT_OK;
+}
+
+// Per-step modulation layout: [double b: txt 6H | img 6H] for every double
+// block, then [single b: 3H], then the final layer's [shift | scale] (2H).
+size_t mod_floats(const mmdit_dims* d) {
+    const size_t H = d->hidden;
+    return (size_t)d->n_double * 12 * H + (size_t)d->n_single * 3 * H + 2 * H;
+}
+size_t mod_double_off(const mmdit_dims* d, int b) { return (size_t)b * 12 * d->hidden; }
+size_t mod_single_off(const mmdit_dims* d, int b) {
+    return (size_t)d->n_double * 12 * d->hidden + (size_t)b * 3 * d->hidden;
+}
+size_t mod_final_off(const mmdit_dims* d) { return mod_floats(d) - 2 * (size_t)d->hidden; }
+
+struct ModBatchWs {
+    float* emb;      // [512]
+    float* tmp;      // [2H]
+    float* vecs;     // [n_steps, H]
+    uint16_t* a16;   // [n_steps, H] fp16 SiLU(vec)
+};
+
+ModBatchWs carve_modbatch(const mmdit_dims* d, int n_steps, Carver& c) {
+    const size_t H = d->hidden;
+    ModBatchWs w;
+    w.emb = c.take<float>(512);
+    w.tmp = c.take<float>(2 * H);
+    w.vecs = c.take<float>((size_t)n_steps * H);
+    w.a16 = c.take<uint16_t>((size_t)n_steps * H);
+    return w;
+}
+
+int model_ok(const mmdit_dims* d, const mmdit_model* m) {
+    if (!m) return MMDIT_E_NULL;
+    if (d->in_channels < 64 || d->in_channels % 64 != 0) return MMDIT_E_SHAPE;
+    if (d->n_double < 0 || d->n_single < 0) return MMDIT_E_SHAPE;
+    const int dt = d->weight_dtype;
+    MMDIT_TRY(check_linear(m->img_in, dt));
+    for (int i = 0; i < 2; ++i) {
+        MMDIT_TRY(check_linear(m->time_in[i], dt));
+        if (d->guidance_embed) MMDIT_TRY(check_linear(m->guid_in[i], dt));
+    }
+    MMDIT_TRY(check_linear(m->final_mod, dt));
+    MMDIT_TRY(check_linear(m->final_out, dt));
+    if (d->n_double > 0 && !m->doubles) return MMDIT_E_NULL;
+    if (d->n_single > 0 && !m->singles) return MMDIT_E_NULL;
+    for (int i = 0; i < d->n_double; ++i) MMDIT_TRY(double_weights_ok(&m->doubles[i], dt));
+    for (int i = 0; i < d->n_single; ++i) MMDIT_TRY(single_weights_ok(&m->singles[i], dt));
+    return MMDIT_OK;
+}
+
+// The step after validation. premod: this step's modulation (mod_floats
+// layout) or null to compute the conditioning and every modulation here.
+int run_step(const mmdit_dims* d, const mmdit_model* m, const float* premod, float* latent, const float* txt,
+             const float* rope, float t_cur, float t_next, float guidance, const StepWs& sw, hipStream_t s) {
+    const int Lt = d->txt_len, Li = d->img_len, H = d->hidden, C = d->in_channels, dt = d->weight_dtype;
+    const int Ln = Li - d->ref_len;   // noisy image rows; the rest is the reference latent
+    if (!premod) MMDIT_TRY(run_time_embed(d, m, t_cur, guidance, sw.vec, sw.emb, sw.tmp, s));
+    // x = [txt | img_in(latent)] (reference rows included)
+    MMDIT_HIP(launch_copy_f32(sw.x, txt, (int64_t)Lt * H, s));
+    {
+        const int64_t n = (int64_t)Li * C;
+        int64_t blocks = (n + 255) / 256;
+        if (blocks > 4096) blocks = 4096;
+        hipLaunchKernelGGL(f32_to_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, latent, sw.z16, n);
+        MMDIT_HIP(hipGetLastError());
+        GemmArgs g = gemm_base(H, C, dt, sw.z16, C, MMDIT_EPI_BIAS_F32, sw.x + (size_t)Lt * H, H);
+        MMDIT_HIP(gemm_1(g, group(0, Li, m->img_in), s));
+    }
+    Carver cb(sw.blocks);
+    const DoubleWs dws = carve_double(d, cb);
+    Carver cs(sw.blocks);
+    const SingleWs sws = carve_single(d, cs);
+    for (int i = 0; i < d->n_double; ++i)
+        MMDIT_TRY(run_double(d, &m->doubles[i], sw.vec, rope, sw.x, sw.x, dws, s,
+                             premod ? premod + mod_double_off(d, i) : nullptr));
+    for (int i = 0; i < d->n_single; ++i)
+        MMDIT_TRY(run_single(d, &m->singles[i], sw.vec, rope, sw.x, sw.x, sws, s,
+                             premod ? premod + mod_single_off(d, i) : nullptr));
+    // final layer on the noisy image rows, fused with the Euler update
+    const float* fmod = premod ? premod + mod_final_off(d) : sw.fmod;
+    if (!premod) MMDIT_HIP(gemv(sw.vec, H, m->final_mod, 2 * H, dt, 1, 0, sw.fmod, s));
+    MMDIT_HIP(launch_ln_modulate(sw.x + (size_t)Lt * H, Ln, H, 0, fmod, fmod + H, fmod, fmod + H, d->ln_eps,
+                                 dws.h, s));
+    {
+        GemmArgs g = gemm_base(C, H, dt, dws.h, H, MMDIT_EPI_EULER, latent, C);
+        g.alpha = t_next - t_cur;
+        MMDIT_HIP(gemm_1(g, group(0, Ln, m->final_out), s));
     }
     return MMDIT_OK;
 }
@@ -425,21 +518,7 @@ int mmdit_denoise_step(const mmdit_dims* d, const mmdit_model* m, float* latent,
                        const float* rope, float t_cur, float t_next, float guidance, void* ws,
                        size_t ws_bytes, hipStream_t s) {
     MMDIT_TRY(check_dims(d));
-    if (!m) return MMDIT_E_NULL;
-    if (d->in_channels < 64 || d->in_channels % 64 != 0) return MMDIT_E_SHAPE;
-    if (d->n_double < 0 || d->n_single < 0) return MMDIT_E_SHAPE;
-    const int dt = d->weight_dtype;
-    MMDIT_TRY(check_linear(m->img_in, dt));
-    for (int i = 0; i < 2; ++i) {
-        MMDIT_TRY(check_linear(m->time_in[i], dt));
-        if (d->guidance_embed) MMDIT_TRY(check_linear(m->guid_in[i], dt));
-    }
-    MMDIT_TRY(check_linear(m->final_mod, dt));
-    MMDIT_TRY(check_linear(m->final_out, dt));
-    if (d->n_double > 0 && !m->doubles) return MMDIT_E_NULL;
-    if (d->n_single > 0 && !m->singles) return MMDIT_E_NULL;
-    for (int i = 0; i < d->n_double; ++i) MMDIT_TRY(double_weights_ok(&m->doubles[i], dt));
-    for (int i = 0; i < d->n_single; ++i) MMDIT_TRY(single_weights_ok(&m->singles[i], dt));
+    MMDIT_TRY(model_ok(d, m));
     MMDIT_TRY(check_ptr(latent));
     MMDIT_TRY(check_ptr(txt));
     MMDIT_TRY(check_ptr(rope));
@@ -448,40 +527,71 @@ int mmdit_denoise_step(const mmdit_dims* d, const mmdit_model* m, float* latent,
     Carver c(ws);
     const StepWs sw = carve_step(d, c);
     if (ws_bytes < c.off) return MMDIT_E_WORKSPACE;
+    return run_step(d, m, nullptr, latent, txt, rope, t_cur, t_next, guidance, sw, s);
+}
 
-    const int Lt = d->txt_len, Li = d->img_len, L = Lt + Li, H = d->hidden, C = d->in_channels;
-    const int Ln = Li - d->ref_len;   // noisy image rows; the rest is the reference latent
-    MMDIT_TRY(run_time_embed(d, m, t_cur, guidance, sw.vec, sw.emb, sw.tmp, s));
-    // x = [txt | img_in(latent)] (reference rows included)
-    MMDIT_HIP(launch_copy_f32(sw.x, txt, (int64_t)Lt * H, s));
-    {
-        const int64_t n = (int64_t)Li * C;
-        int64_t blocks = (n + 255) / 256;
-        if (blocks > 4096) blocks = 4096;
-        hipLaunchKernelGGL(f32_to_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, latent, sw.z16, n);
-        MMDIT_HIP(hipGetLastError());
-        GemmArgs g = gemm_base(H, C, dt, sw.z16, C, MMDIT_EPI_BIAS_F32, sw.x + (size_t)Lt * H, H);
-        MMDIT_HIP(gemm_1(g, group(0, Li, m->img_in), s));
+size_t mmdit_modulation_floats(const mmdit_dims* d) {
+    if (check_dims(d) != MMDIT_OK || d->n_double < 0 || d->n_single < 0) return 0;
+    return mod_floats(d);
+}
+
+size_t mmdit_modulation_workspace_bytes(const mmdit_dims* d, int n_steps) {
+    if (check_dims(d) != MMDIT_OK || n_steps < 1 || n_steps > MMDIT_MAX_BATCH_STEPS) return 0;
+    Carver c(nullptr);
+    carve_modbatch(d, n_steps, c);
+    return c.off;
+}
+
+int mmdit_modulation_batch(const mmdit_dims* d, const mmdit_model* m, const float* t, int n_steps,
+                           float guidance, float* mod, void* ws, size_t ws_bytes, hipStream_t s) {
+    MMDIT_TRY(check_dims(d));
+    MMDIT_TRY(model_ok(d, m));
+    if (!t) return MMDIT_E_NULL;
+    if (n_steps < 1 || n_steps > MMDIT_MAX_BATCH_STEPS) return MMDIT_E_SHAPE;
+    for (int i = 0; i < n_steps; ++i)
+        if (!std::isfinite(t[i])) return MMDIT_E_ARG;
+    if (!std::isfinite(guidance)) return MMDIT_E_ARG;
+    MMDIT_TRY(check_ptr(mod));
+    MMDIT_TRY(check_ptr(ws));
+    Carver c(ws);
+    const ModBatchWs w = carve_modbatch(d, n_steps, c);
+    if (ws_bytes < c.off) return MMDIT_E_WORKSPACE;
+    const int H = d->hidden, dt = d->weight_dtype;
+    const int ld = (int)mod_floats(d);
+    // conditioning vectors of every step, then SiLU(vec) as the fp16 operand
+    for (int i = 0; i < n_steps; ++i)
+        MMDIT_TRY(run_time_embed(d, m, t[i], guidance, w.vecs + (size_t)i * H, w.emb, w.tmp, s));
+    MMDIT_HIP(launch_silu_to_f16(w.vecs, w.a16, (int64_t)n_steps * H, s));
+    // one GEMM per modulation linear over all steps: each weight is read once
+    auto mod_gemm = [&](const mmdit_linear& l, int n, size_t off) -> int {
+        GemmArgs g = gemm_base(n, H, dt, w.a16, H, MMDIT_EPI_BIAS_F32, mod + off, ld);
+        MMDIT_HIP(gemm_1(g, group(0, n_steps, l), s));
+        return MMDIT_OK;
+    };
+    for (int b = 0; b < d->n_double; ++b) {
+        MMDIT_TRY(mod_gemm(m->doubles[b].txt.mod, 6 * H, mod_double_off(d, b)));
+        MMDIT_TRY(mod_gemm(m->doubles[b].img.mod, 6 * H, mod_double_off(d, b) + 6 * (size_t)H));
     }
-    Carver cb(sw.blocks);
-    const DoubleWs dws = carve_double(d, cb);
-    Carver cs(sw.blocks);
-    const SingleWs sws = carve_single(d, cs);
-    for (int i = 0; i < d->n_double; ++i)
-        MMDIT_TRY(run_double(d, &m->doubles[i], sw.vec, rope, sw.x, sw.x, dws, s));
-    for (int i = 0; i < d->n_single; ++i)
-        MMDIT_TRY(run_single(d, &m->singles[i], sw.vec, rope, sw.x, sw.x, sws, s));
-    // final layer on the noisy image rows, fused with the Euler update
-    MMDIT_HIP(gemv(sw.vec, H, m->final_mod, 2 * H, dt, 1, 0, sw.fmod, s));
-    MMDIT_HIP(launch_ln_modulate(sw.x + (size_t)Lt * H, Ln, H, 0, sw.fmod, sw.fmod + H, sw.fmod,
-                                 sw.fmod + H, d->ln_eps, dws.h, s));
-    {
-        GemmArgs g = gemm_base(C, H, dt, dws.h, H, MMDIT_EPI_EULER, latent, C);
-        g.alpha = t_next - t_cur;
-        MMDIT_HIP(gemm_1(g, group(0, Ln, m->final_out), s));
-    }
-    (void)L;
+    for (int b = 0; b < d->n_single; ++b) MMDIT_TRY(mod_gemm(m->singles[b].mod, 3 * H, mod_single_off(d, b)));
+    MMDIT_TRY(mod_gemm(m->final_mod, 2 * H, mod_final_off(d)));
     return MMDIT_OK;
+}
+
+int mmdit_denoise_step_premod(const mmdit_dims* d, const mmdit_model* m, const float* mod, float* latent,
+                              const float* txt, const float* rope, float t_cur, float t_next, void* ws,
+                              size_t ws_bytes, hipStream_t s) {
+    MMDIT_TRY(check_dims(d));
+    MMDIT_TRY(model_ok(d, m));
+    MMDIT_TRY(check_ptr(mod));
+    MMDIT_TRY(check_ptr(latent));
+    MMDIT_TRY(check_ptr(txt));
+    MMDIT_TRY(check_ptr(rope));
+    MMDIT_TRY(check_ptr(ws));
+    if (!std::isfinite(t_cur) || !std::isfinite(t_next)) return MMDIT_E_ARG;
+    Carver c(ws);
+    const StepWs sw = carve_step(d, c);
+    if (ws_bytes < c.off) return MMDIT_E_WORKSPACE;
+    return run_step(d, m, mod, latent, txt, rope, t_cur, t_next, 0.f, sw, s);
 }
 
 int mmdit_rope_table(const mmdit_dims* d, const int32_t* ids, float* rope, hipStream_t s) {

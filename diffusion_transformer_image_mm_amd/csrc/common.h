@@ -154,4 +154,7 @@ hipError_t launch_rope_table(const int32_t* ids, int seq_len, int head_dim, int 
 
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t s);
 
+// y fp16 = SiLU(x fp32), n elements
+hipError_t launch_silu_to_f16(const float* x, uint16_t* y, int64_t n, hipStream_t s);
+
 }  // namespace mmdit

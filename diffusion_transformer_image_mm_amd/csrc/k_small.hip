@@ -228,6 +228,23 @@ hipError_t launch_rope_table(const int32_t* ids, int seq_len, int head_dim, int 
 }
 
 // ---------------------------------------------------------------------------
+// out fp16 [rows, n] = SiLU(x fp32 [rows, n]): the activation operand of the
+// modulation linears when they run as one GEMM over many conditioning vectors
+// ---------------------------------------------------------------------------
+__global__ void silu_to_f16_kernel(const float* __restrict__ x, uint16_t* __restrict__ y, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        y[i] = f2h(silu(x[i]));
+}
+
+hipError_t launch_silu_to_f16(const float* x, uint16_t* y, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(silu_to_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, y, n);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 __global__ void copy_f32_kernel(float* __restrict__ dst, const float* __restrict__ src, int64_t n4) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x)
         reinterpret_cast<float4*>(dst)[i] = reinterpret_cast<const float4*>(src)[i];

@@ -248,6 +248,44 @@ int mmdit_denoise_step(const mmdit_dims* dims, const mmdit_model* model,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Modulation of every block for many denoise steps at once. The conditioning
+ * vector depends only on the step's time (and the guidance value), not on
+ * the latent, so the modulation of all blocks for all steps of a sampling
+ * run is known before the first step; computed here as one GEMM per
+ * modulation linear over all steps, each weight is read once per run instead
+ * of once per step (Luminal blog, "Where the time goes on the MI300X": the
+ * glue kernels; the modulations are 226 MB of weights per FLUX double block).
+ *   t:   HOST array of n_steps step times (1 <= n_steps <= MMDIT_MAX_BATCH_STEPS)
+ *   mod: fp32 [n_steps, mmdit_modulation_floats(dims)]; row i holds, for step
+ *        i: per double block [txt 6H | img 6H], then per single block [3H],
+ *        then the final layer's [shift | scale] (2H), chunk orders as in the
+ *        weight structs
+ *   ws:  at least mmdit_modulation_workspace_bytes(dims, n_steps)
+ * The conditioning vectors are computed in fp32 as in mmdit_denoise_step;
+ * SiLU(vec) enters the matrix cores as fp16 (the per-step path keeps it fp32
+ * in its GEMV), a relative rounding of at most 2^-11 per element.
+ */
+#define MMDIT_MAX_BATCH_STEPS 256
+size_t mmdit_modulation_floats(const mmdit_dims* dims);
+size_t mmdit_modulation_workspace_bytes(const mmdit_dims* dims, int n_steps);
+int mmdit_modulation_batch(const mmdit_dims* dims, const mmdit_model* model,
+                           const float* t, int n_steps, float guidance,
+                           float* mod, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * mmdit_denoise_step with the modulation given: mod is this step's row of
+ * mmdit_modulation_batch (fp32 [mmdit_modulation_floats(dims)], device). No
+ * conditioning vector and no modulation GEMV is computed; everything else is
+ * as in mmdit_denoise_step (same workspace, MMDIT_WS_STEP). The launch
+ * sequence is fixed for fixed dims, pointers and times, and enqueues no
+ * memory fills, so a caller may capture it in a HIP graph.
+ */
+int mmdit_denoise_step_premod(const mmdit_dims* dims, const mmdit_model* model,
+                              const float* mod, float* latent, const float* txt,
+                              const float* rope, float t_cur, float t_next,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * RoPE table from axial position ids: ids int32 [L, 3] (t, h, w) on the
  * device; rope fp32 [L, D/2, 2]. Pair p of the head dim belongs to axis a
  * (consecutive segments of rope_axes[0], [1], [2] dims); its j-th pair in

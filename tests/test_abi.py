@@ -113,6 +113,37 @@ def test_single_and_step_validation():
     assert B.mmdit_denoise_step(d, m, FAKE, FAKE, FAKE, 1.0, 0.9, 3.5, FAKE, need - 1) == B.MMDIT_E_WORKSPACE
 
 
+def test_modulation_batch_and_premod_validation():
+    d = _dims()
+    H = d.hidden
+    d.n_double, d.n_single = 2, 3
+    assert B.mmdit_modulation_floats(d) == 2 * 12 * H + 3 * 3 * H + 2 * H
+    assert B.mmdit_modulation_workspace_bytes(d, 0) == 0
+    assert B.mmdit_modulation_workspace_bytes(d, 257) == 0
+    need = B.mmdit_modulation_workspace_bytes(d, 28)
+    assert need > 0
+    m = B.mmdit_model()
+    for f in ("img_in", "final_mod", "final_out"):
+        setattr(m, f, _linear())
+    for i in range(2):
+        m.time_in[i] = _linear()
+        m.guid_in[i] = _linear()
+    doubles = (B.mmdit_double_weights * 2)(_double(), _double())
+    singles = (B.mmdit_single_weights * 3)(*[B.mmdit_single_weights(_linear(), _linear(), _linear(), FAKE, FAKE)
+                                             for _ in range(3)])
+    m.doubles, m.singles = doubles, singles
+    ts = [1.0 - i / 28 for i in range(28)]
+    assert B.mmdit_modulation_batch(d, m, [], 3.5, FAKE, FAKE, need) == B.MMDIT_E_SHAPE
+    assert B.mmdit_modulation_batch(d, m, ts[:3] + [float("inf")], 3.5, FAKE, FAKE, need) == B.MMDIT_E_ARG
+    assert B.mmdit_modulation_batch(d, m, ts, 3.5, FAKE + 4, FAKE, need) == B.MMDIT_E_ALIGN
+    assert B.mmdit_modulation_batch(d, m, ts, 3.5, FAKE, FAKE, need - 1) == B.MMDIT_E_WORKSPACE
+    step_ws = B.mmdit_workspace_bytes(d, B.MMDIT_WS_STEP)
+    assert B.mmdit_denoise_step_premod(d, m, 0, FAKE, FAKE, FAKE, 1.0, 0.9, FAKE, step_ws) == B.MMDIT_E_NULL
+    assert B.mmdit_denoise_step_premod(d, m, FAKE, FAKE, FAKE, FAKE, 1.0, float("nan"), FAKE, step_ws) == B.MMDIT_E_ARG
+    assert B.mmdit_denoise_step_premod(d, m, FAKE, FAKE, FAKE, FAKE, 1.0, 0.9, FAKE, step_ws - 1) == \
+        B.MMDIT_E_WORKSPACE
+
+
 def test_kernel_entry_validation():
     assert B.mmdit_k_ln_modulate(FAKE, 10, 100, 0, FAKE, FAKE, FAKE, FAKE, 1e-6, FAKE) == B.MMDIT_E_SHAPE
     assert B.mmdit_k_ln_modulate(FAKE, 10, 256, 0, FAKE, FAKE, FAKE, FAKE, 0.0, FAKE) == B.MMDIT_E_ARG
