@@ -122,6 +122,11 @@ struct GemmArgs {
     float alpha;
     int ngroups;
     GemmGroup g[2];
+    // Set by the launcher: the last tail_rows row tiles (of both groups'
+    // row tiles stacked) run as 128-wide tiles after the full_tiles 256-wide
+    // ones, so that a partial last round of 256-wide tiles becomes half as long.
+    int tail_rows;
+    int full_tiles;
 };
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);

@@ -43,6 +43,11 @@
 //   fragment reads of one k-substep with the MFMAs of the other;
 // * grouped launch: up to two weight sets (text / image stream) over
 //   disjoint row ranges in one grid; tiles are laid out per XCD (tile_of);
+// * tail tiles: when the last round of 256-wide tiles would occupy at most
+//   half of the compute units (the FLUX MLP-in projection: 864 tiles = 3
+//   rounds + 96), the last row tiles run as 128-wide tiles in the same
+//   launch (768 + 192 tiles: the last round becomes half as long); every
+//   output element sees the same k-order either way (bit-identical);
 // * SwiGLU epilogues (a gated MLP, Luminal blog section "What the compiler
 //   found on its own": the fused SwiGLU activation of Flux.2 Klein): the
 //   weight keeps its natural layout, rows [gate (M) | up (M)]. A tile covers
@@ -58,7 +63,7 @@ namespace mmdit {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 256, BN = 256, BK = 64;   // BN: the full tile; tail tiles are BN / 2 wide
 constexpr int PIPE_MIN_K = 8192;   // contractions at least this long use the pipelined loop
 constexpr int NTHREADS = 512;
 constexpr int A_TILE_BYTES = BM * BK * 2;   // 32 KB
@@ -134,21 +139,21 @@ struct TileCoord {
 // the strips, so no XCD streams a whole text-stream weight matrix alone.
 constexpr int RASTER_ROWS = 6;
 
-MMDIT_DEV TileCoord tile_of(const GemmArgs& a, int bid, int total) {
+// The grid covers row tiles [rt0, rt0 + tmt) of the stacked list.
+MMDIT_DEV TileCoord tile_of(const GemmArgs& a, int bid, int total, int bn, int rt0, int tmt) {
     const int x = bid & 7, j = bid >> 3, q = total >> 3, r = total & 7;
     const int idx = x * q + (x < r ? x : r) + j;   // a bijection on [0, total)
-    const int tn = (a.n + BN - 1) / BN;
+    const int tn = (a.n + bn - 1) / bn;
     const int tm0 = (a.g[0].m + BM - 1) / BM;
-    const int tmt = a.ngroups == 2 ? tm0 + (a.g[1].m + BM - 1) / BM : tm0;
     const int cs = (tn % 8 == 0) ? 8 : (tn % 4 == 0) ? 4 : (tn % 2 == 0) ? 2 : 1;
     const int cols = tn / cs;
     const int strip = idx / (tmt * cols), in_strip = idx - strip * tmt * cols;
     const int band = in_strip / (RASTER_ROWS * cols), rem = in_strip - band * RASTER_ROWS * cols;
     const int r0 = band * RASTER_ROWS;
     const int rows = (tmt - r0) < RASTER_ROWS ? (tmt - r0) : RASTER_ROWS;
-    int mt = r0 + rem % rows;
+    int mt = rt0 + r0 + rem % rows;
     TileCoord c;
-    c.n0 = (strip * cols + rem / rows) * BN;
+    c.n0 = (strip * cols + rem / rows) * bn;
     if (a.ngroups == 1 || mt < tm0) {
         c.g = 0;
     } else {
@@ -172,24 +177,29 @@ MMDIT_DEV int weight_row(int v, int swiglu_from, int half) {
 
 }  // namespace
 
-template <int WT, int EPI, int PIPE>
-__global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) {
+// One output tile. TNW: MFMA sub-tiles per wavefront along n, 4 (the
+// 256-wide tile) or 2 (a 128-wide tail tile). The grid's tiles of this width
+// are numbered bid in [0, total) over row tiles [rt0, rt0 + tmt).
+template <int WT, int EPI, int PIPE, int TNW>
+MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, int rt0, int tmt) {
     constexpr bool INT8 = WT == MMDIT_INT8;
     constexpr bool F16W = WT == MMDIT_F16;
+    constexpr bool SWIGLU = EPI == MMDIT_EPI_SWIGLU || EPI == MMDIT_EPI_SPLIT_SWIGLU;
     static_assert(PIPE == 0 || F16W, "the pipelined main loop reads plain fp16 weight fragments");
-    extern __shared__ __attribute__((aligned(1024))) char smem[];
-    constexpr int W_TILE = INT8 ? W_TILE_BYTES_I8 : W_TILE_BYTES_BF16;   // fp16: as bf16
+    static_assert(TNW == 4 || (TNW == 2 && PIPE == 0 && !SWIGLU), "tail tiles: plain loop, no SwiGLU");
+    constexpr int BNT = 64 * TNW;                                 // tile width (output columns)
+    constexpr int W_TILE = BNT * BK * (INT8 ? 1 : 2);             // fp16 weights: as bf16
     constexpr int STAGE = A_TILE_BYTES + W_TILE;
-    constexpr int TM = 8, TN = 4;   // MFMA sub-tiles per wavefront (m, n)
+    constexpr int TM = 8, TN = TNW;   // MFMA sub-tiles per wavefront (m, n)
+    constexpr int WL = TNW, WL8 = TNW / 2;   // W loads per wavefront per stage (16-bit, int8)
     // stage s: A tile at smem + s*STAGE, W tile right after it
 
-    const TileCoord tc = tile_of(args, blockIdx.x, gridDim.x);
+    const TileCoord tc = tile_of(args, bid, total, BNT, rt0, tmt);
     const GemmGroup& G = args.g[tc.g];
     const int M = G.m, N = args.n, K = args.k;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;
-    constexpr bool SWIGLU = EPI == MMDIT_EPI_SWIGLU || EPI == MMDIT_EPI_SPLIT_SWIGLU;
     // SwiGLU columns start at sw_from (0, or split_n for the split epilogue);
     // sw_half = M, the number of features
     const int sw_from = EPI == MMDIT_EPI_SPLIT_SWIGLU ? args.split_n : 0;
@@ -215,11 +225,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) 
     // units of 16 codes; a load covers 16 rows (lane i: row (2w + j)*16 +
     // i/4, position i%4); unit u of row r is stored at position u ^ ((r >> 2) & 3).
     const char* w_g = static_cast<const char*>(G.w);
-    uint32_t w_off_g[4];
+    uint32_t w_off_g[WL];
     if (!INT8) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = (wave * 4 + j) * 8 + lrow;
+        for (int j = 0; j < WL; ++j) {
+            const int r = (wave * WL + j) * 8 + lrow;
             const int c = lpos ^ ((r >> 1) & 7);
             int gn = tc.n0 + r;
             gn = gn < N ? gn : N - 1;
@@ -228,8 +238,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) 
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int r = (wave * 2 + j) * 16 + (lane >> 2);
+        for (int j = 0; j < WL8; ++j) {
+            const int r = (wave * WL8 + j) * 16 + (lane >> 2);
             const int u = (lane & 3) ^ ((r >> 2) & 3);
             int gn = tc.n0 + r;
             gn = gn < N ? gn : N - 1;
@@ -251,13 +261,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) 
         char* wb = base + A_TILE_BYTES;
         if (!INT8) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                dma(w_g + (w_off_g[j] + ka), (lds_void*)(wb + ((wave * 4 + j) * 8) * 128));
+            for (int j = 0; j < WL; ++j)
+                dma(w_g + (w_off_g[j] + ka), (lds_void*)(wb + ((wave * WL + j) * 8) * 128));
         } else {
             const uint32_t kw = (uint32_t)kt * BK;
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                g2l_16(w_g + (w_off_g[j] + kw), (lds_void*)(wb + ((wave * 2 + j) * 16) * 64));
+            for (int j = 0; j < WL8; ++j)
+                g2l_16(w_g + (w_off_g[j] + kw), (lds_void*)(wb + ((wave * WL8 + j) * 16) * 64));
         }
     };
 
@@ -270,9 +280,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) 
         const int c = ks * 4 + lg;
         a_off[ks] = (wm * 128 + lr) * 128 + ((c ^ ((lr >> 1) & 7)) * 16);
         if (!INT8)
-            w_off[ks] = (wn * 64 + lr) * 128 + ((c ^ ((lr >> 1) & 7)) * 16);
+            w_off[ks] = (wn * 16 * TNW + lr) * 128 + ((c ^ ((lr >> 1) & 7)) * 16);
         else
-            w_off[ks] = (wn * 64 + lr) * 64 + (((c >> 1) ^ ((lr >> 2) & 3)) * 16) + (c & 1) * 8;
+            w_off[ks] = (wn * 16 * TNW + lr) * 64 + (((c >> 1) ^ ((lr >> 2) & 3)) * 16) + (c & 1) * 8;
     }
 
     f32x4_t acc[TN][TM];
@@ -371,8 +381,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) 
     }
 
     // ---- epilogue. acc[in][im] element j: output column
-    // n = n0 + wn*64 + in*16 + lg*4 + j, row m = m0 + wm*128 + im*16 + lr.
-    const int nb = tc.n0 + wn * 64 + lg * 4;
+    // n = n0 + wn*16*TNW + in*16 + lg*4 + j, row m = m0 + wm*128 + im*16 + lr.
+    const int nb = tc.n0 + wn * 16 * TNW + lg * 4;
     const int mb = tc.m0 + wm * 128 + lr;
     if (SWIGLU && tc.n0 >= sw_from) {
         // accumulators in = 0, 1 hold gate, in = 2, 3 up of the same features
@@ -474,18 +484,67 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) 
     }
 }
 
+template <int WT, int EPI, int PIPE>
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) {
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    constexpr bool SWIGLU = EPI == MMDIT_EPI_SWIGLU || EPI == MMDIT_EPI_SPLIT_SWIGLU;
+    const int tm0 = (args.g[0].m + BM - 1) / BM;
+    const int tmt = args.ngroups == 2 ? tm0 + (args.g[1].m + BM - 1) / BM : tm0;
+    const int nf = args.full_tiles;
+    if constexpr (!SWIGLU && PIPE == 0) {
+        if ((int)blockIdx.x >= nf) {
+            gemm_tile<WT, EPI, 0, 2>(args, smem, blockIdx.x - nf, gridDim.x - nf, tmt - args.tail_rows,
+                                     args.tail_rows);
+            return;
+        }
+    }
+    gemm_tile<WT, EPI, PIPE, 4>(args, smem, blockIdx.x, nf, 0, tmt - args.tail_rows);
+}
+
+// Compute units of the current device (queried once per device).
+static int cu_count() {
+    static int cached[16] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 template <int WT>
-static hipError_t launch_gemm_t(const GemmArgs& a, hipStream_t s) {
+static hipError_t launch_gemm_t(const GemmArgs& a0, hipStream_t s) {
     constexpr bool INT8 = WT == MMDIT_INT8;
+    GemmArgs a = a0;
     const int tn = (a.n + BN - 1) / BN;
-    int tiles = 0;
-    for (int g = 0; g < a.ngroups; ++g) tiles += ((a.g[g].m + BM - 1) / BM) * tn;
-    if (tiles == 0) return hipSuccess;
-    const size_t lds = 2 * (size_t)(A_TILE_BYTES + (INT8 ? W_TILE_BYTES_I8 : W_TILE_BYTES_BF16));
-    dim3 grid(tiles), block(NTHREADS);
+    int tmt = 0;
+    for (int g = 0; g < a.ngroups; ++g) tmt += (a.g[g].m + BM - 1) / BM;
+    if (tmt == 0 || tn == 0) return hipSuccess;
+    const bool swiglu = a.epilogue == MMDIT_EPI_SWIGLU || a.epilogue == MMDIT_EPI_SPLIT_SWIGLU;
     // The pipelined loop pays off on long contractions (measured: +10% at
     // K = 12288, +3% at K = 15360, -1% to 0 at K = 3072).
     const bool pipe = WT == MMDIT_F16 && a.k >= PIPE_MIN_K;
+    // Tail tiles: when the last round of 256-wide tiles would fill at most
+    // half of the compute units, and the last r row tiles can be cut off so
+    // that the rest fills whole rounds, those r row tiles run as 128-wide
+    // tiles instead (twice as many, each half as long).
+    const int cus = cu_count();
+    a.tail_rows = 0;
+    if (!swiglu && !pipe && (tmt * tn) % cus != 0 && (tmt * tn) % cus <= cus / 2) {
+        const int tn2 = (a.n + BN / 2 - 1) / (BN / 2);
+        for (int r = 1; r < tmt; ++r) {
+            if (((tmt - r) * tn) % cus == 0 && r * tn2 <= cus) {
+                a.tail_rows = r;
+                break;
+            }
+        }
+    }
+    a.full_tiles = (tmt - a.tail_rows) * tn;
+    const int tiles = a.full_tiles + a.tail_rows * ((a.n + BN / 2 - 1) / (BN / 2));
+    const size_t lds = 2 * (size_t)(A_TILE_BYTES + (INT8 ? W_TILE_BYTES_I8 : W_TILE_BYTES_BF16));
+    dim3 grid(tiles), block(NTHREADS);
 #define GEMM_CASE(E)                                                                        \
     case E: {                                                                               \
         auto kfn = pipe ? gemm_kernel<WT, E, (WT == MMDIT_F16 ? 1 : 0)> : gemm_kernel<WT, E, 0>; \

@@ -343,6 +343,68 @@ def test_gemm_swiglu_klein_size_sampled_rows(m, n, k, epi):
     assert _gemm_err(g, ref, epi, k) <= TOL
 
 
+@pytest.mark.parametrize("n,k,epi,wt", [(4032, 256, B.MMDIT_EPI_BIAS, "bf16"), (4096, 320, B.MMDIT_EPI_GATE_RESID, "int8"),
+                                       (4096, 256, B.MMDIT_EPI_BIAS_GELU, "f16"),
+                                       (4032, 192, B.MMDIT_EPI_SPLIT_GELU, "bf16"),
+                                       (4096, 128, B.MMDIT_EPI_EULER, "f16")])
+def test_gemm_tail_tiles(n, k, epi, wt):
+    """4400 rows = 18 row tiles x 16 column tiles = 288 tiles: the last two
+    row tiles run as 128-wide tail tiles (as in the FLUX MLP-in projection).
+    Against the oracle on every element, and bit for bit against the same
+    product computed as two calls (rows 0-4095 and 4096-4399) that use
+    256-wide tiles only: the tile width does not change any element's sums."""
+    say(f"gemm tail tiles m=4400 n={n} k={k} epi={epi} weights={wt}")
+    m = 4400
+    g, ref = _run_gemm(m, n, k, epi, wt == "int8", tid=130, f16=wt == "f16")
+    assert _gemm_err(g, ref, epi, k) <= TOL
+    A = DeviceArena(f16_weights=wt == "f16")
+    a = synth.f16_exact(rnd(130, (m, k)))
+    lin = _lin(132, n, k, wt == "int8")
+    da = A.f16(a)
+    wl = A.linear(lin)
+    wtype = B.MMDIT_INT8 if wt == "int8" else (B.MMDIT_F16 if wt == "f16" else B.MMDIT_BF16)
+    f32out = epi in (B.MMDIT_EPI_GATE_RESID, B.MMDIT_EPI_BIAS_F32, B.MMDIT_EPI_EULER)
+    split = _SPLIT[0]
+    outs = []
+    for rows in ((0, m), (0, 4096), (4096, m)):
+        r0, r1 = rows
+        gate = rnd(135, (n,), 0.7)
+        resid = rnd(136, (m, n))
+        if f32out:
+            out = A.f32(resid) if epi == B.MMDIT_EPI_EULER else A.empty_f32(m, n)
+        else:
+            out = A.empty_f16(m, split) if epi == B.MMDIT_EPI_BIAS_GELU else A.empty_bf16(m, split)
+        outs.append(out)
+    full, part = outs[0], outs[1]
+    for (r0, r1), out in (((0, m), full), ((0, 4096), part), ((4096, m), part)):
+        gm = B.mmdit_gemm(m=r1 - r0, n=n, k=k, weight_dtype=wtype, a=da[r0:].data_ptr(), lda=k, w=wl, epilogue=epi)
+        f32 = out.dtype == torch.float32
+        gm.out, gm.ldo = out[r0:].data_ptr(), (n if f32 else split)
+        out2 = None
+        if epi == B.MMDIT_EPI_GATE_RESID:
+            gr = A.f32(rnd(135, (n,), 0.7))
+            rs = A.f32(rnd(136, (m, n)))
+            gm.gate, gm.resid, gm.ldr = gr.data_ptr(), rs[r0:].data_ptr(), n
+        if epi == B.MMDIT_EPI_SPLIT_GELU:
+            key = "o2_full" if out is full else "o2_part"
+            if key not in _O2:
+                _O2[key] = A.empty_f16(m, 64 + n - split)
+            out2 = _O2[key]
+            gm.split_n, gm.out2, gm.ldo2, gm.out2_col = split, out2[r0:].data_ptr(), 64 + n - split, 64
+        if epi == B.MMDIT_EPI_EULER:
+            gm.alpha = -1.0 / 28
+        B.check(B.mmdit_k_gemm(gm, stream()))
+    sync()
+    np.testing.assert_array_equal(to_numpy_f32(full), to_numpy_f32(part))
+    if epi == B.MMDIT_EPI_SPLIT_GELU:
+        # columns 0-63 of out2 are never written (out2_col = 64)
+        np.testing.assert_array_equal(to_numpy_f32(_O2["o2_full"])[:, 64:], to_numpy_f32(_O2["o2_part"])[:, 64:])
+    _O2.clear()
+
+
+_O2 = {}
+
+
 def test_gemm_int8_rerun_bit_exact():
     say("gemm int8 rerun")
     a1, _ = _run_gemm(700, 256, 1024, B.MMDIT_EPI_GATE_RESID, True, tid=70)
