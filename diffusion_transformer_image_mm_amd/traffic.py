@@ -10,8 +10,9 @@ times and then copies 1 GiB device-to-device three times):
 ``python -m diffusion_transformer_image_mm_amd.traffic gpurun_out/pmc_fetch
 gpurun_out/pmc_write`` then writes the summary that bench.py reads. Each
 counter (KiB per dispatch) is scaled by expected/measured for the copy of
-known size, and the result is tied to the SHA-256 of the kernel's source:
-once the source changes, bench.py reports the traffic as unknown (null).
+known size, and the result is tied to the SHA-256 of the kernel's sources
+(k_gemm.hip and common.h): once they change, bench.py reports the traffic as
+unknown (null).
 """
 from __future__ import annotations
 
@@ -23,7 +24,8 @@ import statistics
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-KERNEL_SOURCE = os.path.join(ROOT, "diffusion_transformer_image_mm_amd", "csrc", "k_gemm.hip")
+# the kernel's source and the header whose device helpers it inlines
+KERNEL_SOURCES = [os.path.join(ROOT, "diffusion_transformer_image_mm_amd", "csrc", f) for f in ("k_gemm.hip", "common.h")]
 SUMMARY = os.path.join(ROOT, "profiles", "gemm_mlp_in_flux_traffic.txt")
 KERNEL_MATCH = "gemm_kernel<2, 1, 0>"       # fp16 weights, bias + GELU epilogue, plain loop
 COPY_MATCH = "__amd_rocclr_copyBuffer"
@@ -31,8 +33,11 @@ COPY_KIB = 1 << 20                            # the probe copies 1 GiB
 
 
 def source_sha256() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def _values(run_dir: str, match: str):
