@@ -285,3 +285,53 @@ def test_modulation_batch_and_premod_steps(shape, wt):
     say(f"  {n_steps} premod steps: rel_err(z)={e:.3e} rel_err(z - z0)={ev:.3e}")
     assert e <= TOL and ev <= TOL, (e, ev)
     np.testing.assert_array_equal(run(), g1)
+
+
+def test_premod_step_graph_capture_replays_match_eager():
+    """A premodulated step is a fixed launch sequence without memory fills,
+    so it can be captured in a HIP graph: every replay (with eager work and
+    synchronisations in between) equals the eager step bit for bit."""
+    import torch
+    say("premod step HIP graph capture")
+    shape = STEP
+    m = synth.model_weights(shape, int8=False)
+    s = synth.step_inputs(shape)
+    A = DeviceArena(f16_weights=True)
+    d = dims_for(shape, False, True)
+    mm = A.model(m)
+    rope = _rope(A, d, shape)
+    ts = synth.sigma_schedule(4)
+    nf = B.mmdit_modulation_floats(d)
+    mod = A.empty_f32(2, nf)
+    mws = A.workspace(B.mmdit_modulation_workspace_bytes(d, 2))
+    B.check(B.mmdit_modulation_batch(d, mm, ts[:2], 3.5, mod, mws, mws.numel(), stream()), "modbatch")
+    ws = A.workspace(B.mmdit_workspace_bytes(d, B.MMDIT_WS_STEP))
+    txt = A.f32(s["txt"])
+    z0 = A.f32(s["z"])
+    z = A.f32(s["z"])
+
+    def two_steps(st):
+        for i in range(2):
+            B.check(B.mmdit_denoise_step_premod(d, mm, mod[i], z, txt, rope, ts[i], ts[i + 1], ws, ws.numel(), st),
+                    "premod step")
+
+    two_steps(stream())              # eager (also sets every kernel attribute before capture)
+    sync()
+    eager = z.cpu().numpy()
+    z.copy_(z0)
+    sync()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            two_steps(cap)
+    torch.cuda.current_stream().wait_stream(cap)
+    sync()
+    for rep in range(3):
+        z.copy_(z0)                   # eager work between replays
+        sync()
+        graph.replay()
+        sync()
+        np.testing.assert_array_equal(z.cpu().numpy(), eager, err_msg=f"replay {rep}")
+    del graph
