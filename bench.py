@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, published
 PEAK_HBM_GBS = 8000.0
 
 
@@ -196,6 +197,40 @@ def main() -> int:
     gemm_tflops = gemm_flops / (ms_gemm * 1e-3) / 1e12
     log(f"bench: fc1 GEMM {L}x{M}x{H} {ms_gemm * 1e3:.1f} us -> {gemm_tflops:.1f} TFLOP/s")
 
+    # ------------------------------------------------------------ fp8 MLP-in GEMM (OCP e4m3 operands)
+    a8 = torch.zeros(L, H, dtype=torch.uint8, device="cuda")
+    as8 = torch.empty(L, dtype=torch.float32, device="cuda")
+    w8 = torch.zeros(M, H, dtype=torch.uint8, device="cuda")
+    ws8 = torch.empty(M, dtype=torch.float32, device="cuda")
+    a_src = torch.randn(L, H, generator=torch.Generator(device="cuda").manual_seed(5), device="cuda").to(torch.float16)
+    w_src = (torch.randn(M, H, generator=torch.Generator(device="cuda").manual_seed(6), device="cuda") * 0.02
+             ).to(torch.bfloat16)
+    B.check(B.mmdit_quantize_fp8_rows(w_src, B.MMDIT_BF16, M, H, H, w8, H, ws8, stream), "quantize w")
+    B.check(B.mmdit_quantize_fp8_rows(a_src, B.MMDIT_F16, L, H, H, a8, H, as8, stream), "quantize a")
+    g8 = B.mmdit_gemm(m=L, n=M, k=H, weight_dtype=B.MMDIT_FP8, a=a8.data_ptr(), lda=H,
+                      w=B.mmdit_linear(w8.data_ptr(), ws8.data_ptr(), w.img.fc1.bias), epilogue=B.MMDIT_EPI_BIAS_GELU,
+                      out=a_out.data_ptr(), ldo=M)
+    g8.a_scale = as8.data_ptr()
+    for _ in range(3):
+        B.check(B.mmdit_k_gemm(g8, stream), "gemm fp8")
+    torch.cuda.synchronize()
+    g0.record(stream)
+    for _ in range(n_g):
+        B.check(B.mmdit_k_gemm(g8, stream), "gemm fp8")
+    g1.record(stream)
+    torch.cuda.synchronize()
+    ms_g8 = g0.elapsed_time(g1) / n_g
+    g0.record(stream)
+    for _ in range(n_g):
+        B.check(B.mmdit_quantize_fp8_rows(a_src, B.MMDIT_F16, L, H, H, a8, H, as8, stream), "quantize a")
+    g1.record(stream)
+    torch.cuda.synchronize()
+    ms_q8 = g0.elapsed_time(g1) / n_g
+    tf8 = gemm_flops / (ms_g8 * 1e-3) / 1e12
+    log(f"bench: fp8 fc1 GEMM {L}x{M}x{H} {ms_g8 * 1e3:.1f} us -> {tf8:.1f} TFLOP/s (fp8 dense peak 5000); "
+        f"row quantisation of its {L}x{H} fp16 input {ms_q8 * 1e3:.1f} us")
+    del a8, w8, a_src, w_src
+
     from diffusion_transformer_image_mm_amd.traffic import load_traffic
     traffic = load_traffic()   # HBM bytes per launch from the committed counter summary, None if stale
     if traffic is not None:
@@ -226,6 +261,10 @@ def main() -> int:
                      "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "avg_us": round(ms_gemm * 1e3, 2)},
+        "fp8_mlp_in_gemm": {"kernel": "gemm_kernel<fp8 e4m3 A and W, row/channel scales, BIAS_GELU>",
+                            "achieved": round(tf8, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(tf8 / PEAK_FP8_TFLOPS, 4), "avg_us": round(ms_g8 * 1e3, 2),
+                            "activation_quantisation_us": round(ms_q8 * 1e3, 2)},
     }
 
     # ------------------------------------------------------------ full denoise step

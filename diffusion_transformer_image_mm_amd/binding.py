@@ -37,7 +37,7 @@ lib = ctypes.CDLL(LIB_PATH)
 MMDIT_ABI_VERSION = 3
 MMDIT_OK, MMDIT_E_NULL, MMDIT_E_ALIGN, MMDIT_E_SHAPE = 0, 1, 2, 3
 MMDIT_E_DTYPE, MMDIT_E_WORKSPACE, MMDIT_E_HIP, MMDIT_E_ARG = 4, 5, 6, 7
-MMDIT_BF16, MMDIT_INT8, MMDIT_F16 = 0, 1, 2
+MMDIT_BF16, MMDIT_INT8, MMDIT_F16, MMDIT_FP8 = 0, 1, 2, 3
 MMDIT_WS_DOUBLE, MMDIT_WS_SINGLE, MMDIT_WS_STEP = 0, 1, 2
 (MMDIT_EPI_BIAS, MMDIT_EPI_BIAS_GELU, MMDIT_EPI_GATE_RESID, MMDIT_EPI_SPLIT_GELU,
  MMDIT_EPI_BIAS_F32, MMDIT_EPI_EULER, MMDIT_EPI_SWIGLU, MMDIT_EPI_SPLIT_SWIGLU) = range(8)
@@ -83,7 +83,7 @@ class mmdit_gemm(Structure):
                 ("a", c_void_p), ("lda", c_int32), ("w", mmdit_linear), ("epilogue", c_int32),
                 ("out", c_void_p), ("ldo", c_int32), ("gate", c_void_p), ("resid", c_void_p),
                 ("ldr", c_int32), ("split_n", c_int32), ("out2", c_void_p), ("ldo2", c_int32),
-                ("out2_col", c_int32), ("alpha", c_float)]
+                ("out2_col", c_int32), ("alpha", c_float), ("a_scale", c_void_p)]
 
 
 # ---------------------------------------------------------------- marshalling
@@ -116,6 +116,7 @@ _SIGS = {
     "mmdit_denoise_step": (c_int, [POINTER(mmdit_dims), POINTER(mmdit_model), _P, _P, _P, c_float,
                                    c_float, c_float, _P, c_size_t, _P]),
     "mmdit_rope_table": (c_int, [POINTER(mmdit_dims), _P, _P, _P]),
+    "mmdit_quantize_fp8_rows": (c_int, [_P, c_int, c_int, c_int, c_int, _P, c_int, _P, _P]),
     "mmdit_modulation_floats": (c_size_t, [POINTER(mmdit_dims)]),
     "mmdit_modulation_workspace_bytes": (c_size_t, [POINTER(mmdit_dims), c_int]),
     "mmdit_modulation_batch": (c_int, [POINTER(mmdit_dims), POINTER(mmdit_model), POINTER(c_float), c_int, c_float,
@@ -178,6 +179,11 @@ def mmdit_block_forward(dims, w, vec, rope, x_in, x_out, ws, ws_bytes, stream=No
 def mmdit_single_block_forward(dims, w, vec, rope, x_in, x_out, ws, ws_bytes, stream=None) -> int:
     return lib.mmdit_single_block_forward(ctypes.byref(dims), ctypes.byref(w), ptr(vec), ptr(rope),
                                           ptr(x_in), ptr(x_out), ptr(ws), ws_bytes, stream_handle(stream))
+
+
+def mmdit_quantize_fp8_rows(x, x_dtype, rows, cols, ldx, codes, ldc, scales, stream=None) -> int:
+    return lib.mmdit_quantize_fp8_rows(ptr(x), x_dtype, rows, cols, ldx, ptr(codes), ldc, ptr(scales),
+                                       stream_handle(stream))
 
 
 def mmdit_modulation_floats(dims) -> int:

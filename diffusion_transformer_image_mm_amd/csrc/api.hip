@@ -58,7 +58,7 @@ int check_linear(const mmdit_linear& l, int dtype) {
     int st;
     if ((st = check_ptr(l.w)) != MMDIT_OK) return st;
     if ((st = check_ptr(l.bias)) != MMDIT_OK) return st;
-    if (dtype == MMDIT_INT8) {
+    if (dtype == MMDIT_INT8 || dtype == MMDIT_FP8) {
         if (!l.scale) return MMDIT_E_DTYPE;
         if (!aligned16(l.scale)) return MMDIT_E_ALIGN;
     }
@@ -657,8 +657,14 @@ int mmdit_k_gemm(const mmdit_gemm* g, hipStream_t s) {
     if (!g) return MMDIT_E_NULL;
     if (g->m < 1 || g->n < 64 || g->n % 64 != 0 || g->k < 64 || g->k % 64 != 0) return MMDIT_E_SHAPE;
     if (g->lda < g->k || g->lda % 8 != 0) return MMDIT_E_SHAPE;
-    if (!dtype_ok(g->weight_dtype)) return MMDIT_E_DTYPE;
+    if (!dtype_ok(g->weight_dtype) && g->weight_dtype != MMDIT_FP8) return MMDIT_E_DTYPE;
     if (g->epilogue < MMDIT_EPI_BIAS || g->epilogue > MMDIT_EPI_SPLIT_SWIGLU) return MMDIT_E_ARG;
+    if (g->weight_dtype == MMDIT_FP8) {
+        // fp8 codes for A too: 128 k per stage, rows 16-byte aligned, a row scale
+        if (g->k % 128 != 0 || g->lda % 16 != 0) return MMDIT_E_SHAPE;
+        if (g->epilogue == MMDIT_EPI_SWIGLU || g->epilogue == MMDIT_EPI_SPLIT_SWIGLU) return MMDIT_E_ARG;
+        MMDIT_TRY(check_ptr(g->a_scale));
+    }
     MMDIT_TRY(check_ptr(g->a));
     MMDIT_TRY(check_linear(g->w, g->weight_dtype));
     MMDIT_TRY(check_ptr(g->out));
@@ -690,7 +696,21 @@ int mmdit_k_gemm(const mmdit_gemm* g, hipStream_t s) {
     a.ldo2 = g->ldo2;
     a.out2_col = g->out2_col;
     a.alpha = g->alpha;
+    a.a_scale = g->a_scale;
     MMDIT_HIP(gemm_1(a, group(0, g->m, g->w, g->gate), s));
+    return MMDIT_OK;
+}
+
+int mmdit_quantize_fp8_rows(const void* x, int x_dtype, int rows, int cols, int ldx, uint8_t* codes, int ldc,
+                            float* scales, hipStream_t s) {
+    if (x_dtype != MMDIT_BF16 && x_dtype != MMDIT_F16) return MMDIT_E_DTYPE;
+    if (rows < 0 || cols < 16 || cols % 16 != 0 || ldx < cols || ldx % 8 != 0 || ldc < cols || ldc % 16 != 0)
+        return MMDIT_E_SHAPE;
+    MMDIT_TRY(check_ptr(x));
+    MMDIT_TRY(check_ptr(codes));
+    MMDIT_TRY(check_ptr(scales));
+    MMDIT_HIP(launch_quantize_fp8_rows(static_cast<const uint16_t*>(x), x_dtype == MMDIT_BF16, rows, cols, ldx,
+                                       codes, ldc, scales, s));
     return MMDIT_OK;
 }
 

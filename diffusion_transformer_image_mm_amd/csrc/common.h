@@ -15,6 +15,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));   // 32 fp8 codes
 
 namespace mmdit {
 
@@ -131,6 +132,7 @@ struct GemmArgs {
     // ones, so that a partial last round of 256-wide tiles becomes half as long.
     int tail_rows;
     int full_tiles;
+    const float* a_scale;   // fp32 per row of A, fp8 operands only
 };
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
@@ -162,6 +164,10 @@ hipError_t launch_rope_table(const int32_t* ids, int seq_len, int head_dim, int 
                              float theta, float* rope, hipStream_t s);
 
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t s);
+
+// Per-row fp8 e4m3 quantisation of 16-bit rows (bf16 when x_bf16, else fp16)
+hipError_t launch_quantize_fp8_rows(const uint16_t* x, bool x_bf16, int rows, int cols, int ldx,
+                                    uint8_t* codes, int ldc, float* scales, hipStream_t s);
 
 // y fp16 = SiLU(x fp32), n elements
 hipError_t launch_silu_to_f16(const float* x, uint16_t* y, int64_t n, hipStream_t s);

@@ -184,9 +184,12 @@ template <int WT, int EPI, int PIPE, int TNW>
 MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, int rt0, int tmt) {
     constexpr bool INT8 = WT == MMDIT_INT8;
     constexpr bool F16W = WT == MMDIT_F16;
+    constexpr bool FP8 = WT == MMDIT_FP8;      // fp8 A and W, 128 k per stage
     constexpr bool SWIGLU = EPI == MMDIT_EPI_SWIGLU || EPI == MMDIT_EPI_SPLIT_SWIGLU;
     static_assert(PIPE == 0 || F16W, "the pipelined main loop reads plain fp16 weight fragments");
     static_assert(TNW == 4 || (TNW == 2 && PIPE == 0 && !SWIGLU), "tail tiles: plain loop, no SwiGLU");
+    static_assert(!FP8 || (TNW == 4 && !SWIGLU), "fp8: 256-wide tiles, no SwiGLU epilogue");
+    constexpr int ES = FP8 ? 1 : 2;            // bytes per element of A (and of 16-bit / fp8 W)
     constexpr int BNT = 64 * TNW;                                 // tile width (output columns)
     constexpr int W_TILE = BNT * BK * (INT8 ? 1 : 2);             // fp16 weights: as bf16
     constexpr int STAGE = A_TILE_BYTES + W_TILE;
@@ -211,7 +214,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
     // lane i covers row r = (4w + j)*8 + i/8 at LDS position p = i%8,
     // fetching chunk c = p ^ ((r >> 1) & 7).
     const int lrow = lane >> 3, lpos = lane & 7;
-    const char* a_g = reinterpret_cast<const char*>(args.a + (size_t)G.row0 * args.lda);
+    const char* a_g = reinterpret_cast<const char*>(args.a) + (size_t)G.row0 * args.lda * ES;
     uint32_t a_off_g[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -219,7 +222,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
         const int c = lpos ^ ((r >> 1) & 7);
         int gr = tc.m0 + r;
         gr = gr < M ? gr : M - 1;
-        a_off_g[j] = (uint32_t)gr * (uint32_t)args.lda * 2u + (uint32_t)c * 16u;
+        a_off_g[j] = (uint32_t)gr * (uint32_t)args.lda * (uint32_t)ES + (uint32_t)c * 16u;
     }
     // W tile. bf16: same pattern as A over N rows. int8: 64 B per row = 4
     // units of 16 codes; a load covers 16 rows (lane i: row (2w + j)*16 +
@@ -234,7 +237,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
             int gn = tc.n0 + r;
             gn = gn < N ? gn : N - 1;
             if (SWIGLU) gn = weight_row(gn, sw_from, sw_half);
-            w_off_g[j] = (uint32_t)gn * (uint32_t)K * 2u + (uint32_t)c * 16u;
+            w_off_g[j] = (uint32_t)gn * (uint32_t)K * (uint32_t)ES + (uint32_t)c * 16u;
         }
     } else {
 #pragma unroll
@@ -291,11 +294,52 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
 #pragma unroll
         for (int j = 0; j < TM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = K / BK;
+    const int nk = FP8 ? K / 128 : K / BK;   // a stage holds 128 bytes of every row
     issue_stage(0, 0);
     wait_vmcnt0();
     __syncthreads();
 
+    if constexpr (FP8) {
+        // fp8: one v_mfma_scale_f32_16x16x128_f8f6f4 per 16x16 sub-tile and
+        // stage (unit block scales). Lane l takes row l%16 and k-bytes
+        // 32(l/16) .. +31 of the stage: the 16-byte chunks 2(l/16) and
+        // 2(l/16)+1 of its LDS row, each at its swizzled position.
+        int a_off8[2], w_off8[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int c = 2 * lg + h;
+            a_off8[h] = (wm * 128 + lr) * 128 + ((c ^ ((lr >> 1) & 7)) * 16);
+            w_off8[h] = (wn * 64 + lr) * 128 + ((c ^ ((lr >> 1) & 7)) * 16);
+        }
+        for (int kt = 0; kt < nk; ++kt) {
+            const int s = kt & 1;
+            const char* sa = smem + s * STAGE;
+            const char* sw = sa + A_TILE_BYTES;
+            i32x8_t fa[TM], fw[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const uint4 lo = *reinterpret_cast<const uint4*>(sa + a_off8[0] + i * 16 * 128);
+                const uint4 hi = *reinterpret_cast<const uint4*>(sa + a_off8[1] + i * 16 * 128);
+                fa[i] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            }
+#pragma unroll
+            for (int i = 0; i < TN; ++i) {
+                const uint4 lo = *reinterpret_cast<const uint4*>(sw + w_off8[0] + i * 16 * 128);
+                const uint4 hi = *reinterpret_cast<const uint4*>(sw + w_off8[1] + i * 16 * 128);
+                fw[i] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            }
+            if (kt + 1 < nk) issue_stage(kt + 1, s ^ 1);
+#pragma unroll
+            for (int in = 0; in < TN; ++in)
+#pragma unroll
+                for (int im = 0; im < TM; ++im)
+                    acc[in][im] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fw[in], fa[im], acc[in][im], 0, 0,
+                                                                                    0, 127, 0, 127);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt0();
+            __syncthreads();
+        }
+    } else
     if (PIPE) {
         // Half-stage register pipeline for long contractions: r0 holds the
         // fragments of k-substep 0, r1 those of substep 1 (the same 96
@@ -431,7 +475,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
         const float b[4] = {bf2f(braw.x & 0xffff), bf2f(braw.x >> 16), bf2f(braw.y & 0xffff),
                             bf2f(braw.y >> 16)};
         float sc[4] = {1.f, 1.f, 1.f, 1.f};
-        if (INT8) {
+        if (INT8 || FP8) {
             const float4 s4 = *reinterpret_cast<const float4*>(G.scale + n);
             sc[0] = s4.x; sc[1] = s4.y; sc[2] = s4.z; sc[3] = s4.w;
         }
@@ -448,6 +492,12 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
             float y[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) y[j] = acc[in][im][j] * sc[j] + b[j];
+            if (FP8) {
+                // the row's activation scale: y = (sum * a_scale) * w_scale + b
+                const float sa = args.a_scale[grow];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) y[j] = (acc[in][im][j] * sa) * sc[j] + b[j];
+            }
             if (EPI == MMDIT_EPI_BIAS || EPI == MMDIT_EPI_SPLIT_SWIGLU ||
                 (EPI == MMDIT_EPI_SPLIT_GELU && n < args.split_n)) {
                 // attention-side operands (q, k, v): bf16
@@ -491,7 +541,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) 
     const int tm0 = (args.g[0].m + BM - 1) / BM;
     const int tmt = args.ngroups == 2 ? tm0 + (args.g[1].m + BM - 1) / BM : tm0;
     const int nf = args.full_tiles;
-    if constexpr (!SWIGLU && PIPE == 0) {
+    if constexpr (!SWIGLU && PIPE == 0 && WT != MMDIT_FP8) {
         if ((int)blockIdx.x >= nf) {
             gemm_tile<WT, EPI, 0, 2>(args, smem, blockIdx.x - nf, gridDim.x - nf, tmt - args.tail_rows,
                                      args.tail_rows);
@@ -532,7 +582,7 @@ static hipError_t launch_gemm_t(const GemmArgs& a0, hipStream_t s) {
     // tiles instead (twice as many, each half as long).
     const int cus = cu_count();
     a.tail_rows = 0;
-    if (!swiglu && !pipe && (tmt * tn) % cus != 0 && (tmt * tn) % cus <= cus / 2) {
+    if (WT != MMDIT_FP8 && !swiglu && !pipe && (tmt * tn) % cus != 0 && (tmt * tn) % cus <= cus / 2) {
         const int tn2 = (a.n + BN / 2 - 1) / (BN / 2);
         for (int r = 1; r < tmt; ++r) {
             if (((tmt - r) * tn) % cus == 0 && r * tn2 <= cus) {
@@ -546,7 +596,9 @@ static hipError_t launch_gemm_t(const GemmArgs& a0, hipStream_t s) {
     const size_t lds = 2 * (size_t)(A_TILE_BYTES + (INT8 ? W_TILE_BYTES_I8 : W_TILE_BYTES_BF16));
     dim3 grid(tiles), block(NTHREADS);
 #define GEMM_CASE(E)                                                                        \
-    case E: {                                                                               \
+    case E: if constexpr (WT == MMDIT_FP8 && (E == MMDIT_EPI_SWIGLU || E == MMDIT_EPI_SPLIT_SWIGLU)) { \
+        return hipErrorInvalidValue;                                                        \
+    } else {                                                                                \
         auto kfn = pipe ? gemm_kernel<WT, E, (WT == MMDIT_F16 ? 1 : 0)> : gemm_kernel<WT, E, 0>; \
         static bool attr_done[2] = {false, false};                                          \
         if (!attr_done[pipe]) {                                                             \
@@ -580,6 +632,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
         case MMDIT_BF16: return launch_gemm_t<MMDIT_BF16>(a, s);
         case MMDIT_INT8: return launch_gemm_t<MMDIT_INT8>(a, s);
         case MMDIT_F16: return launch_gemm_t<MMDIT_F16>(a, s);
+        case MMDIT_FP8: return launch_gemm_t<MMDIT_FP8>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

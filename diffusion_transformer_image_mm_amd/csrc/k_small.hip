@@ -228,6 +228,65 @@ hipError_t launch_rope_table(const int32_t* ids, int seq_len, int head_dim, int 
 }
 
 // ---------------------------------------------------------------------------
+// Per-row fp8 quantisation (OCP e4m3, largest finite 448): scale = max|x| /
+// 448, code = e4m3(x / scale), both divisions correctly rounded fp32, the
+// conversion round-to-nearest-even (v_cvt_pk_fp8_f32). One 256-thread
+// workgroup per row; 8 values per thread and pass (16-byte loads, 8-byte
+// stores); the row is read twice (the second pass from L2).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quantize_fp8_rows_kernel(const uint16_t* __restrict__ x, int x_bf16,
+                                                                int cols, int ldx, uint8_t* __restrict__ codes,
+                                                                int ldc, float* __restrict__ scales) {
+    __shared__ float red[4];
+    const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)row * ldx);
+    const int n8 = cols >> 3;
+    auto val = [&](uint32_t bits) -> float { return x_bf16 ? bf2f((uint16_t)bits) : h2f((uint16_t)bits); };
+    float m = 0.f;
+    for (int c = tid; c < n8; c += 256) {
+        const uint4 v = xr[c];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(val(w[i] & 0xffffu)), fabsf(val(w[i] >> 16))));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float sc = m / 448.0f;
+    uint2* cr = reinterpret_cast<uint2*>(codes + (size_t)row * ldc);
+    for (int c = tid; c < n8; c += 256) {
+        const uint4 v = xr[c];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t packed[2] = {0u, 0u};
+        if (sc > 0.f) {
+            float q[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                q[2 * i] = val(w[i] & 0xffffu) / sc;
+                q[2 * i + 1] = val(w[i] >> 16) / sc;
+            }
+            // codes 0-3 into word 0 (low half, then high half), 4-7 into word 1
+            packed[0] = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0u, false);
+            packed[0] = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], packed[0], true);
+            packed[1] = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0u, false);
+            packed[1] = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], packed[1], true);
+        }
+        cr[c] = make_uint2(packed[0], packed[1]);
+    }
+    if (tid == 0) scales[row] = sc;
+}
+
+hipError_t launch_quantize_fp8_rows(const uint16_t* x, bool x_bf16, int rows, int cols, int ldx,
+                                    uint8_t* codes, int ldc, float* scales, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(quantize_fp8_rows_kernel, dim3(rows), dim3(256), 0, s, x, x_bf16 ? 1 : 0, cols, ldx, codes,
+                       ldc, scales);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // out fp16 [rows, n] = SiLU(x fp32 [rows, n]): the activation operand of the
 // modulation linears when they run as one GEMM over many conditioning vectors
 // ---------------------------------------------------------------------------

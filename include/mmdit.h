@@ -73,13 +73,21 @@ enum mmdit_weight_dtype {
     MMDIT_INT8 = 1, /* weights are int8 codes [out, in] with fp32 scale [out]:
                        W = diag(scale) * codes (flux-amd-rocm benchmarks page:
                        int8 weight-only linears) */
-    MMDIT_F16 = 2   /* weights are fp16 [out, in]: bf16 weights re-encoded once
+    MMDIT_F16 = 2,  /* weights are fp16 [out, in]: bf16 weights re-encoded once
                        by mmdit_weights_to_f16. The matrix cores take both
                        operands in one format and the activation operands are
                        fp16, so the bf16 path converts every weight fragment
                        in registers on every use; this format does it once.
                        Same rounding, so results are bit-identical to
                        MMDIT_BF16 with the bf16 originals */
+    MMDIT_FP8 = 3   /* OCP fp8 e4m3 codes [out, in] with an fp32 scale per output
+                       channel: W = diag(scale) * decode(codes). GEMMs only
+                       (mmdit_k_gemm): the activation operand is fp8 e4m3 too,
+                       with an fp32 scale per row (mmdit_gemm.a_scale), and the
+                       product runs on the fp8 matrix cores (SGLang-AMD,
+                       "Architecture Deep Dive": fp8 on CDNA). Codes and scales
+                       come from mmdit_quantize_fp8_rows. Not accepted by the
+                       block and step entries */
 };
 
 /* ------------------------------------------------------------------ sizes */
@@ -403,9 +411,26 @@ typedef struct mmdit_gemm {
     int32_t ldo2;
     int32_t out2_col;
     float alpha;        /* EULER */
+    const float* a_scale; /* fp32 [m], MMDIT_FP8 only: row i of A is a_scale[i] * decode(a[i]) */
 } mmdit_gemm;
 
+/* With weight_dtype MMDIT_FP8, a holds fp8 e4m3 codes (lda in bytes, a
+ * multiple of 16), k is a multiple of 128, w.scale and a_scale are required:
+ * y[i][j] = a_scale[i] * w.scale[j] * sum_k decode(a[i][k]) decode(w[j][k]) + b[j]
+ * (the fp8 products are exact and the sums accumulate in fp32). */
 int mmdit_k_gemm(const mmdit_gemm* g, hipStream_t stream);
+
+/*
+ * Per-row fp8 quantisation (OCP e4m3, largest finite value 448): for each of
+ * `rows` rows of x (16-bit floats, x_dtype MMDIT_BF16 or MMDIT_F16, row
+ * stride ldx elements, `cols` values), scale = max|x| / 448 (fp32 division)
+ * and code = e4m3(x / scale) (fp32 division, round to nearest even); an
+ * all-zero row gets scale 0 and zero codes. Weights [out, in] quantised this
+ * way get one scale per output channel; activations one per token.
+ *   codes: fp8 [rows, ldc] (ldc bytes >= cols, a multiple of 16); scales: fp32 [rows]
+ */
+int mmdit_quantize_fp8_rows(const void* x, int x_dtype, int rows, int cols, int ldx,
+                            uint8_t* codes, int ldc, float* scales, hipStream_t stream);
 
 /*
  * out[n] (+)= W act(x) + b for one vector (modulation and embedder layers):

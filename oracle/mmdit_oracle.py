@@ -370,3 +370,47 @@ def denoise_step(z, txt, ids, m, shp, t_cur: float, t_next: float, guidance: flo
     n = shp.img_len - shp.ref_len
     z_next[:n] = euler(z[:n], v, t_cur, t_next)
     return z_next, v
+
+
+# --------------------------------------------------------------------------
+# fp8 (OCP e4m3) quantisation: the fp8 variant of the linears
+# --------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_round(x) -> np.ndarray:
+    """Round to the nearest OCP fp8 e4m3 value, ties to the even mantissa.
+    e4m3: 4 exponent bits (bias 7), 3 mantissa bits; normal values
+    (1 + m/8) 2^(e-7) for e = 1..15 (e = 15, m = 7 is NaN, so the largest
+    finite value is 1.75 * 2^8 = 448); subnormals (m/8) 2^-6, a step of 2^-9.
+    Inputs must lie within +-(448 + half a step), the quantiser's range."""
+    x = _f64(x)
+    a = np.abs(x)
+    assert np.all(a < 464.0), "outside the e4m3 range this quantiser produces"
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)          # below 2^-6 the spacing stays 2^-9
+    step = np.exp2(e - 3.0)
+    return np.round(x / step) * step  # np.round: half to even; x / step is exact
+
+
+def quantize_rows_fp8(x):
+    """Per-row fp8 quantisation as the fp8 linears use it: the row's scale is
+    max|x| / 448 and its codes e4m3(x / scale), both divisions in fp32 (the
+    precision the kernels take these decisions in); an all-zero row gets scale
+    0 and zero codes. Returns (code values [rows, cols] float64, scales fp32)."""
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x32), axis=1).astype(np.float32)
+    sc = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    safe = np.where(sc > 0, sc, np.float32(1.0)).astype(np.float32)
+    q = (x32 / safe[:, None]).astype(np.float32)
+    codes = np.where(sc[:, None] > 0, e4m3_round(q), 0.0)
+    return codes, sc
+
+
+def linear_fp8(a_codes, a_scale, w_codes, w_scale, bias) -> np.ndarray:
+    """y = (diag(a_scale) A) (diag(w_scale) W)^T + b from the decoded fp8
+    codes, in fp64."""
+    a = _f64(a_scale)[:, None] * _f64(a_codes)
+    w = _f64(w_scale)[:, None] * _f64(w_codes)
+    return a @ w.T + _f64(bias)[None, :]

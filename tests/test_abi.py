@@ -160,8 +160,17 @@ def test_kernel_entry_validation():
     assert B.mmdit_k_gemm(g) == B.MMDIT_E_NULL  # gate / resid missing
     g.epilogue, g.weight_dtype = 0, B.MMDIT_INT8
     assert B.mmdit_k_gemm(g) == B.MMDIT_E_DTYPE  # int8 without scales
-    g.weight_dtype = 3
+    g.weight_dtype = 4
     assert B.mmdit_k_gemm(g) == B.MMDIT_E_DTYPE
+    g.weight_dtype = B.MMDIT_FP8           # fp8 operands: k a multiple of 128, a row scale, weight scales
+    assert B.mmdit_k_gemm(g) == B.MMDIT_E_SHAPE
+    g.k, g.lda = 128, 128
+    assert B.mmdit_k_gemm(g) == B.MMDIT_E_NULL
+    g.a_scale = FAKE
+    assert B.mmdit_k_gemm(g) == B.MMDIT_E_DTYPE   # w.scale missing
+    g.lda = 136
+    assert B.mmdit_k_gemm(g) == B.MMDIT_E_SHAPE   # fp8 rows must stay 16-byte aligned
+    g.k, g.lda, g.a_scale = 64, 64, None
     g.weight_dtype, g.epilogue, g.ldo = 0, B.MMDIT_EPI_SWIGLU, 64
     assert B.mmdit_k_gemm(g) == B.MMDIT_E_SHAPE  # SwiGLU: n (2M) a multiple of 256
     g.n, g.ldo = 256, 120
@@ -173,6 +182,15 @@ def test_kernel_entry_validation():
     assert B.mmdit_k_gemv(FAKE, 128, lin, 10, 3, 1, 0, FAKE) == B.MMDIT_E_DTYPE
     assert B.mmdit_k_gemv(FAKE, 4160, lin, 10, 0, 1, 0, FAKE) == B.MMDIT_E_SHAPE  # k > 4096
     assert B.mmdit_k_euler(FAKE + 8, FAKE, 10, 0.1) == B.MMDIT_E_ALIGN
+
+
+def test_quantize_fp8_validation():
+    assert B.mmdit_quantize_fp8_rows(FAKE, B.MMDIT_INT8, 4, 64, 64, FAKE, 64, FAKE) == B.MMDIT_E_DTYPE
+    assert B.mmdit_quantize_fp8_rows(FAKE, B.MMDIT_F16, 4, 40, 64, FAKE, 64, FAKE) == B.MMDIT_E_SHAPE
+    assert B.mmdit_quantize_fp8_rows(FAKE, B.MMDIT_F16, 4, 64, 64, FAKE, 72, FAKE) == B.MMDIT_E_SHAPE
+    assert B.mmdit_quantize_fp8_rows(FAKE, B.MMDIT_BF16, 4, 64, 60, FAKE, 64, FAKE) == B.MMDIT_E_SHAPE
+    assert B.mmdit_quantize_fp8_rows(0, B.MMDIT_BF16, 4, 64, 64, FAKE, 64, FAKE) == B.MMDIT_E_NULL
+    assert B.mmdit_quantize_fp8_rows(FAKE, B.MMDIT_BF16, 4, 64, 64, FAKE, 64, FAKE + 4) == B.MMDIT_E_ALIGN
 
 
 def test_weight_conversion_validation():

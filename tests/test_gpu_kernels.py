@@ -497,3 +497,138 @@ def test_euler():
     B.check(B.mmdit_k_euler(dz, A.f32(v), z.size, -1.0 / 28, stream()))
     sync()
     np.testing.assert_allclose(dz.cpu().numpy(), O.euler(z, v, 1.0, 1.0 - 1.0 / 28), rtol=0, atol=1e-6)
+
+
+
+# ------------------------------------------------------------------ fp8 (OCP e4m3)
+def _e4m3_table() -> np.ndarray:
+    t = np.empty(256)
+    for c in range(256):
+        sign = -1.0 if c & 0x80 else 1.0
+        e, m = (c >> 3) & 0xF, c & 0x7
+        if e == 0xF and m == 0x7:
+            t[c] = np.nan
+        elif e == 0:
+            t[c] = sign * (m / 8.0) * 2.0 ** -6
+        else:
+            t[c] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return t
+
+
+E4M3 = _e4m3_table()
+
+
+def _quantize_gpu(A, x, dtype, ldx=None, ldc=None):
+    """Upload x (16-bit exact values) and quantise it per row on the GPU."""
+    rows, cols = x.shape
+    ldx = ldx or cols
+    ldc = ldc or cols
+    xp = np.zeros((rows, ldx), dtype=np.float32)
+    xp[:, :cols] = x
+    dx = A.f16(xp) if dtype == "f16" else A.bf16(xp)
+    codes = A._hold(torch.zeros(rows, ldc, dtype=torch.uint8, device="cuda"))
+    scales = A.empty_f32(rows)
+    xd = B.MMDIT_F16 if dtype == "f16" else B.MMDIT_BF16
+    B.check(B.mmdit_quantize_fp8_rows(dx, xd, rows, cols, ldx, codes, ldc, scales, stream()), "quantize")
+    return codes, scales
+
+
+@pytest.mark.parametrize("rows,cols,ldx,ldc,dt", [(37, 3072, 3072, 3072, "f16"), (5, 256, 264, 272, "bf16"),
+                                               (300, 12288, 12288, 12288, "f16"), (1, 16, 16, 16, "bf16")])
+def test_quantize_fp8_rows_bit_exact(rows, cols, ldx, ldc, dt):
+    """Scales and codes equal the oracle's bit for bit: both take the
+    decisions in fp32 (scale = max|x| / 448, x / scale, round to nearest even)."""
+    say(f"quantize fp8 rows={rows} cols={cols} {dt}")
+    A = DeviceArena()
+    x = rnd(150, (rows, cols), 3.0)
+    x = synth.f16_exact(x) if dt == "f16" else x
+    if rows > 2:
+        x[2] = 0.0
+    codes, scales = _quantize_gpu(A, x, dt, ldx, ldc)
+    sync()
+    c = codes.cpu().numpy()[:, :cols]
+    ref_codes, ref_sc = O.quantize_rows_fp8(x)
+    np.testing.assert_array_equal(scales.cpu().numpy(), ref_sc)
+    np.testing.assert_array_equal(E4M3[c], ref_codes)
+
+
+def _run_gemm_fp8(m, n, k, epi, rows=None, tid=140):
+    A = DeviceArena()
+    a = synth.f16_exact(rnd(tid, (m, k)))
+    w = rnd(tid + 1, (n, k), 0.02)
+    b = rnd(tid + 2, (n,), 0.02)
+    ac, asc = _quantize_gpu(A, a, "f16")
+    wc, wsc = _quantize_gpu(A, w, "bf16")
+    db = A.bf16(b)
+    g = B.mmdit_gemm(m=m, n=n, k=k, weight_dtype=B.MMDIT_FP8, a=ac.data_ptr(), lda=k,
+                     w=B.mmdit_linear(wc.data_ptr(), wsc.data_ptr(), db.data_ptr()), epilogue=epi)
+    g.a_scale = asc.data_ptr()
+    f32out = epi in (B.MMDIT_EPI_GATE_RESID, B.MMDIT_EPI_BIAS_F32)
+    gate = rnd(tid + 5, (n,), 0.7)
+    resid = rnd(tid + 6, (m, n))
+    if f32out:
+        out = A.empty_f32(m, n)
+    else:
+        out = A.empty_f16(m, n) if epi == B.MMDIT_EPI_BIAS_GELU else A.empty_bf16(m, n)
+    g.out, g.ldo = out.data_ptr(), n
+    if epi == B.MMDIT_EPI_GATE_RESID:
+        g.gate, g.resid, g.ldr = A.f32(gate).data_ptr(), A.f32(resid).data_ptr(), n
+    B.check(B.mmdit_k_gemm(g, stream()), "gemm fp8")
+    sync()
+    # the GPU's codes are the oracle's (bit-exact quantisation), so the
+    # reference is the fp64 product of the decoded operands
+    sel = np.arange(m) if rows is None else rows
+    ref_ac, ref_as = O.quantize_rows_fp8(a[sel])
+    ref_wc, ref_ws = O.quantize_rows_fp8(w)
+    np.testing.assert_array_equal(E4M3[ac.cpu().numpy()[sel]], ref_ac)
+    np.testing.assert_array_equal(E4M3[wc.cpu().numpy()], ref_wc)
+    y = O.linear_fp8(ref_ac, ref_as, ref_wc, ref_ws, b)
+    exact = O.linear(a[sel], synth.Linear(w, b))
+    got = to_numpy_f32(out)[sel]
+    if epi == B.MMDIT_EPI_BIAS_GELU:
+        ref = O.gelu_tanh(y)
+    elif epi == B.MMDIT_EPI_GATE_RESID:
+        ref = resid[sel] + gate * y
+    else:
+        ref = y
+    return got, ref, y, exact
+
+
+@pytest.mark.parametrize("m,n,k,epi", [(513, 1024, 256, B.MMDIT_EPI_BIAS_F32), (300, 320, 1024, B.MMDIT_EPI_BIAS_GELU),
+                                       (77, 512, 384, B.MMDIT_EPI_GATE_RESID), (1, 256, 128, B.MMDIT_EPI_BIAS),
+                                       (700, 256, 3072, B.MMDIT_EPI_BIAS_F32)])
+def test_gemm_fp8(m, n, k, epi):
+    """fp8 matrix cores: against the fp64 product of the decoded operands.
+    The products of two e4m3 values are exact; the matrix cores' own sums over
+    a 128-deep fp8 block are not fp32-exact (measured ~1e-4 of the RMS), so
+    the bar is 2e-3 of the RMS: far below the quantisation itself, far above
+    the O(1) errors of a wrong lane layout or scale."""
+    say(f"gemm fp8 m={m} n={n} k={k} epi={epi}")
+    got, ref, y, exact = _run_gemm_fp8(m, n, k, epi)
+    if epi in (B.MMDIT_EPI_BIAS_F32, B.MMDIT_EPI_GATE_RESID):
+        e = rel_err(got, ref)
+        say(f"  rel_err vs decoded-operand product {e:.3e}")
+        assert e <= 2e-3, e
+    elif epi == B.MMDIT_EPI_BIAS_GELU:
+        assert rel_err_rounded_out(got, ref, "f16") <= 2e-3
+    else:
+        assert rel_err_rounded_out(got, ref, "bf16") <= 2e-3
+    # against the unquantised product: each e4m3 rounding is at most 2^-4 of
+    # its value (RMS ~2^-4/sqrt(3) = 3.6%); two of them per product term leave
+    # an error of ~5% of the output's RMS in RMS, a few times that at the
+    # maximum over ~10^5 outputs
+    d = y - exact
+    rms = float(np.sqrt(np.mean(d * d)) / np.sqrt(np.mean(exact * exact)))
+    eq = rel_err(y, exact)
+    say(f"  fp8 quantisation error vs the exact product: rms {rms:.3e}, max {eq:.3e}")
+    assert rms <= 0.08 and eq <= 0.4, (rms, eq)
+
+
+def test_gemm_fp8_mlp_in_size_sampled_rows():
+    m, n, k = 4608, 12288, 3072
+    say(f"gemm fp8 full m={m} n={n} k={k}")
+    rows = np.unique(np.r_[0, 255, 256, m - 1, np.random.default_rng(7).integers(0, m, 40)])
+    got, ref, y, exact = _run_gemm_fp8(m, n, k, B.MMDIT_EPI_BIAS_GELU, rows=rows, tid=160)
+    e = rel_err_rounded_out(got, ref, "f16")
+    say(f"  rel_err beyond the fp16 output rounding {e:.3e}; quantisation error {rel_err(y, exact):.3e}")
+    assert e <= 2e-3, e

@@ -535,3 +535,64 @@ def test_edit_step_reference_rows_and_guidance_free_conditioning():
     assert np.max(np.abs(v3 - v)) > 1e-6
     # shared modulation: every block of a type holds the same weights
     assert m["single"][0]["mod"] is m["single"][-1]["mod"]
+
+
+
+def _e4m3_decode(code: int) -> float:
+    """OCP e4m3 bit pattern -> value, straight from the field layout."""
+    sign = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def test_e4m3_round_against_the_bit_level_format():
+    """The oracle's e4m3 rounding reproduces the format's 253 distinct finite
+    values, fixes every one of them, and sends each midpoint to the neighbour
+    with the even code (round to nearest even); 448 is the largest value."""
+    vals = sorted({_e4m3_decode(c) for c in range(256) if not math.isnan(_e4m3_decode(c))})
+    assert len(vals) == 253 and vals[-1] == 448.0 and vals[0] == -448.0
+    np.testing.assert_array_equal(O.e4m3_round(np.array(vals)), np.array(vals))
+    pos = [v for v in vals if v >= 0]
+    code_of = {}
+    for c in range(128):
+        v = _e4m3_decode(c)
+        if not math.isnan(v):
+            code_of.setdefault(v, c)
+    for lo, hi in zip(pos[:-1], pos[1:]):
+        mid = (lo + hi) / 2
+        even = lo if code_of[lo] % 2 == 0 else hi
+        assert O.e4m3_round(np.array([mid]))[0] == even, (lo, hi)
+        assert O.e4m3_round(np.array([-mid]))[0] == -even
+        # just off the midpoint: the nearer neighbour
+        assert O.e4m3_round(np.array([mid - (hi - lo) / 64]))[0] == lo
+        assert O.e4m3_round(np.array([mid + (hi - lo) / 64]))[0] == hi
+    assert O.e4m3_round(np.array([2.0 ** -9]))[0] == 2.0 ** -9          # smallest subnormal
+    assert O.e4m3_round(np.array([2.0 ** -10]))[0] == 0.0               # tie to 0 (even)
+
+
+def test_fp8_row_quantisation_closed_forms():
+    x = rng.standard_normal((6, 96)).astype(np.float32)
+    x[3] = 0.0
+    codes, sc = O.quantize_rows_fp8(x)
+    assert sc.dtype == np.float32 and sc[3] == 0 and np.all(codes[3] == 0)
+    for r in (0, 1, 2, 4, 5):
+        assert sc[r] == np.float32(np.max(np.abs(x[r])) / np.float32(448.0))
+        assert np.max(np.abs(codes[r])) == 448.0        # the largest element maps to the top code
+        # dequantisation error: at most half a step, i.e. 2^-4 of the value for normal codes
+        deq = sc[r].astype(np.float64) * codes[r]
+        err = np.abs(deq - x[r])
+        normal = np.abs(codes[r]) >= 2.0 ** -6
+        assert np.all(err[normal] <= np.abs(x[r][normal]) * 2.0 ** -4 * (1 + 1e-6))
+        assert np.all(err[~normal] <= sc[r] * 2.0 ** -10 * (1 + 1e-6))
+    # a linear over dequantised operands is the plain product of the dequantised matrices
+    w = rng.standard_normal((8, 96)).astype(np.float32)
+    wc, ws = O.quantize_rows_fp8(w)
+    b = rng.standard_normal(8)
+    y = O.linear_fp8(codes, sc, wc, ws, b)
+    brute = np.array([[sum(float(sc[i]) * codes[i, k] * float(ws[j]) * wc[j, k] for k in range(96)) + b[j]
+                       for j in range(8)] for i in range(6)])
+    np.testing.assert_allclose(y, brute, rtol=1e-12, atol=1e-12)
