@@ -131,13 +131,14 @@ def main() -> int:
     inp = synth.block_inputs(shp, "double")
     flops = block_flops(shp)
 
-    def time_block(f16: bool):
+    def time_block(f16: bool, fp8: bool = False):
         """Median ms of mmdit_block_forward over args.steps calls. f16: the
         bf16 weights re-encoded once as fp16 (mmdit_weights_to_f16), which
         gives the GEMMs bit-identical results without the per-use
-        conversion."""
-        A = DeviceArena(f16_weights=f16)
-        d = dims_for(shp, f16=f16)
+        conversion. fp8: weights quantised per output channel to e4m3 and
+        every projection's activation per token, inside the block."""
+        A = DeviceArena(f16_weights=f16, fp8_weights=fp8)
+        d = dims_for(shp, f16=f16, fp8=fp8)
         rope = A.empty_f32(shp.seq_len, shp.head_dim // 2, 2)
         B.check(B.mmdit_rope_table(d, A.i32(inp["ids"]), rope, stream), "rope")
         w = A.double_weights(inp["w"])
@@ -150,7 +151,7 @@ def main() -> int:
         def block_call():
             B.check(B.mmdit_block_forward(d, w, vec, rope, x0, x, ws, ws.numel(), stream), "block")
 
-        tag = "fp16-encoded" if f16 else "bf16"
+        tag = "fp16-encoded" if f16 else "fp8 e4m3" if fp8 else "bf16"
         log(f"bench: block ({tag} weights) warmup {args.warmup}, timed {args.steps}")
         for _ in range(args.warmup):
             block_call()
@@ -171,6 +172,8 @@ def main() -> int:
         return ms, per, A, w
 
     ms_block_bf16, _, A, _ = time_block(False)
+    del A
+    ms_block_fp8, per8, A, _ = time_block(False, fp8=True)
     del A
     ms_block, per, A, w = time_block(True)
     tflops = flops / (ms_block * 1e-3) / 1e12
@@ -265,6 +268,11 @@ def main() -> int:
                             "achieved": round(tf8, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                             "frac": round(tf8 / PEAK_FP8_TFLOPS, 4), "avg_us": round(ms_g8 * 1e3, 2),
                             "activation_quantisation_us": round(ms_q8 * 1e3, 2)},
+        "fp8_double_block": {"weights": "e4m3 per output channel; activations e4m3 per token before each "
+                                        "projection (quantiser launches included)",
+                             "ms": round(ms_block_fp8, 4), "ms_p90": round(float(np.percentile(per8, 90)), 4),
+                             "effective_tflops": round(flops / (ms_block_fp8 * 1e-3) / 1e12, 2),
+                             "speedup_vs_fp16_operands": round(ms_block / ms_block_fp8, 3)},
     }
 
     # ------------------------------------------------------------ full denoise step

@@ -14,7 +14,7 @@ size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool dtype_ok(int dt) { return dt == MMDIT_BF16 || dt == MMDIT_INT8 || dt == MMDIT_F16; }
+bool dtype_ok(int dt) { return dt == MMDIT_BF16 || dt == MMDIT_INT8 || dt == MMDIT_F16 || dt == MMDIT_FP8; }
 
 // Validate the sizes of a model. Returns MMDIT_OK or the status.
 int check_dims(const mmdit_dims* d) {
@@ -34,6 +34,11 @@ int check_dims(const mmdit_dims* d) {
     if (!(d->ln_eps > 0.f) || !(d->rms_eps > 0.f) || !(d->rope_theta > 1.f)) return MMDIT_E_SHAPE;
     if (!dtype_ok(d->weight_dtype)) return MMDIT_E_DTYPE;
     if (d->mlp_act != MMDIT_ACT_GELU_TANH && d->mlp_act != MMDIT_ACT_SWIGLU) return MMDIT_E_ARG;
+    // fp8 blocks: GELU MLPs only (the SwiGLU epilogues take 16-bit operands)
+    if (d->weight_dtype == MMDIT_FP8 && d->mlp_act != MMDIT_ACT_GELU_TANH) return MMDIT_E_DTYPE;
+    // fp8 GEMMs take 128 k per stage: every projection's k (H, M, H + M)
+    if (d->weight_dtype == MMDIT_FP8 && (d->hidden % 128 != 0 || d->mlp_hidden % 128 != 0))
+        return MMDIT_E_SHAPE;
     // SwiGLU GEMM tiles hold 128 features and never straddle the q|k|v / MLP
     // split of the single-stream linear1 (at 3H)
     if (d->mlp_act == MMDIT_ACT_SWIGLU && (d->hidden % 256 != 0 || d->mlp_hidden % 128 != 0))
@@ -129,6 +134,13 @@ struct DoubleWs {
     uint16_t* vt;    // [heads, D, l_pad] bf16
     uint16_t* o;     // [L, H] fp16 (attention output)
     uint16_t* a;     // [L, M] fp16 (GELU hidden)
+    // fp8 blocks only: the projections' operands as e4m3 codes + row scales
+    uint8_t* h8;     // [L, H]
+    uint8_t* o8;     // [L, H]
+    uint8_t* a8;     // [L, M]
+    float* sh;       // [L]
+    float* so;       // [L]
+    float* sa;       // [L]
 };
 
 DoubleWs carve_double(const mmdit_dims* d, Carver& c) {
@@ -142,6 +154,16 @@ DoubleWs carve_double(const mmdit_dims* d, Carver& c) {
     w.vt = c.take<uint16_t>(LP * H);
     w.o = c.take<uint16_t>(L * H);
     w.a = c.take<uint16_t>(L * M);
+    w.h8 = w.o8 = w.a8 = nullptr;
+    w.sh = w.so = w.sa = nullptr;
+    if (d->weight_dtype == MMDIT_FP8) {
+        w.h8 = c.take<uint8_t>(L * H);
+        w.o8 = c.take<uint8_t>(L * H);
+        w.a8 = c.take<uint8_t>(L * M);
+        w.sh = c.take<float>(L);
+        w.so = c.take<float>(L);
+        w.sa = c.take<float>(L);
+    }
     return w;
 }
 
@@ -153,6 +175,10 @@ struct SingleWs {
     uint16_t* k;
     uint16_t* vt;
     uint16_t* cat;   // [L, H + M] fp16: [attention | GELU(mlp)]
+    uint8_t* h8;     // fp8 blocks only: [L, H] and [L, H + M] e4m3 codes + row scales
+    uint8_t* cat8;
+    float* sh;
+    float* sc;
 };
 
 SingleWs carve_single(const mmdit_dims* d, Carver& c) {
@@ -165,6 +191,14 @@ SingleWs carve_single(const mmdit_dims* d, Carver& c) {
     w.k = c.take<uint16_t>(LP * H);
     w.vt = c.take<uint16_t>(LP * H);
     w.cat = c.take<uint16_t>(L * (H + M));
+    w.h8 = w.cat8 = nullptr;
+    w.sh = w.sc = nullptr;
+    if (d->weight_dtype == MMDIT_FP8) {
+        w.h8 = c.take<uint8_t>(L * H);
+        w.cat8 = c.take<uint8_t>(L * (H + M));
+        w.sh = c.take<float>(L);
+        w.sc = c.take<float>(L);
+    }
     return w;
 }
 
@@ -265,6 +299,21 @@ hipError_t gemm_1(GemmArgs g, const GemmGroup& g0, hipStream_t s) {
     return launch_gemm(g, s);
 }
 
+// fp8 blocks: the 16-bit activation rows x [rows, cols] as e4m3 codes + row scales
+hipError_t quant_rows(const uint16_t* x, int rows, int cols, uint8_t* q, float* sc, hipStream_t s) {
+    return launch_quantize_fp8_rows(x, false, rows, cols, cols, q, cols, sc, s);
+}
+
+// The projection's activation operand: the fp16 rows themselves, or their fp8
+// codes (quantised here) with a row scale for fp8 weights.
+GemmArgs proj_base(const mmdit_dims* d, int n, int k, const uint16_t* a16, uint8_t* a8, float* sa, int epi,
+                   void* out, int ldo) {
+    if (d->weight_dtype != MMDIT_FP8) return gemm_base(n, k, d->weight_dtype, a16, k, epi, out, ldo);
+    GemmArgs g = gemm_base(n, k, MMDIT_FP8, reinterpret_cast<const uint16_t*>(a8), k, epi, out, ldo);
+    g.a_scale = sa;
+    return g;
+}
+
 // fp32 latent -> fp16 activation operand of the patch-embedding projection
 __global__ void f32_to_f16_kernel(const float* __restrict__ x, uint16_t* __restrict__ y, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
@@ -283,10 +332,12 @@ int run_double(const mmdit_dims* d, const mmdit_double_weights* w, const float* 
     const float* mi = mt + 6 * H;
     // a1: modulation of each stream
     if (!premod) MMDIT_HIP(gemv_2(vec, H, w->txt.mod, ws.mod, w->img.mod, ws.mod + 6 * H, 6 * H, dt, 1, s));
+    const bool fp8 = dt == MMDIT_FP8;
     // a2: LN1 + modulate
     MMDIT_HIP(launch_ln_modulate(x_in, L, H, Lt, mt, mt + H, mi, mi + H, d->ln_eps, ws.h, s));
+    if (fp8) MMDIT_HIP(quant_rows(ws.h, L, H, ws.h8, ws.sh, s));
     // a3: QKV
-    MMDIT_HIP(gemm_2(gemm_base(3 * H, H, dt, ws.h, H, MMDIT_EPI_BIAS, ws.qkv, 3 * H),
+    MMDIT_HIP(gemm_2(proj_base(d, 3 * H, H, ws.h, ws.h8, ws.sh, MMDIT_EPI_BIAS, ws.qkv, 3 * H),
                      group(0, Lt, w->txt.qkv), group(Lt, Li, w->img.qkv), s));
     // a4: QK-RMSNorm + RoPE + relayout
     MMDIT_HIP(launch_qknorm_rope(ws.qkv, 3 * H, L, d->heads, d->head_dim, Lt,
@@ -295,8 +346,9 @@ int run_double(const mmdit_dims* d, const mmdit_double_weights* w, const float* 
     // a5: joint attention
     MMDIT_HIP(launch_attention(ws.q, ws.k, ws.vt, d->heads, L, d->head_dim, LP, ws.o, H, s));
     // a6: out projection + gated residual
+    if (fp8) MMDIT_HIP(quant_rows(ws.o, L, H, ws.o8, ws.so, s));
     {
-        GemmArgs g = gemm_base(H, H, dt, ws.o, H, MMDIT_EPI_GATE_RESID, x_out, H);
+        GemmArgs g = proj_base(d, H, H, ws.o, ws.o8, ws.so, MMDIT_EPI_GATE_RESID, x_out, H);
         g.resid = x_in;
         g.ldr = H;
         MMDIT_HIP(gemm_2(g, group(0, Lt, w->txt.proj, mt + 2 * H), group(Lt, Li, w->img.proj, mi + 2 * H), s));
@@ -304,15 +356,17 @@ int run_double(const mmdit_dims* d, const mmdit_double_weights* w, const float* 
     // a7: LN2 + modulate
     MMDIT_HIP(launch_ln_modulate(x_out, L, H, Lt, mt + 3 * H, mt + 4 * H, mi + 3 * H, mi + 4 * H,
                                  d->ln_eps, ws.h, s));
+    if (fp8) MMDIT_HIP(quant_rows(ws.h, L, H, ws.h8, ws.sh, s));
     // a8: fc1 + GELU (or SwiGLU: fc1 rows [gate | up], hidden = SiLU(gate) * up)
     {
         const int epi = d->mlp_act == MMDIT_ACT_SWIGLU ? MMDIT_EPI_SWIGLU : MMDIT_EPI_BIAS_GELU;
-        MMDIT_HIP(gemm_2(gemm_base(mlp_cols(d), H, dt, ws.h, H, epi, ws.a, M),
+        MMDIT_HIP(gemm_2(proj_base(d, mlp_cols(d), H, ws.h, ws.h8, ws.sh, epi, ws.a, M),
                          group(0, Lt, w->txt.fc1), group(Lt, Li, w->img.fc1), s));
     }
+    if (fp8) MMDIT_HIP(quant_rows(ws.a, L, M, ws.a8, ws.sa, s));
     // a9: fc2 + gated residual
     {
-        GemmArgs g = gemm_base(H, M, dt, ws.a, M, MMDIT_EPI_GATE_RESID, x_out, H);
+        GemmArgs g = proj_base(d, H, M, ws.a, ws.a8, ws.sa, MMDIT_EPI_GATE_RESID, x_out, H);
         g.resid = x_out;
         g.ldr = H;
         MMDIT_HIP(gemm_2(g, group(0, Lt, w->txt.fc2, mt + 5 * H), group(Lt, Li, w->img.fc2, mi + 5 * H), s));
@@ -327,10 +381,12 @@ int run_single(const mmdit_dims* d, const mmdit_single_weights* w, const float* 
     const int dt = d->weight_dtype, LP = padded_len(d);
     const float* m = premod ? premod : ws.mod;
     if (!premod) MMDIT_HIP(gemv(vec, H, w->mod, 3 * H, dt, 1, 0, ws.mod, s));
+    const bool fp8 = dt == MMDIT_FP8;
     MMDIT_HIP(launch_ln_modulate(x_in, L, H, 0, m, m + H, m, m + H, d->ln_eps, ws.h, s));
+    if (fp8) MMDIT_HIP(quant_rows(ws.h, L, H, ws.h8, ws.sh, s));
     {
         const int epi = d->mlp_act == MMDIT_ACT_SWIGLU ? MMDIT_EPI_SPLIT_SWIGLU : MMDIT_EPI_SPLIT_GELU;
-        GemmArgs g = gemm_base(3 * H + mlp_cols(d), H, dt, ws.h, H, epi, ws.qkv, 3 * H);
+        GemmArgs g = proj_base(d, 3 * H + mlp_cols(d), H, ws.h, ws.h8, ws.sh, epi, ws.qkv, 3 * H);
         g.split_n = 3 * H;
         g.out2 = ws.cat;
         g.ldo2 = H + M;
@@ -340,8 +396,9 @@ int run_single(const mmdit_dims* d, const mmdit_single_weights* w, const float* 
     MMDIT_HIP(launch_qknorm_rope(ws.qkv, 3 * H, L, d->heads, d->head_dim, L, w->q_norm, w->k_norm,
                                  w->q_norm, w->k_norm, rope, d->rms_eps, LP, ws.q, ws.k, ws.vt, s));
     MMDIT_HIP(launch_attention(ws.q, ws.k, ws.vt, d->heads, L, d->head_dim, LP, ws.cat, H + M, s));
+    if (fp8) MMDIT_HIP(quant_rows(ws.cat, L, H + M, ws.cat8, ws.sc, s));
     {
-        GemmArgs g = gemm_base(H, H + M, dt, ws.cat, H + M, MMDIT_EPI_GATE_RESID, x_out, H);
+        GemmArgs g = proj_base(d, H, H + M, ws.cat, ws.cat8, ws.sc, MMDIT_EPI_GATE_RESID, x_out, H);
         g.resid = x_in;
         g.ldr = H;
         MMDIT_HIP(gemm_1(g, group(0, L, w->linear2, m + 2 * H), s));
@@ -393,6 +450,9 @@ ModBatchWs carve_modbatch(const mmdit_dims* d, int n_steps, Carver& c) {
 
 int model_ok(const mmdit_dims* d, const mmdit_model* m) {
     if (!m) return MMDIT_E_NULL;
+    // fp8 operands are wired into the blocks only (the step's patch embedding
+    // and final projection take 16-bit operands)
+    if (d->weight_dtype == MMDIT_FP8) return MMDIT_E_DTYPE;
     if (d->in_channels < 64 || d->in_channels % 64 != 0) return MMDIT_E_SHAPE;
     if (d->n_double < 0 || d->n_single < 0) return MMDIT_E_SHAPE;
     const int dt = d->weight_dtype;

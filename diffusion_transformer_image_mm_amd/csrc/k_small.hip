@@ -26,8 +26,10 @@ template <int WT, int NL>
 __global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ x, int k, int n,
                                                    int silu_input, int accumulate, const GemvSets sets) {
     constexpr bool INT8 = WT == MMDIT_INT8;
-    constexpr int E = INT8 ? 16 : 8;
-    constexpr int ES = INT8 ? 1 : 2;   // bytes per weight
+    constexpr bool FP8 = WT == MMDIT_FP8;
+    constexpr bool BYTE = INT8 || FP8;  // one byte per weight, a scale per row
+    constexpr int E = BYTE ? 16 : 8;
+    constexpr int ES = BYTE ? 1 : 2;   // bytes per weight
     const int lane = threadIdx.x & 63;
     const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int nw = gridDim.x * 4;
@@ -70,6 +72,16 @@ __global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ x, 
                     const int8_t* e = reinterpret_cast<const int8_t*>(&raw[rr][i]);
 #pragma unroll
                     for (int j = 0; j < 16; ++j) acc += (float)e[j] * xs[i][j];
+                } else if (FP8) {
+                    // e4m3 codes -> fp32 (exact), two per conversion
+                    const uint32_t w[4] = {raw[rr][i].x, raw[rr][i].y, raw[rr][i].z, raw[rr][i].w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], false);
+                        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], true);
+                        acc += lo[0] * xs[i][4 * j] + lo[1] * xs[i][4 * j + 1];
+                        acc += hi[0] * xs[i][4 * j + 2] + hi[1] * xs[i][4 * j + 3];
+                    }
                 } else if (WT == MMDIT_F16) {
                     // fp16 -> fp32 by rescaling the bits: magnitude bits shifted
                     // into the fp32 exponent/mantissa position, times 2^112
@@ -93,7 +105,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ x, 
             if (lane == 0 && row < rows) {
                 const int s = row < n ? 0 : 1, r = row - s * n;
                 const GemvSet& st = sets.s[s];
-                const float y = (INT8 ? acc * st.scale[r] : acc) + bf2f(st.bias[r]);
+                const float y = (BYTE ? acc * st.scale[r] : acc) + bf2f(st.bias[r]);
                 st.out[r] = accumulate ? st.out[r] + y : y;
             }
         }
@@ -114,7 +126,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ x, 
 hipError_t launch_gemv(const float* x, int k, int n, int wtype, int silu_input, int accumulate,
                        const GemvSets& sets, hipStream_t s) {
     if (n <= 0 || sets.count < 1) return hipSuccess;
-    const int E = wtype == MMDIT_INT8 ? 16 : 8;
+    const int E = (wtype == MMDIT_INT8 || wtype == MMDIT_FP8) ? 16 : 8;
     const int nl = (k + 64 * E - 1) / (64 * E);
     const int groups = (sets.count * n + GEMV_RPW - 1) / GEMV_RPW;
     int blocks = (groups + 3) / 4;
@@ -130,6 +142,7 @@ hipError_t launch_gemv(const float* x, int k, int n, int wtype, int silu_input, 
     GEMV_CASE(MMDIT_F16, 1) GEMV_CASE(MMDIT_F16, 2) GEMV_CASE(MMDIT_F16, 3) GEMV_CASE(MMDIT_F16, 4)
     GEMV_CASE(MMDIT_F16, 5) GEMV_CASE(MMDIT_F16, 6) GEMV_CASE(MMDIT_F16, 7) GEMV_CASE(MMDIT_F16, 8)
     GEMV_CASE(MMDIT_INT8, 1) GEMV_CASE(MMDIT_INT8, 2) GEMV_CASE(MMDIT_INT8, 3) GEMV_CASE(MMDIT_INT8, 4)
+    GEMV_CASE(MMDIT_FP8, 1) GEMV_CASE(MMDIT_FP8, 2) GEMV_CASE(MMDIT_FP8, 3) GEMV_CASE(MMDIT_FP8, 4)
 #undef GEMV_CASE
     return hipErrorInvalidValue;
 }

@@ -18,12 +18,16 @@ from . import synth
 class DeviceArena:
     """Owns device tensors so that the addresses in ABI structs stay valid.
     With f16_weights, the bf16 weights of every non-int8 linear are uploaded
-    and re-encoded on the device by mmdit_weights_to_f16 (MMDIT_F16)."""
+    and re-encoded on the device by mmdit_weights_to_f16 (MMDIT_F16); with
+    fp8_weights, quantised per output channel on the device by
+    mmdit_quantize_fp8_rows (MMDIT_FP8: e4m3 codes + fp32 scales)."""
 
-    def __init__(self, device: str = "cuda", f16_weights: bool = False):
+    def __init__(self, device: str = "cuda", f16_weights: bool = False, fp8_weights: bool = False):
+        assert not (f16_weights and fp8_weights)
         self.device = torch.device(device)
         self.keep: List[torch.Tensor] = []
         self.f16_weights = f16_weights
+        self.fp8_weights = fp8_weights
 
     def _hold(self, t: torch.Tensor) -> torch.Tensor:
         self.keep.append(t)
@@ -69,6 +73,11 @@ class DeviceArena:
             q = self.i8(lin.q)
             s = self.f32(lin.s)
             return B.mmdit_linear(q.data_ptr(), s.data_ptr(), b.data_ptr())
+        if self.fp8_weights:
+            codes, scales = to_fp8_weights(self._upload_bf16(lin.w))
+            self._hold(codes)
+            self._hold(scales)
+            return B.mmdit_linear(codes.data_ptr(), scales.data_ptr(), b.data_ptr())
         if self.f16_weights:
             w = self._hold(to_f16_weights(self._upload_bf16(lin.w)))
         else:
@@ -114,6 +123,19 @@ def to_f16_weights(w: torch.Tensor) -> torch.Tensor:
     out = torch.empty(w.shape, dtype=torch.float16, device=w.device)
     B.check(B.mmdit_weights_to_f16(w, out, w.numel(), torch.cuda.current_stream()))
     return out
+
+
+def to_fp8_weights(w: torch.Tensor):
+    """bf16 device weights [n, k] -> (e4m3 codes uint8 [n, k], fp32 scales
+    [n]), one scale per output channel, made by mmdit_quantize_fp8_rows on the
+    current stream (w may be dropped right away, as for to_f16_weights)."""
+    assert w.dtype == torch.bfloat16 and w.is_contiguous() and w.dim() == 2
+    n, k = w.shape
+    codes = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((n,), dtype=torch.float32, device=w.device)
+    B.check(B.mmdit_quantize_fp8_rows(w, B.MMDIT_BF16, n, k, k, codes, k, scales,
+                                      torch.cuda.current_stream()), "quantize fp8 weights")
+    return codes, scales
 
 
 class TimingModel:
@@ -185,14 +207,15 @@ class TimingModel:
         return self._hold((torch.rand(d, generator=self.gen, device=self.dev) + 0.5).to(torch.bfloat16))
 
 
-def dims_for(shp: synth.Shape, int8: bool = False, f16: bool = False) -> B.mmdit_dims:
+def dims_for(shp: synth.Shape, int8: bool = False, f16: bool = False, fp8: bool = False) -> B.mmdit_dims:
     d = B.mmdit_dims()
     d.txt_len, d.img_len = shp.txt_len, shp.img_len
     d.hidden, d.heads, d.head_dim, d.mlp_hidden = shp.hidden, shp.heads, shp.head_dim, shp.mlp
     d.in_channels = shp.in_channels
     d.rope_axes[0], d.rope_axes[1], d.rope_axes[2] = shp.axes
     d.rope_theta, d.ln_eps, d.rms_eps = shp.theta, shp.ln_eps, shp.rms_eps
-    d.weight_dtype = B.MMDIT_INT8 if int8 else (B.MMDIT_F16 if f16 else B.MMDIT_BF16)
+    d.weight_dtype = (B.MMDIT_INT8 if int8 else B.MMDIT_F16 if f16 else B.MMDIT_FP8 if fp8
+                      else B.MMDIT_BF16)
     d.n_double, d.n_single = shp.n_double, shp.n_single
     d.mlp_act = B.MMDIT_ACT_SWIGLU if shp.mlp_act == "swiglu" else B.MMDIT_ACT_GELU_TANH
     d.guidance_embed = 1 if shp.guidance_embed else 0

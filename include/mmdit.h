@@ -86,8 +86,12 @@ enum mmdit_weight_dtype {
                        with an fp32 scale per row (mmdit_gemm.a_scale), and the
                        product runs on the fp8 matrix cores (SGLang-AMD,
                        "Architecture Deep Dive": fp8 on CDNA). Codes and scales
-                       come from mmdit_quantize_fp8_rows. Not accepted by the
-                       block and step entries */
+                       come from mmdit_quantize_fp8_rows. The block entries
+                       accept it for GELU MLPs: every projection's activation
+                       operand is quantised per token right before its GEMM
+                       (LayerNorm outputs, attention output, GELU hidden);
+                       attention and the residual stream are unchanged. The
+                       step entries do not accept it (MMDIT_E_DTYPE) */
 };
 
 /* ------------------------------------------------------------------ sizes */

@@ -226,7 +226,7 @@ def norm_rope_heads(u, g, phi, heads: int, eps: float) -> np.ndarray:
 
 
 def double_block(x, vec, ids, w, shp, rows: Optional[np.ndarray] = None,
-                 return_stages: bool = False):
+                 return_stages: bool = False, fp8: bool = False):
     """Double-stream block ("Flux.2 Klein 9B" and "What the compiler found on
     its own" sections of the Luminal blog).
 
@@ -240,9 +240,14 @@ def double_block(x, vec, ids, w, shp, rows: Optional[np.ndarray] = None,
       x_s += gate1 * (O_s W_proj^T + b)
       x_s += gate2 * (GELU(LN(x_s) * (1 + scale2) + shift2) W_fc1^T + b) W_fc2^T + b)
     With ``rows`` only those output rows are returned (all keys and values
-    are still computed).
+    are still computed). With ``fp8`` every linear takes its fp8 form
+    (``fp8_weights``, ``linear_act_fp8``): projections on per-token fp8
+    activations, the modulation on the fp8 weights alone.
     """
     H, heads, L_t = shp.hidden, shp.heads, shp.txt_len
+    lin = linear_act_fp8 if fp8 else linear
+    if fp8:
+        w = fp8_weights(w)
     x = _f64(x)
     L = x.shape[0]
     phi = rope_angles(ids, shp.axes, shp.theta)
@@ -253,7 +258,7 @@ def double_block(x, vec, ids, w, shp, rows: Optional[np.ndarray] = None,
     for s, sl in seg.items():
         sh1, sc1 = mods[s][0], mods[s][1]
         h = ln_modulate(x[sl], sh1, sc1, shp.ln_eps)
-        qkv = linear(h, w[s]["qkv"])
+        qkv = lin(h, w[s]["qkv"])
         q[sl], k[sl], v[sl] = qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:]
         stages[f"h1_{s}"] = h
         stages[f"qkv_{s}"] = qkv
@@ -272,10 +277,10 @@ def double_block(x, vec, ids, w, shp, rows: Optional[np.ndarray] = None,
         if not mask.any():
             continue
         sh1, sc1, g1, sh2, sc2, g2 = mods[s]
-        xs = xo[mask] + g1 * linear(o[mask], w[s]["proj"])
+        xs = xo[mask] + g1 * lin(o[mask], w[s]["proj"])
         h2 = ln_modulate(xs, sh2, sc2, shp.ln_eps)
-        a = mlp_activation(linear(h2, w[s]["fc1"]), shp.mlp_act)
-        xs = xs + g2 * linear(a, w[s]["fc2"])
+        a = mlp_activation(lin(h2, w[s]["fc1"]), shp.mlp_act)
+        xs = xs + g2 * lin(a, w[s]["fc2"])
         xo[mask] = xs
     if return_stages:
         stages["mods"] = mods
@@ -284,27 +289,31 @@ def double_block(x, vec, ids, w, shp, rows: Optional[np.ndarray] = None,
 
 
 def single_block(x, vec, ids, w, shp, rows: Optional[np.ndarray] = None,
-                 return_stages: bool = False):
+                 return_stages: bool = False, fp8: bool = False):
     """Single-stream block: one set of weights over the joint sequence.
       shift, scale, gate = modulation(vec)
       u = (LN(x) * (1 + scale) + shift) W_1^T + b_1 -> q | k | v | m
       q, k = RMSNorm per head, then RoPE; O = attention(q, k, v)
       x += gate * ([O | GELU(m)] W_2^T + b_2)
+    ``fp8`` as for ``double_block``.
     """
     H, heads = shp.hidden, shp.heads
+    lin = linear_act_fp8 if fp8 else linear
+    if fp8:
+        w = fp8_weights(w)
     x = _f64(x)
     L = x.shape[0]
     phi = rope_angles(ids, shp.axes, shp.theta)
     sh, sc, g = modulation(vec, w["mod"], 3)
     h = ln_modulate(x, sh, sc, shp.ln_eps)
-    u = linear(h, w["linear1"])
+    u = lin(h, w["linear1"])
     q, k, v, m = u[:, :H], u[:, H:2 * H], u[:, 2 * H:3 * H], u[:, 3 * H:]
     q = norm_rope_heads(q, w["q_norm"], phi, heads, shp.rms_eps)
     k = norm_rope_heads(k, w["k_norm"], phi, heads, shp.rms_eps)
     out_rows = np.arange(L) if rows is None else np.asarray(rows)
     o = attention(q, k, v, heads, out_rows)
     cat = np.concatenate([o, mlp_activation(m[out_rows], shp.mlp_act)], axis=1)
-    xo = x[out_rows] + g * linear(cat, w["linear2"])
+    xo = x[out_rows] + g * lin(cat, w["linear2"])
     if return_stages:
         return xo, {"h": h, "u": u, "q": q, "k": k, "v": v, "attn": o, "mod": (sh, sc, g)}
     return xo
@@ -414,3 +423,37 @@ def linear_fp8(a_codes, a_scale, w_codes, w_scale, bias) -> np.ndarray:
     a = _f64(a_scale)[:, None] * _f64(a_codes)
     w = _f64(w_scale)[:, None] * _f64(w_codes)
     return a @ w.T + _f64(bias)[None, :]
+
+
+class Fp8Linear:
+    """A linear layer in its fp8 form: e4m3 code values q [out, in] (decoded,
+    float64) with one fp32 scale per output channel s, and the layer's bias.
+    ``weight_matrix`` reads it as diag(s) q."""
+
+    def __init__(self, q, s, b):
+        self.w, self.q, self.s, self.b = None, q, s, b
+
+
+def fp8_weights(w):
+    """The fp8 form of a block's weights ("Architecture Deep Dive": fp8 on
+    CDNA): every 16-bit weight matrix quantised per output channel exactly as
+    activations are per token (``quantize_rows_fp8``); biases and norm scales
+    stay as they are. Nested dicts are mapped; layers already in fp8 form
+    (and int8 layers) pass through unchanged."""
+    if isinstance(w, dict):
+        return {k: fp8_weights(v) for k, v in w.items()}
+    if getattr(w, "w", None) is None or not hasattr(w, "b"):
+        return w
+    codes, sc = quantize_rows_fp8(w.w)
+    return Fp8Linear(codes, sc, w.b)
+
+
+def linear_act_fp8(x, lin) -> np.ndarray:
+    """A projection of the fp8 path: the activation rows x quantised per token
+    (``quantize_rows_fp8``), times the fp8 weights. The codes are integer
+    decisions, so they are taken on the operand as the fp8 path holds it
+    before quantising: a 16-bit (fp16) activation, divided in fp32."""
+    x16 = np.asarray(x, dtype=np.float64).astype(np.float16)
+    assert np.all(np.isfinite(x16)), "activation outside the fp16 range"
+    codes, sc = quantize_rows_fp8(x16.astype(np.float32))
+    return linear_fp8(codes, sc, lin.q, lin.s, lin.b)

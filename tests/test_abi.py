@@ -200,7 +200,13 @@ def test_weight_conversion_validation():
     assert B.mmdit_weights_to_f16(FAKE, FAKE + 128, 0) == B.MMDIT_OK      # nothing to do
     d = _dims(weight_dtype=B.MMDIT_F16)
     assert B.mmdit_workspace_bytes(d, B.MMDIT_WS_DOUBLE) > 0
-    assert B.mmdit_workspace_bytes(_dims(weight_dtype=3), B.MMDIT_WS_DOUBLE) == 0
+    assert B.mmdit_workspace_bytes(_dims(weight_dtype=4), B.MMDIT_WS_DOUBLE) == 0
+    # fp8 blocks need the extra code and scale buffers; SwiGLU MLPs reject fp8
+    d8 = _dims(weight_dtype=B.MMDIT_FP8)
+    assert B.mmdit_workspace_bytes(d8, B.MMDIT_WS_DOUBLE) > B.mmdit_workspace_bytes(d, B.MMDIT_WS_DOUBLE)
+    assert B.mmdit_workspace_bytes(d8, B.MMDIT_WS_SINGLE) > B.mmdit_workspace_bytes(d, B.MMDIT_WS_SINGLE)
+    assert B.mmdit_workspace_bytes(_dims(weight_dtype=B.MMDIT_FP8, mlp_act=B.MMDIT_ACT_SWIGLU),
+                                   B.MMDIT_WS_DOUBLE) == 0
 
 
 def test_one_hip_runtime_per_process():

@@ -454,20 +454,24 @@ def test_weights_to_f16_exhaustive():
                                                 (18432, 3072, "int8", 1, 0), (3072, 256, "int8", 0, 1),
                                                 (100, 64, "bf16", 0, 1), (18432, 3072, "f16", 1, 0),
                                                 (100, 64, "f16", 0, 1), (101, 4096, "bf16", 1, 0),
-                                                (7, 1024, "int8", 1, 1), (9, 4096, "int8", 0, 0)])
+                                                (7, 1024, "int8", 1, 1), (9, 4096, "int8", 0, 0),
+                                                (18432, 3072, "fp8", 1, 0), (9216, 3072, "fp8", 1, 1),
+                                                (33, 64, "fp8", 0, 1), (101, 4096, "fp8", 1, 0)])
 def test_gemv(n, k, wt, silu_in, acc):
+    """fp8 weights: against the fp64 product with the decoded codes (the
+    activation stays fp32 in the modulation GEMV)."""
     say(f"gemv n={n} k={k} weights={wt}")
-    int8, f16 = wt == "int8", wt == "f16"
-    A = DeviceArena(f16_weights=f16)
+    int8, f16, fp8 = wt == "int8", wt == "f16", wt == "fp8"
+    A = DeviceArena(f16_weights=f16, fp8_weights=fp8)
     x = rnd(80, (k,))
     lin = _lin(81, n, k, int8)
     base = rnd(83, (n,))
     out = A.f32(base)
-    dt = B.MMDIT_INT8 if int8 else (B.MMDIT_F16 if f16 else B.MMDIT_BF16)
+    dt = B.MMDIT_INT8 if int8 else (B.MMDIT_F16 if f16 else B.MMDIT_FP8 if fp8 else B.MMDIT_BF16)
     B.check(B.mmdit_k_gemv(A.f32(x), k, A.linear(lin), n, dt, silu_in, acc, out, stream()))
     sync()
     xin = O.silu(x) if silu_in else x
-    ref = O.linear(xin[None, :], lin)[0] + (base if acc else 0)
+    ref = O.linear(xin[None, :], O.fp8_weights(lin) if fp8 else lin)[0] + (base if acc else 0)
     assert rel_err(out.cpu().numpy(), ref) <= 1e-4
 
 
