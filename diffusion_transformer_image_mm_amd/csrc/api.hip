@@ -705,7 +705,7 @@ int mmdit_k_qknorm_rope(const mmdit_bf16* qkv, int ld, int seq, int heads, int h
 int mmdit_k_attention(const mmdit_bf16* q, const mmdit_bf16* k, const mmdit_bf16* vt, int heads, int seq,
                       int head_dim, int l_pad, mmdit_bf16* out, int ldo, hipStream_t s) {
     if (head_dim != 64 && head_dim != 128) return MMDIT_E_SHAPE;
-    if (seq < 1 || heads < 1 || l_pad < seq || l_pad % 64 != 0) return MMDIT_E_SHAPE;
+    if (seq < 1 || heads < 1 || l_pad < seq || l_pad % 64 != 0 || l_pad >= (1 << 24)) return MMDIT_E_SHAPE;
     if (ldo < heads * head_dim || ldo % 8 != 0) return MMDIT_E_SHAPE;
     for (const void* p : {(const void*)q, (const void*)k, (const void*)vt, (const void*)out})
         MMDIT_TRY(check_ptr(p));

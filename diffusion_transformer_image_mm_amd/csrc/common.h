@@ -132,6 +132,9 @@ struct GemmArgs {
     // ones, so that a partial last round of 256-wide tiles becomes half as long.
     int tail_rows;
     int full_tiles;
+    // Set by the launcher: the first head_rows row tiles run as 128-wide
+    // tiles ahead of the 256-wide ones (0: none).
+    int head_rows;
     const float* a_scale;   // fp32 per row of A, fp8 operands only
 };
 

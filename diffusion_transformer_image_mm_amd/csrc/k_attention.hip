@@ -24,9 +24,14 @@
 //   swapped, so a lane's 8 keys are one 16-byte LDS read (the 16 lanes served
 //   together hit 16 distinct bank groups);
 // * K and V^T tiles go global -> LDS with 16-byte direct-to-LDS loads into
-//   two distinct LDS buffers (double buffering; distinct variables let the
-//   compiler see that the next tile's loads do not alias this tile's reads);
-//   chunk positions are XOR-swizzled by row to spread LDS banks;
+//   two distinct LDS buffers (double buffering); chunk positions are
+//   XOR-swizzled by row to spread LDS banks. The loads are written as
+//   instructions (a wave-uniform base plus 32-bit lane offsets, the LDS
+//   destination in m0): the compiler then counts the fragment reads exactly
+//   and each MFMA waits only for its own operand, with the 16 fragment reads
+//   of a phase issued four ahead of the MFMAs that consume them (with the
+//   compiler's load builtin every MFMA waited for all reads in flight);
+//   the kernel orders its LDS accesses itself with waits and barriers;
 // * the last key tile masks keys >= seq_len to -inf; query rows >= seq_len
 //   are computed on zero padding and not stored;
 // * O is stored as fp16: it is the activation operand of the output
@@ -38,8 +43,23 @@ namespace mmdit {
 namespace {
 typedef __attribute__((address_space(3))) void lds_void;
 MMDIT_DEV void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// 16-byte direct global -> LDS load (lane i writes lds_base + 16 i), written
+// as an instruction so that the compiler's wait counting does not treat it as
+// an LDS access of unknown extent.
 MMDIT_DEV void g2l_16(const void* gsrc, lds_void* lds_base) {
-    __builtin_amdgcn_global_load_lds(gsrc, lds_base, 16, 0, 0);
+    const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(l), "v"(gsrc) : "memory", "m0");
+}
+// Schedule of one 16-read, 16-MFMA phase: four reads ahead, then one MFMA and
+// one read alternately, then the last four MFMAs.
+MMDIT_DEV void read_ahead_schedule() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // LDS reads
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 }  // namespace
 
@@ -77,7 +97,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
     int bid = blockIdx.x;
     if (total % 8 == 0) bid = (bid % 8) * (total / 8) + bid / 8;
     const int h = bid / nq, qt = bid % nq;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 5, r32 = lane & 31;
     const int qrow = qt * 128 + wave * 32 + r32;
 
@@ -87,37 +107,42 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
     bf16x8_t qf[D / 16];
 #pragma unroll
     for (int ds = 0; ds < D / 16; ++ds) qf[ds] = *reinterpret_cast<const bf16x8_t*>(qp + ds * 16);
+    // Q has landed before the loop: the compiler does not see the K/V loads,
+    // so a first-use wait for Q inside the loop would wait for those instead.
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) asm volatile("" ::"v"(qf[ds]));
 
-    // ---- load descriptors
-    const uint16_t* kbase = k + (size_t)h * l_pad * D;
-    const uint16_t* vbase = vt + (size_t)h * D * l_pad;
-    const char* k_src[T::K_LPW];
+    // ---- load descriptors: wave-uniform head bases, 32-bit lane offsets
+    // (l_pad < 2^24 keeps every offset below 2^32)
+    const char* kbase = reinterpret_cast<const char*>(k + (size_t)h * l_pad * D);
+    const char* vbase = reinterpret_cast<const char*>(vt + (size_t)h * D * l_pad);
+    uint32_t k_src[T::K_LPW];
     int k_dst[T::K_LPW];
 #pragma unroll
     for (int j = 0; j < T::K_LPW; ++j) {
         const int first = (wave * T::K_LPW + j) * T::K_RPI;
         const int r = first + lane / T::CPR;
         const int c = (lane % T::CPR) ^ (r & (T::CPR - 1));
-        k_src[j] = reinterpret_cast<const char*>(kbase + (size_t)r * D + c * 8);
+        k_src[j] = (uint32_t)(r * D + c * 8) * 2u;
         k_dst[j] = first * T::RB;
     }
-    const char* v_src[T::V_LPW];
+    uint32_t v_src[T::V_LPW];
     int v_dst[T::V_LPW];
 #pragma unroll
     for (int j = 0; j < T::V_LPW; ++j) {
         const int first = (wave * T::V_LPW + j) * 8;
         const int d = first + lane / 8;
         const int c = (lane % 8) ^ ((d >> 1) & 7);
-        v_src[j] = reinterpret_cast<const char*>(vbase + (size_t)d * l_pad + c * 8);
+        v_src[j] = ((uint32_t)d * (uint32_t)l_pad + (uint32_t)(c * 8)) * 2u;
         v_dst[j] = first * 128;
     }
     auto issue = [&](int t, char* sK, char* sV) {
-        const size_t koff = (size_t)t * T::KV * T::RB;  // bytes along the key rows
-        const size_t voff = (size_t)t * T::KV * 2;      // bytes along a V^T row
+        const uint32_t koff = (uint32_t)t * T::KV * T::RB;  // bytes along the key rows
+        const uint32_t voff = (uint32_t)t * T::KV * 2;      // bytes along a V^T row
 #pragma unroll
-        for (int j = 0; j < T::K_LPW; ++j) g2l_16(k_src[j] + koff, (lds_void*)(sK + k_dst[j]));
+        for (int j = 0; j < T::K_LPW; ++j) g2l_16(kbase + (k_src[j] + koff), (lds_void*)(sK + k_dst[j]));
 #pragma unroll
-        for (int j = 0; j < T::V_LPW; ++j) g2l_16(v_src[j] + voff, (lds_void*)(sV + v_dst[j]));
+        for (int j = 0; j < T::V_LPW; ++j) g2l_16(vbase + (v_src[j] + voff), (lds_void*)(sV + v_dst[j]));
     };
 
     // ---- fragment offsets
@@ -164,6 +189,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
                 s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s[st], 0, 0, 0);
             }
         }
+        if constexpr (D == 128) read_ahead_schedule();
         // element i of s[st]: key t*64 + st*32 + 8*(i/4) + 4g + i%4
         const int kv0 = t * T::KV;
         if (kv0 + T::KV > seq_len) {
@@ -216,6 +242,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
                 const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(sV + v_off[dt][u]);
                 o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[u], o[dt], 0, 0, 0);
             }
+        if constexpr (D == 128) read_ahead_schedule();
     };
 
     issue(0, sK0, sV0);
@@ -255,6 +282,7 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
                             int seq_len, int head_dim, int l_pad, uint16_t* out, int ldo,
                             hipStream_t s) {
     if (seq_len <= 0) return hipSuccess;
+    if (l_pad >= (1 << 24)) return hipErrorInvalidValue;   // 32-bit load offsets
     dim3 grid(((seq_len + 127) / 128) * heads), block(256);
     const float c_log2 = 1.4426950408889634f / sqrtf((float)head_dim);
     if (head_dim == 128)

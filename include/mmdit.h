@@ -364,7 +364,7 @@ int mmdit_k_qknorm_rope(const mmdit_bf16* qkv, int ld, int seq_len, int heads, i
  * its own" and "The AMD MI300X pipeline": fused, tiled softmax(QK^T)V).
  *   q, k: bf16 [heads, l_pad, D]; vt: bf16 [heads, D, l_pad] in the
  *   quad-swapped key order written by mmdit_k_qknorm_rope (zero beyond
- *   seq_len); l_pad a multiple of 64; scale 1/sqrt(D).
+ *   seq_len); l_pad a multiple of 64 and below 2^24; scale 1/sqrt(D).
  *   out: fp16 [seq_len, ldo], head h at columns [h*D, (h+1)*D).
  */
 int mmdit_k_attention(const mmdit_bf16* q, const mmdit_bf16* k, const mmdit_bf16* vt,
