@@ -49,8 +49,8 @@
 //   launch (768 + 192 tiles: the last round becomes half as long); every
 //   output element sees the same k-order either way (bit-identical);
 // * head tiles: in a grouped launch the text-stream group (at most two row
-//   tiles, weight slabs shared by only two tiles, so HBM-latency bound) runs
-//   as 128-wide tiles dispatched first (see launch_gemm_t);
+//   tiles, weight slabs shared by only two tiles, so HBM-latency bound) can
+//   run as 128-wide tiles dispatched first (the rule is in launch_gemm_t);
 // * SwiGLU epilogues (a gated MLP, Luminal blog section "What the compiler
 //   found on its own": the fused SwiGLU activation of Flux.2 Klein): the
 //   weight keeps its natural layout, rows [gate (M) | up (M)]. A tile covers
@@ -565,6 +565,29 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) 
     gemm_tile<WT, EPI, PIPE, 4>(args, smem, blockIdx.x, nf, 0, tmt - args.tail_rows);
 }
 
+// Length, in half tile-times, of a launch that dispatches n_half tiles of
+// half a tile-time and then n_full tiles of one tile-time, in grid order,
+// each to the first compute unit that becomes free (cus units).
+static int launch_half_units(int n_half, int n_full, int cus) {
+    int freed[3] = {cus, 0, 0};   // units that become free at t, t + 1, t + 2
+    int end = 0;
+    for (int t = 0; n_half + n_full > 0; ++t) {
+        int avail = freed[t % 3];
+        freed[t % 3] = 0;
+        const int h = avail < n_half ? avail : n_half;
+        n_half -= h;
+        avail -= h;
+        const int f = avail < n_full ? avail : n_full;
+        n_full -= f;
+        freed[(t + 1) % 3] += h;
+        freed[(t + 2) % 3] += f;
+        if (h) end = end > t + 1 ? end : t + 1;
+        if (f) end = end > t + 2 ? end : t + 2;
+        freed[(t + 1) % 3] += avail - f;   // idle units stay free
+    }
+    return end;
+}
+
 // Compute units of the current device (queried once per device).
 static int cu_count() {
     static int cached[16] = {0};
@@ -608,20 +631,29 @@ static hipError_t launch_gemm_t(const GemmArgs& a0, hipStream_t s) {
     a.full_tiles = (tmt - a.tail_rows) * tn;
     int tiles = a.full_tiles + a.tail_rows * ((a.n + BN / 2 - 1) / (BN / 2));
     // Head tiles: in a grouped launch whose first group has at most two row
-    // tiles (the text stream: 512 rows), that group runs as 128-wide tiles
-    // dispatched ahead of the 256-wide ones. Its weight slabs are shared by
-    // only two tiles, so its k-steps wait on HBM, not L2; in a launch of one
-    // round (the output and MLP-out projections: 216 tiles on 256 CUs) those
-    // tiles set the end of the launch, and halving their work per k-step
-    // (48 narrow tiles use 24 of the otherwise idle CUs) shortens it.
-    // Measured on the FLUX double block: 1.430 -> 1.408 ms; outputs are
+    // tiles (the text stream: 512 rows), that group can run as 128-wide tiles
+    // dispatched ahead of the 256-wide ones, in place of tail tiles. Its
+    // weight slabs are shared by only two tiles, so its k-steps wait on HBM,
+    // not L2, and its tiles are the slowest of the launch; halved and started
+    // first they no longer set its end. They are used when, counting every
+    // 256-wide tile as one tile-time, the launch gets no longer than with the
+    // plain (or tail-tile) dispatch: the FLUX double block's four projections
+    // (216, 648, 864 tiles: ties), not Flux.2 Klein's QKV at 512x512 (480
+    // tiles: 2 -> 2.5 tile-times) or its launches of whole rounds. Measured:
+    // FLUX double block 1.455 -> 1.431 ms and 1.430 -> 1.408 ms (same-process
+    // A/B on two boxes; a third showed no change), Klein double block at
+    // 512x512 1.359 -> 1.341 ms, larger Klein blocks unchanged; outputs are
     // bit-identical (every element keeps its k-order).
     a.head_rows = 0;
     {
         const int tm0g = (a.g[0].m + BM - 1) / BM;
         const int tn2 = (a.n + BN / 2 - 1) / (BN / 2);
-        if (WT != MMDIT_FP8 && !swiglu && a.ngroups == 2 && a.tail_rows == 0 && tm0g <= 2 && (tm0g * tn2) % 8 == 0) {
+        const int now = a.tail_rows ? launch_half_units(0, a.full_tiles, cus) + 1
+                                    : launch_half_units(0, tmt * tn, cus);
+        if (WT != MMDIT_FP8 && !swiglu && a.ngroups == 2 && tm0g <= 2 && (tm0g * tn2) % 8 == 0 &&
+            launch_half_units(tm0g * tn2, (tmt - tm0g) * tn, cus) <= now) {
             a.head_rows = tm0g;
+            a.tail_rows = 0;
             a.full_tiles = (tmt - tm0g) * tn;
             tiles = a.full_tiles + tm0g * tn2;
         }
