@@ -470,37 +470,43 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
         }
         return;
     }
+    // Per-column values of the lane's 4 x TN output columns, then the rows:
+    // the TN stores of one row (its 16 x TN columns, i.e. whole 128-byte lines
+    // of 16-bit output) are issued back to back.
+    float b[TN][4], sc[TN][4], gt[TN][4];
 #pragma unroll
     for (int in = 0; in < TN; ++in) {
         const int n = nb + in * 16;
-        if (n >= N) continue;
-        const uint2 braw = *reinterpret_cast<const uint2*>(G.bias + n);
-        const float b[4] = {bf2f(braw.x & 0xffff), bf2f(braw.x >> 16), bf2f(braw.y & 0xffff),
-                            bf2f(braw.y >> 16)};
-        float sc[4] = {1.f, 1.f, 1.f, 1.f};
-        if (INT8 || FP8) {
-            const float4 s4 = *reinterpret_cast<const float4*>(G.scale + n);
-            sc[0] = s4.x; sc[1] = s4.y; sc[2] = s4.z; sc[3] = s4.w;
-        }
-        float gt[4] = {0.f, 0.f, 0.f, 0.f};
-        if (EPI == MMDIT_EPI_GATE_RESID) {
-            const float4 g4 = *reinterpret_cast<const float4*>(G.gate + n);
-            gt[0] = g4.x; gt[1] = g4.y; gt[2] = g4.z; gt[3] = g4.w;
-        }
+        const int nc = n < N ? n : nb;   // out-of-range columns are not stored
+        const uint2 braw = *reinterpret_cast<const uint2*>(G.bias + nc);
+        b[in][0] = bf2f(braw.x & 0xffff); b[in][1] = bf2f(braw.x >> 16);
+        b[in][2] = bf2f(braw.y & 0xffff); b[in][3] = bf2f(braw.y >> 16);
 #pragma unroll
-        for (int im = 0; im < TM; ++im) {
-            const int m = mb + im * 16;
-            if (m >= M) continue;
-            const size_t grow = (size_t)(G.row0 + m);
+        for (int j = 0; j < 4; ++j) { sc[in][j] = 1.f; gt[in][j] = 0.f; }
+        if (INT8 || FP8) {
+            const float4 s4 = *reinterpret_cast<const float4*>(G.scale + nc);
+            sc[in][0] = s4.x; sc[in][1] = s4.y; sc[in][2] = s4.z; sc[in][3] = s4.w;
+        }
+        if (EPI == MMDIT_EPI_GATE_RESID) {
+            const float4 g4 = *reinterpret_cast<const float4*>(G.gate + nc);
+            gt[in][0] = g4.x; gt[in][1] = g4.y; gt[in][2] = g4.z; gt[in][3] = g4.w;
+        }
+    }
+#pragma unroll
+    for (int im = 0; im < TM; ++im) {
+        const int m = mb + im * 16;
+        if (m >= M) continue;
+        const size_t grow = (size_t)(G.row0 + m);
+        float sa = 1.f;
+        if (FP8) sa = args.a_scale[grow];   // the row's activation scale
+#pragma unroll
+        for (int in = 0; in < TN; ++in) {
+            const int n = nb + in * 16;
+            if (n >= N) continue;
             float y[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) y[j] = acc[in][im][j] * sc[j] + b[j];
-            if (FP8) {
-                // the row's activation scale: y = (sum * a_scale) * w_scale + b
-                const float sa = args.a_scale[grow];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) y[j] = (acc[in][im][j] * sa) * sc[j] + b[j];
-            }
+            for (int j = 0; j < 4; ++j)
+                y[j] = FP8 ? (acc[in][im][j] * sa) * sc[in][j] + b[in][j] : acc[in][im][j] * sc[in][j] + b[in][j];
             if (EPI == MMDIT_EPI_BIAS || EPI == MMDIT_EPI_SPLIT_SWIGLU ||
                 (EPI == MMDIT_EPI_SPLIT_GELU && n < args.split_n)) {
                 // attention-side operands (q, k, v): bf16
@@ -520,8 +526,8 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
                 *reinterpret_cast<uint2*>(o) = make_uint2(pack2h(y[0], y[1]), pack2h(y[2], y[3]));
             } else if (EPI == MMDIT_EPI_GATE_RESID) {
                 const float4 r = *reinterpret_cast<const float4*>(args.resid + grow * args.ldr + n);
-                float4 o4 = make_float4(r.x + gt[0] * y[0], r.y + gt[1] * y[1], r.z + gt[2] * y[2],
-                                        r.w + gt[3] * y[3]);
+                float4 o4 = make_float4(r.x + gt[in][0] * y[0], r.y + gt[in][1] * y[1], r.z + gt[in][2] * y[2],
+                                        r.w + gt[in][3] * y[3]);
                 *reinterpret_cast<float4*>(static_cast<float*>(args.out) + grow * args.ldo + n) = o4;
             } else if (EPI == MMDIT_EPI_BIAS_F32) {
                 *reinterpret_cast<float4*>(static_cast<float*>(args.out) + grow * args.ldo + n) =
