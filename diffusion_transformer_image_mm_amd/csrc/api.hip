@@ -263,7 +263,7 @@ hipError_t gemv_2(const float* x, int k, const mmdit_linear& l0, float* out0, co
 }
 
 GemmGroup group(int row0, int m, const mmdit_linear& l, const float* gate = nullptr) {
-    GemmGroup g;
+    GemmGroup g = {};
     g.row0 = row0;
     g.m = m;
     g.w = l.w;
@@ -336,13 +336,34 @@ int run_double(const mmdit_dims* d, const mmdit_double_weights* w, const float* 
     // a2: LN1 + modulate
     MMDIT_HIP(launch_ln_modulate(x_in, L, H, Lt, mt, mt + H, mi, mi + H, d->ln_eps, ws.h, s));
     if (fp8) MMDIT_HIP(quant_rows(ws.h, L, H, ws.h8, ws.sh, s));
-    // a3: QKV
-    MMDIT_HIP(gemm_2(proj_base(d, 3 * H, H, ws.h, ws.h8, ws.sh, MMDIT_EPI_BIAS, ws.qkv, 3 * H),
-                     group(0, Lt, w->txt.qkv), group(Lt, Li, w->img.qkv), s));
-    // a4: QK-RMSNorm + RoPE + relayout
-    MMDIT_HIP(launch_qknorm_rope(ws.qkv, 3 * H, L, d->heads, d->head_dim, Lt,
-                                 w->txt.q_norm, w->txt.k_norm, w->img.q_norm, w->img.k_norm, rope,
-                                 d->rms_eps, LP, ws.q, ws.k, ws.vt, s));
+    if (H % 256 == 0) {
+        // a3 + a4: QKV projection whose epilogue applies the per-head
+        // RMSNorm of q and k and RoPE and writes q, k and v^T in the layout
+        // the attention kernel reads (a 256-wide tile lies in one of q|k|v)
+        GemmArgs g = proj_base(d, 3 * H, H, ws.h, ws.h8, ws.sh, EPI_QKV_ATTN, nullptr, 0);
+        g.q_out = ws.q;
+        g.k_out = ws.k;
+        g.vt_out = ws.vt;
+        g.l_pad = LP;
+        g.head_dim = d->head_dim;
+        g.rope = rope;
+        g.rms_eps = d->rms_eps;
+        GemmGroup gt = group(0, Lt, w->txt.qkv), gi = group(Lt, Li, w->img.qkv);
+        gt.qn = w->txt.q_norm;
+        gt.kn = w->txt.k_norm;
+        gi.qn = w->img.q_norm ? w->img.q_norm : w->txt.q_norm;
+        gi.kn = w->img.k_norm ? w->img.k_norm : w->txt.k_norm;
+        MMDIT_HIP(gemm_2(g, gt, gi, s));
+        MMDIT_HIP(launch_zero_attn_pad(ws.q, ws.k, ws.vt, d->heads, d->head_dim, L, LP, s));
+    } else {
+        // a3: QKV
+        MMDIT_HIP(gemm_2(proj_base(d, 3 * H, H, ws.h, ws.h8, ws.sh, MMDIT_EPI_BIAS, ws.qkv, 3 * H),
+                         group(0, Lt, w->txt.qkv), group(Lt, Li, w->img.qkv), s));
+        // a4: QK-RMSNorm + RoPE + relayout
+        MMDIT_HIP(launch_qknorm_rope(ws.qkv, 3 * H, L, d->heads, d->head_dim, Lt,
+                                     w->txt.q_norm, w->txt.k_norm, w->img.q_norm, w->img.k_norm, rope,
+                                     d->rms_eps, LP, ws.q, ws.k, ws.vt, s));
+    }
     // a5: joint attention
     MMDIT_HIP(launch_attention(ws.q, ws.k, ws.vt, d->heads, L, d->head_dim, LP, ws.o, H, s));
     // a6: out projection + gated residual

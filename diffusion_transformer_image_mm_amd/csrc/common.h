@@ -108,7 +108,15 @@ struct GemmGroup {
     const float* scale;
     const uint16_t* bias;
     const float* gate;
+    const uint16_t* qn;   // EPI_QKV_ATTN: RMSNorm scales [D] of q and k (bf16)
+    const uint16_t* kn;
 };
+
+// Internal epilogue of the double block's QKV projection (not accepted by the
+// per-kernel entry): columns [q | k | v] of the joint sequence; q and k get
+// per-head RMSNorm and RoPE and go to [heads, l_pad, D], v to the transposed,
+// quad-swapped [heads, D, l_pad] layout the attention kernel reads.
+constexpr int EPI_QKV_ATTN = 64;
 
 struct GemmArgs {
     int n, k;
@@ -136,7 +144,18 @@ struct GemmArgs {
     // tiles ahead of the 256-wide ones (0: none).
     int head_rows;
     const float* a_scale;   // fp32 per row of A, fp8 operands only
+    // EPI_QKV_ATTN only
+    uint16_t* q_out;        // [heads, l_pad, D] bf16
+    uint16_t* k_out;
+    uint16_t* vt_out;       // [heads, D, l_pad] bf16
+    int l_pad, head_dim;
+    const float* rope;      // [L, D/2, 2] fp32 (cos, sin) per pair
+    float rms_eps;
 };
+
+// Rows [seq_len, l_pad) of the attention operands as zeros.
+hipError_t launch_zero_attn_pad(uint16_t* q, uint16_t* k, uint16_t* vt, int heads, int head_dim, int seq_len,
+                                int l_pad, hipStream_t s);
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 

@@ -51,6 +51,13 @@
 // * head tiles: in a grouped launch the text-stream group (at most two row
 //   tiles, weight slabs shared by only two tiles, so HBM-latency bound) can
 //   run as 128-wide tiles dispatched first (the rule is in launch_gemm_t);
+// * the double block's QKV epilogue (EPI_QKV_ATTN) does the per-head QK
+//   RMSNorm and RoPE in fp32 on the accumulators (the row's sum of squares
+//   over a head: in-lane, then lanes ^16 and ^32, then the wavefronts that
+//   share the head through LDS) and writes q, k and v^T straight into the
+//   attention kernel's layouts, so the bf16 qkv round trip and its separate
+//   kernel disappear (SGLang-AMD "Architecture Deep Dive" fuses QK
+//   normalisation with RoPE; here it also joins the projection);
 // * SwiGLU epilogues (a gated MLP, Luminal blog section "What the compiler
 //   found on its own": the fused SwiGLU activation of Flux.2 Klein): the
 //   weight keeps its natural layout, rows [gate (M) | up (M)]. A tile covers
@@ -470,6 +477,105 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
         }
         return;
     }
+    if constexpr (EPI == EPI_QKV_ATTN) {
+        // Columns [q | k | v] (H = n / 3 each, a multiple of the tile width, so
+        // a tile lies in one of them). y = acc * s + b stays in fp32 here.
+        const int H = N / 3, D = args.head_dim, seg = tc.n0 / H;
+#pragma unroll
+        for (int in = 0; in < TN; ++in) {
+            const int n = nb + in * 16;
+            const uint2 braw = *reinterpret_cast<const uint2*>(G.bias + n);
+            const float b[4] = {bf2f(braw.x & 0xffff), bf2f(braw.x >> 16), bf2f(braw.y & 0xffff), bf2f(braw.y >> 16)};
+            float sc[4] = {1.f, 1.f, 1.f, 1.f};
+            if (INT8 || FP8) {
+                const float4 s4 = *reinterpret_cast<const float4*>(G.scale + n);
+                sc[0] = s4.x; sc[1] = s4.y; sc[2] = s4.z; sc[3] = s4.w;
+            }
+#pragma unroll
+            for (int im = 0; im < TM; ++im) {
+                float sa = 1.f;
+                if (FP8) {
+                    const int m = mb + im * 16;
+                    sa = args.a_scale[G.row0 + (m < M ? m : M - 1)];
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[in][im][j] = (acc[in][im][j] * sa) * sc[j] + b[j];
+            }
+        }
+        if (seg < 2) {
+            // RMSNorm over each head's D columns: lane sums over its 4 x TN
+            // columns, then over the 4 lanes of its row (lane ^ 16, ^ 32), then
+            // over the wavefronts that share the head, through LDS.
+            float* red = reinterpret_cast<float*>(smem);   // [4 column waves][256 rows]
+            __syncthreads();                                // the main loop's LDS reads are done
+#pragma unroll
+            for (int im = 0; im < TM; ++im) {
+                float p = 0.f;
+#pragma unroll
+                for (int in = 0; in < TN; ++in)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) p += acc[in][im][j] * acc[in][im][j];
+                p += __shfl_xor(p, 16, 64);
+                p += __shfl_xor(p, 32, 64);
+                if (lg == 0) red[wn * 256 + wm * 128 + im * 16 + lr] = p;
+            }
+            __syncthreads();
+            const int wph = D / (16 * TNW);        // wavefronts per head: 1, 2 or 4
+            const int w0 = (wn / wph) * wph;
+            const uint16_t* gsc = seg == 0 ? G.qn : G.kn;
+            uint16_t* dst = seg == 0 ? args.q_out : args.k_out;
+            const int nsb = nb - seg * H;           // the lane's first column within q (or k)
+            const int h = nsb / D;                  // every column of a wavefront is in one head
+            float gs[TN][4];
+#pragma unroll
+            for (int in = 0; in < TN; ++in) {
+                const uint2 graw = *reinterpret_cast<const uint2*>(gsc + (nsb + in * 16) % D);
+                gs[in][0] = bf2f(graw.x & 0xffff); gs[in][1] = bf2f(graw.x >> 16);
+                gs[in][2] = bf2f(graw.y & 0xffff); gs[in][3] = bf2f(graw.y >> 16);
+            }
+            const float inv_d = 1.0f / (float)D;
+#pragma unroll
+            for (int im = 0; im < TM; ++im) {
+                const int m = mb + im * 16;
+                if (m >= M) continue;
+                float ss = 0.f;
+                for (int w = 0; w < wph; ++w) ss += red[(w0 + w) * 256 + wm * 128 + im * 16 + lr];
+                const float rstd = 1.0f / sqrtf(ss * inv_d + args.rms_eps);
+                const size_t t = (size_t)(G.row0 + m);
+#pragma unroll
+                for (int in = 0; in < TN; ++in) {
+                    const int dl = (nsb + in * 16) % D;   // 4 consecutive dims dl..dl+3: pairs dl/2, dl/2+1
+                    const float4 cs = *reinterpret_cast<const float4*>(args.rope + (t * (D / 2) + dl / 2) * 2);
+                    const float a0 = acc[in][im][0] * rstd * gs[in][0], b0 = acc[in][im][1] * rstd * gs[in][1];
+                    const float a1 = acc[in][im][2] * rstd * gs[in][2], b1 = acc[in][im][3] * rstd * gs[in][3];
+                    *reinterpret_cast<uint2*>(dst + ((size_t)h * args.l_pad + t) * D + dl) =
+                        make_uint2(pack2bf(a0 * cs.x - b0 * cs.y, a0 * cs.y + b0 * cs.x),
+                                   pack2bf(a1 * cs.z - b1 * cs.w, a1 * cs.w + b1 * cs.z));
+                }
+            }
+        } else {
+            // v: transposed; inside each aligned group of 16 keys the quads are
+            // stored in the order 0, 2, 1, 3 (the attention kernel's operand order)
+            const int nsb = nb - 2 * H;
+            const int h = nsb / D;
+#pragma unroll
+            for (int im = 0; im < TM; ++im) {
+                const int m = mb + im * 16;
+                if (m >= M) continue;
+                const int t = G.row0 + m;
+                const int qd = (t >> 2) & 3;
+                const int pos = (t & ~15) | ((((qd & 1) << 1) | (qd >> 1)) << 2) | (t & 3);
+#pragma unroll
+                for (int in = 0; in < TN; ++in) {
+                    const int dl = (nsb + in * 16) % D;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        args.vt_out[((size_t)h * D + dl + j) * args.l_pad + pos] = f2bf(acc[in][im][j]);
+                }
+            }
+        }
+        return;
+    }
     // Per-column values of the lane's 4 x TN output columns, then the rows:
     // the TN stores of one row (its 16 x TN columns, i.e. whole 128-byte lines
     // of 16-bit output) are issued back to back.
@@ -691,10 +797,38 @@ static hipError_t launch_gemm_t(const GemmArgs& a0, hipStream_t s) {
         GEMM_CASE(MMDIT_EPI_EULER)
         GEMM_CASE(MMDIT_EPI_SWIGLU)
         GEMM_CASE(MMDIT_EPI_SPLIT_SWIGLU)
+        GEMM_CASE(EPI_QKV_ATTN)
         default:
             return hipErrorInvalidValue;
     }
 #undef GEMM_CASE
+    return hipGetLastError();
+}
+
+// Rows [seq_len, l_pad) of q, k [heads, l_pad, D] and of v^T [heads, D,
+// l_pad] (at their quad-swapped positions) as zeros: padded keys stay finite.
+__global__ void zero_attn_pad_kernel(uint16_t* q, uint16_t* k, uint16_t* vt, int heads, int D, int seq_len,
+                                     int l_pad) {
+    const int pad = l_pad - seq_len;
+    const size_t per = (size_t)heads * pad * D;   // elements per tensor
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < per; i += (size_t)gridDim.x * blockDim.x) {
+        const int d = (int)(i % D);
+        const size_t r = i / D;
+        const int h = (int)(r / pad), t = seq_len + (int)(r % pad);
+        q[((size_t)h * l_pad + t) * D + d] = 0;
+        k[((size_t)h * l_pad + t) * D + d] = 0;
+        const int qd = (t >> 2) & 3;
+        const int pos = (t & ~15) | ((((qd & 1) << 1) | (qd >> 1)) << 2) | (t & 3);
+        vt[((size_t)h * D + d) * l_pad + pos] = 0;
+    }
+}
+
+hipError_t launch_zero_attn_pad(uint16_t* q, uint16_t* k, uint16_t* vt, int heads, int head_dim, int seq_len,
+                                int l_pad, hipStream_t s) {
+    if (l_pad <= seq_len) return hipSuccess;
+    const size_t per = (size_t)heads * (l_pad - seq_len) * head_dim;
+    const int blocks = (int)((per + 255) / 256 < 1024 ? (per + 255) / 256 : 1024);
+    hipLaunchKernelGGL(zero_attn_pad_kernel, dim3(blocks), dim3(256), 0, s, q, k, vt, heads, head_dim, seq_len, l_pad);
     return hipGetLastError();
 }
 
