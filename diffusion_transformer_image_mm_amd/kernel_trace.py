@@ -20,11 +20,12 @@ from collections import defaultdict
 DOMINANT = "mmdit::gemm_kernel<2, 1, 0>"
 FLOPS = 2 * 4608 * 12288 * 3072
 LABELS = [("gemv_kernel", "modulation GEMV (both streams)"), ("ln_modulate", "LN + modulate"),
-          ("gemm_kernel<2, 0, 0>", "QKV GEMM"), ("qknorm", "QK-RMSNorm + RoPE + relayout"),
+          ("gemm_kernel<2, 64, 0>", "QKV GEMM + QK-norm + RoPE"), ("gemm_kernel<2, 0, 0>", "QKV GEMM"),
+          ("qknorm", "QK-RMSNorm + RoPE + relayout"),
           ("attention", "attention"), ("gemm_kernel<2, 2, 0>", "gated projection GEMM"),
           ("gemm_kernel<2, 2, 1>", "gated projection GEMM, pipelined"),
           ("gemm_kernel<2, 1, 0>", "MLP-in GEMM + GELU")]
-KERNELS_PER_BLOCK = 9
+KERNELS_PER_BLOCK = 8   # the QKV epilogue also does QK-norm + RoPE + the attention layouts
 
 
 def _label(name: str) -> str:
@@ -53,7 +54,7 @@ def summarize(path: str) -> str:
     out.append(f"  grid {best[0]['Grid_Size_X']} work-items x {best[0]['Workgroup_Size_X']},"
                f" VGPR {best[0]['VGPR_Count']}, LDS {best[0]['LDS_Block_Size']}")
     out.append(f"  -> {FLOPS / (st.mean(timed) * 1e-6) / 1e12:.1f} TFLOP/s")
-    # one block = the 9 launches from one fp16-weight modulation GEMV to the next
+    # one block = the launches from one fp16-weight modulation GEMV to the next
     starts = [i for i, r in enumerate(rows) if "gemv_kernel<2" in r["short"]]
     blocks = [rows[a:b] for a, b in zip(starts, starts[1:]) if b - a == KERNELS_PER_BLOCK]
     if blocks:
