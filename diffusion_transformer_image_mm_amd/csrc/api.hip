@@ -341,6 +341,7 @@ int run_double(const mmdit_dims* d, const mmdit_double_weights* w, const float* 
         // RMSNorm of q and k and RoPE and writes q, k and v^T in the layout
         // the attention kernel reads (a 256-wide tile lies in one of q|k|v)
         GemmArgs g = proj_base(d, 3 * H, H, ws.h, ws.h8, ws.sh, EPI_QKV_ATTN, nullptr, 0);
+        g.split_n = 3 * H;
         g.q_out = ws.q;
         g.k_out = ws.k;
         g.vt_out = ws.vt;
@@ -406,16 +407,35 @@ int run_single(const mmdit_dims* d, const mmdit_single_weights* w, const float* 
     MMDIT_HIP(launch_ln_modulate(x_in, L, H, 0, m, m + H, m, m + H, d->ln_eps, ws.h, s));
     if (fp8) MMDIT_HIP(quant_rows(ws.h, L, H, ws.h8, ws.sh, s));
     {
-        const int epi = d->mlp_act == MMDIT_ACT_SWIGLU ? MMDIT_EPI_SPLIT_SWIGLU : MMDIT_EPI_SPLIT_GELU;
+        const bool fused = H % 256 == 0;
+        const bool swiglu = d->mlp_act == MMDIT_ACT_SWIGLU;
+        const int epi = fused ? (swiglu ? EPI_SPLIT_SWIGLU_ATTN : EPI_SPLIT_GELU_ATTN)
+                              : (swiglu ? MMDIT_EPI_SPLIT_SWIGLU : MMDIT_EPI_SPLIT_GELU);
         GemmArgs g = proj_base(d, 3 * H + mlp_cols(d), H, ws.h, ws.h8, ws.sh, epi, ws.qkv, 3 * H);
         g.split_n = 3 * H;
         g.out2 = ws.cat;
         g.ldo2 = H + M;
         g.out2_col = H;
-        MMDIT_HIP(gemm_1(g, group(0, L, w->linear1), s));
+        GemmGroup g0 = group(0, L, w->linear1);
+        if (fused) {
+            // q|k|v columns: QK-RMSNorm, RoPE and the attention layouts in the
+            // epilogue (as in the double block); the MLP columns as before
+            g.q_out = ws.q;
+            g.k_out = ws.k;
+            g.vt_out = ws.vt;
+            g.l_pad = LP;
+            g.head_dim = d->head_dim;
+            g.rope = rope;
+            g.rms_eps = d->rms_eps;
+            g0.qn = w->q_norm;
+            g0.kn = w->k_norm;
+        }
+        MMDIT_HIP(gemm_1(g, g0, s));
+        if (fused) MMDIT_HIP(launch_zero_attn_pad(ws.q, ws.k, ws.vt, d->heads, d->head_dim, L, LP, s));
+        else
+            MMDIT_HIP(launch_qknorm_rope(ws.qkv, 3 * H, L, d->heads, d->head_dim, L, w->q_norm, w->k_norm,
+                                         w->q_norm, w->k_norm, rope, d->rms_eps, LP, ws.q, ws.k, ws.vt, s));
     }
-    MMDIT_HIP(launch_qknorm_rope(ws.qkv, 3 * H, L, d->heads, d->head_dim, L, w->q_norm, w->k_norm,
-                                 w->q_norm, w->k_norm, rope, d->rms_eps, LP, ws.q, ws.k, ws.vt, s));
     MMDIT_HIP(launch_attention(ws.q, ws.k, ws.vt, d->heads, L, d->head_dim, LP, ws.cat, H + M, s));
     if (fp8) MMDIT_HIP(quant_rows(ws.cat, L, H + M, ws.cat8, ws.sc, s));
     {

@@ -117,6 +117,15 @@ struct GemmGroup {
 // per-head RMSNorm and RoPE and go to [heads, l_pad, D], v to the transposed,
 // quad-swapped [heads, D, l_pad] layout the attention kernel reads.
 constexpr int EPI_QKV_ATTN = 64;
+// The single-stream block's linear1 ([q | k | v | mlp] columns): the split
+// GELU / SwiGLU epilogues whose first split_n = 3H columns take the
+// EPI_QKV_ATTN path (a separate kernel per variant keeps registers in bounds).
+constexpr int EPI_SPLIT_GELU_ATTN = 65;
+constexpr int EPI_SPLIT_SWIGLU_ATTN = 66;
+// The public epilogue an internal one behaves as outside the q|k|v columns.
+constexpr int epi_base(int e) {
+    return e == EPI_SPLIT_GELU_ATTN ? MMDIT_EPI_SPLIT_GELU : e == EPI_SPLIT_SWIGLU_ATTN ? MMDIT_EPI_SPLIT_SWIGLU : e;
+}
 
 struct GemmArgs {
     int n, k;

@@ -190,8 +190,9 @@ MMDIT_DEV int weight_row(int v, int swiglu_from, int half) {
 // One output tile. TNW: MFMA sub-tiles per wavefront along n, 4 (the
 // 256-wide tile) or 2 (a 128-wide tail tile). The grid's tiles of this width
 // are numbered bid in [0, total) over row tiles [rt0, rt0 + tmt).
-template <int WT, int EPI, int PIPE, int TNW>
+template <int WT, int EPI_T, int PIPE, int TNW>
 MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, int rt0, int tmt) {
+    constexpr int EPI = epi_base(EPI_T);   // the epilogue outside the attention columns
     constexpr bool INT8 = WT == MMDIT_INT8;
     constexpr bool F16W = WT == MMDIT_F16;
     constexpr bool FP8 = WT == MMDIT_FP8;      // fp8 A and W, 128 k per stage
@@ -477,10 +478,11 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
         }
         return;
     }
-    if constexpr (EPI == EPI_QKV_ATTN) {
-        // Columns [q | k | v] (H = n / 3 each, a multiple of the tile width, so
-        // a tile lies in one of them). y = acc * s + b stays in fp32 here.
-        const int H = N / 3, D = args.head_dim, seg = tc.n0 / H;
+    if (EPI_T == EPI_QKV_ATTN || (EPI_T != EPI && tc.n0 < args.split_n)) {
+        // Columns [q | k | v] (split_n = 3H; H a multiple of the tile width,
+        // so a tile lies in one of them; the single-stream block's MLP
+        // columns follow at split_n). y = acc * s + b stays in fp32 here.
+        const int H = args.split_n / 3, D = args.head_dim, seg = tc.n0 / H;
 #pragma unroll
         for (int in = 0; in < TN; ++in) {
             const int n = nb + in * 16;
@@ -652,7 +654,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
 template <int WT, int EPI, int PIPE>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
-    constexpr bool SWIGLU = EPI == MMDIT_EPI_SWIGLU || EPI == MMDIT_EPI_SPLIT_SWIGLU;
+    constexpr bool SWIGLU = epi_base(EPI) == MMDIT_EPI_SWIGLU || epi_base(EPI) == MMDIT_EPI_SPLIT_SWIGLU;
     const int tm0 = (args.g[0].m + BM - 1) / BM;
     const int tmt = args.ngroups == 2 ? tm0 + (args.g[1].m + BM - 1) / BM : tm0;
     const int nf = args.full_tiles;
@@ -721,7 +723,7 @@ static hipError_t launch_gemm_t(const GemmArgs& a0, hipStream_t s) {
     int tmt = 0;
     for (int g = 0; g < a.ngroups; ++g) tmt += (a.g[g].m + BM - 1) / BM;
     if (tmt == 0 || tn == 0) return hipSuccess;
-    const bool swiglu = a.epilogue == MMDIT_EPI_SWIGLU || a.epilogue == MMDIT_EPI_SPLIT_SWIGLU;
+    const bool swiglu = epi_base(a.epilogue) == MMDIT_EPI_SWIGLU || epi_base(a.epilogue) == MMDIT_EPI_SPLIT_SWIGLU;
     // The pipelined loop pays off on long contractions (measured: +10% at
     // K = 12288, +3% at K = 15360, -1% to 0 at K = 3072).
     const bool pipe = WT == MMDIT_F16 && a.k >= PIPE_MIN_K;
@@ -773,7 +775,7 @@ static hipError_t launch_gemm_t(const GemmArgs& a0, hipStream_t s) {
     const size_t lds = 2 * (size_t)(A_TILE_BYTES + (INT8 ? W_TILE_BYTES_I8 : W_TILE_BYTES_BF16));
     dim3 grid(tiles), block(NTHREADS);
 #define GEMM_CASE(E)                                                                        \
-    case E: if constexpr (WT == MMDIT_FP8 && (E == MMDIT_EPI_SWIGLU || E == MMDIT_EPI_SPLIT_SWIGLU)) { \
+    case E: if constexpr (WT == MMDIT_FP8 && (epi_base(E) == MMDIT_EPI_SWIGLU || epi_base(E) == MMDIT_EPI_SPLIT_SWIGLU)) { \
         return hipErrorInvalidValue;                                                        \
     } else {                                                                                \
         auto kfn = pipe ? gemm_kernel<WT, E, (WT == MMDIT_F16 ? 1 : 0)> : gemm_kernel<WT, E, 0>; \
@@ -798,6 +800,8 @@ static hipError_t launch_gemm_t(const GemmArgs& a0, hipStream_t s) {
         GEMM_CASE(MMDIT_EPI_SWIGLU)
         GEMM_CASE(MMDIT_EPI_SPLIT_SWIGLU)
         GEMM_CASE(EPI_QKV_ATTN)
+        GEMM_CASE(EPI_SPLIT_GELU_ATTN)
+        GEMM_CASE(EPI_SPLIT_SWIGLU_ATTN)
         default:
             return hipErrorInvalidValue;
     }

@@ -1,7 +1,7 @@
 // Per-head RMSNorm of q and k, axial RoPE, and relayout for attention.
-// (The double-stream block does this in its QKV projection's epilogue when the
-// hidden size is a multiple of 256; this kernel serves the single-stream
-// block, other hidden sizes and the per-kernel entry.)
+// (Both blocks do this in the epilogue of the projection that makes q, k and
+// v when the hidden size is a multiple of 256; this kernel serves other hidden
+// sizes and the per-kernel entry.)
 //
 // Luminal blog, "What the compiler found on its own": RMSNorm is a square, a
 // sum, a reciprocal square root and a multiply; RoPE gathers each element's
