@@ -30,7 +30,8 @@
 //   destination in m0): the compiler then counts the fragment reads exactly
 //   and each MFMA waits only for its own operand, with the 16 fragment reads
 //   of a phase issued four ahead of the MFMAs that consume them (with the
-//   compiler's load builtin every MFMA waited for all reads in flight);
+//   compiler's load builtin every MFMA waited for all reads in flight), and
+//   the first four V^T fragments read before the softmax;
 //   the kernel orders its LDS accesses itself with waits and barriers;
 // * the last key tile masks keys >= seq_len to -inf; query rows >= seq_len
 //   are computed on zero padding and not stored;
@@ -49,6 +50,19 @@ MMDIT_DEV void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); 
 MMDIT_DEV void g2l_16(const void* gsrc, lds_void* lds_base) {
     const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(l), "v"(gsrc) : "memory", "m0");
+}
+// PV phase with its first four V^T fragments already read (before the
+// softmax): two reads, the four MFMAs on those, then read and MFMA
+// alternately, then the last two MFMAs.
+MMDIT_DEV void pv_schedule() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
 }
 // Schedule of one 16-read, 16-MFMA phase: four reads ahead, then one MFMA and
 // one read alternately, then the last four MFMAs.
@@ -190,6 +204,11 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
             }
         }
         if constexpr (D == 128) read_ahead_schedule();
+        // the first V^T fragments, read now so that the PV phase does not
+        // start on an LDS round trip after the softmax
+        bf16x8_t vpre[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) vpre[u] = *reinterpret_cast<const bf16x8_t*>(sV + v_off[0][u]);
         // element i of s[st]: key t*64 + st*32 + 8*(i/4) + 4g + i%4
         const int kv0 = t * T::KV;
         if (kv0 + T::KV > seq_len) {
@@ -239,10 +258,10 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(sV + v_off[dt][u]);
+                const bf16x8_t vf = dt == 0 ? vpre[u] : *reinterpret_cast<const bf16x8_t*>(sV + v_off[dt][u]);
                 o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[u], o[dt], 0, 0, 0);
             }
-        if constexpr (D == 128) read_ahead_schedule();
+        if constexpr (D == 128) pv_schedule();
     };
 
     issue(0, sK0, sV0);
