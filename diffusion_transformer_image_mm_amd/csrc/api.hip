@@ -334,8 +334,9 @@ int run_double(const mmdit_dims* d, const mmdit_double_weights* w, const float* 
     if (!premod) MMDIT_HIP(gemv_2(vec, H, w->txt.mod, ws.mod, w->img.mod, ws.mod + 6 * H, 6 * H, dt, 1, s));
     const bool fp8 = dt == MMDIT_FP8;
     // a2: LN1 + modulate
-    MMDIT_HIP(launch_ln_modulate(x_in, L, H, Lt, mt, mt + H, mi, mi + H, d->ln_eps, ws.h, s));
-    if (fp8) MMDIT_HIP(quant_rows(ws.h, L, H, ws.h8, ws.sh, s));
+    // (fp8 blocks: the LayerNorm kernel writes the e4m3 codes and row scales itself)
+    MMDIT_HIP(launch_ln_modulate(x_in, L, H, Lt, mt, mt + H, mi, mi + H, d->ln_eps, ws.h, s,
+                                 fp8 ? ws.h8 : nullptr, fp8 ? ws.sh : nullptr));
     if (H % 256 == 0) {
         // a3 + a4: QKV projection whose epilogue applies the per-head
         // RMSNorm of q and k and RoPE and writes q, k and v^T in the layout
@@ -377,8 +378,7 @@ int run_double(const mmdit_dims* d, const mmdit_double_weights* w, const float* 
     }
     // a7: LN2 + modulate
     MMDIT_HIP(launch_ln_modulate(x_out, L, H, Lt, mt + 3 * H, mt + 4 * H, mi + 3 * H, mi + 4 * H,
-                                 d->ln_eps, ws.h, s));
-    if (fp8) MMDIT_HIP(quant_rows(ws.h, L, H, ws.h8, ws.sh, s));
+                                 d->ln_eps, ws.h, s, fp8 ? ws.h8 : nullptr, fp8 ? ws.sh : nullptr));
     // a8: fc1 + GELU (or SwiGLU: fc1 rows [gate | up], hidden = SiLU(gate) * up)
     {
         const int epi = d->mlp_act == MMDIT_ACT_SWIGLU ? MMDIT_EPI_SWIGLU : MMDIT_EPI_BIAS_GELU;
@@ -404,8 +404,8 @@ int run_single(const mmdit_dims* d, const mmdit_single_weights* w, const float* 
     const float* m = premod ? premod : ws.mod;
     if (!premod) MMDIT_HIP(gemv(vec, H, w->mod, 3 * H, dt, 1, 0, ws.mod, s));
     const bool fp8 = dt == MMDIT_FP8;
-    MMDIT_HIP(launch_ln_modulate(x_in, L, H, 0, m, m + H, m, m + H, d->ln_eps, ws.h, s));
-    if (fp8) MMDIT_HIP(quant_rows(ws.h, L, H, ws.h8, ws.sh, s));
+    MMDIT_HIP(launch_ln_modulate(x_in, L, H, 0, m, m + H, m, m + H, d->ln_eps, ws.h, s,
+                                 fp8 ? ws.h8 : nullptr, fp8 ? ws.sh : nullptr));
     {
         const bool fused = H % 256 == 0;
         const bool swiglu = d->mlp_act == MMDIT_ACT_SWIGLU;

@@ -89,7 +89,8 @@ namespace mmdit {
 hipError_t launch_ln_modulate(const float* x, int rows, int hidden, int split,
                               const float* shift0, const float* scale0,
                               const float* shift1, const float* scale1, float eps,
-                              uint16_t* out, hipStream_t s);
+                              uint16_t* out, hipStream_t s,
+                              uint8_t* codes = nullptr, float* qscale = nullptr);
 
 hipError_t launch_qknorm_rope(const uint16_t* qkv, int ld, int seq_len, int heads, int head_dim,
                               int split, const uint16_t* qn0, const uint16_t* kn0,

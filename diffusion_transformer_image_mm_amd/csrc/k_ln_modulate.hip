@@ -21,13 +21,18 @@ namespace mmdit {
 // 4/W rows); lane t of wave w holds float4 columns (i*W + w)*64 + t. The two
 // sums are reduced within each wavefront, then over the row's W partials in
 // LDS in a fixed order, so the result does not depend on timing.
-template <int VPT, int W>
+// FP8: the row goes out as OCP e4m3 codes with one fp32 scale instead of
+// fp16 (the projection's fp8 operand): the fp16 rounding of each output is
+// kept, then scale = max|h| / 448 and code = e4m3(h / scale), both divisions
+// in fp32 and the conversion round-to-nearest-even, exactly as the separate
+// per-row quantiser does on the fp16 row (bit-identical codes and scales).
+template <int VPT, int W, bool FP8>
 __global__ __launch_bounds__(256) void ln_modulate_kernel(
     const float* __restrict__ x, int rows, int hidden, int split,
     const float* __restrict__ shift0, const float* __restrict__ scale0,
     const float* __restrict__ shift1, const float* __restrict__ scale1, float eps,
-    uint16_t* __restrict__ out) {
-    __shared__ float red[2][4];
+    uint16_t* __restrict__ out, uint8_t* __restrict__ codes, float* __restrict__ qscale) {
+    __shared__ float red[3][4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = wave % W;                      // this wave's part of the row
     const int row = blockIdx.x * (4 / W) + wave / W;
@@ -80,24 +85,61 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(
     const float4* sh = reinterpret_cast<const float4*>(first ? shift0 : shift1);
     const float4* sc = reinterpret_cast<const float4*>(first ? scale0 : scale1);
     uint2* orow = reinterpret_cast<uint2*>(out + (size_t)(valid ? row : 0) * hidden);
+    uint2 hv[VPT];
+    float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
         const int c = (i * W + sub) * 64 + lane;
+        hv[i] = make_uint2(0u, 0u);
         if (c < n4) {
             const float4 a = sh[c], b = sc[c];
             const float y0 = (v[i].x - mean) * rstd * (1.0f + b.x) + a.x;
             const float y1 = (v[i].y - mean) * rstd * (1.0f + b.y) + a.y;
             const float y2 = (v[i].z - mean) * rstd * (1.0f + b.z) + a.z;
             const float y3 = (v[i].w - mean) * rstd * (1.0f + b.w) + a.w;
-            orow[c] = make_uint2(pack2h(y0, y1), pack2h(y2, y3));
+            hv[i] = make_uint2(pack2h(y0, y1), pack2h(y2, y3));
+            if (!FP8) {
+                orow[c] = hv[i];
+            } else {
+                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(h2f(hv[i].x & 0xffffu)), fabsf(h2f(hv[i].x >> 16))),
+                                         fmaxf(fabsf(h2f(hv[i].y & 0xffffu)), fabsf(h2f(hv[i].y >> 16)))));
+            }
         }
+    }
+    if constexpr (FP8) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+        if (W > 1) {
+            if (lane == 0) red[2][wave] = amax;
+            __syncthreads();
+            const int w0 = wave - sub;
+#pragma unroll
+            for (int w = 0; w < W; ++w) amax = fmaxf(amax, red[2][w0 + w]);
+        }
+        const float qs = amax / 448.0f;
+        uint32_t* crow = reinterpret_cast<uint32_t*>(codes + (size_t)(valid ? row : 0) * hidden);
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int c = (i * W + sub) * 64 + lane;
+            if (c < n4) {
+                uint32_t packed = 0u;
+                if (qs > 0.f) {
+                    packed = __builtin_amdgcn_cvt_pk_fp8_f32(h2f(hv[i].x & 0xffffu) / qs, h2f(hv[i].x >> 16) / qs,
+                                                             0u, false);
+                    packed = __builtin_amdgcn_cvt_pk_fp8_f32(h2f(hv[i].y & 0xffffu) / qs, h2f(hv[i].y >> 16) / qs,
+                                                             packed, true);
+                }
+                crow[c] = packed;
+            }
+        }
+        if (valid && sub == 0 && lane == 0) qscale[row] = qs;
     }
 }
 
 hipError_t launch_ln_modulate(const float* x, int rows, int hidden, int split,
                               const float* shift0, const float* scale0,
                               const float* shift1, const float* scale1, float eps,
-                              uint16_t* out, hipStream_t s) {
+                              uint16_t* out, hipStream_t s, uint8_t* codes, float* qscale) {
     if (rows <= 0) return hipSuccess;
     if (hidden < 64 || hidden % 64 != 0 || hidden > 4096) return hipErrorInvalidValue;
     const int n4 = hidden / 4;
@@ -106,8 +148,12 @@ hipError_t launch_ln_modulate(const float* x, int rows, int hidden, int split,
     dim3 grid((rows + 4 / w - 1) / (4 / w)), block(256);
 #define LNM_CASE(V, WW)                                                                        \
     if (vpt == V && w == WW) {                                                                 \
-        hipLaunchKernelGGL((ln_modulate_kernel<V, WW>), grid, block, 0, s, x, rows, hidden, split, \
-                           shift0, scale0, shift1, scale1, eps, out);                          \
+        if (codes)                                                                             \
+            hipLaunchKernelGGL((ln_modulate_kernel<V, WW, true>), grid, block, 0, s, x, rows, hidden, split, \
+                               shift0, scale0, shift1, scale1, eps, out, codes, qscale);       \
+        else                                                                                   \
+            hipLaunchKernelGGL((ln_modulate_kernel<V, WW, false>), grid, block, 0, s, x, rows, hidden, split, \
+                               shift0, scale0, shift1, scale1, eps, out, codes, qscale);       \
         return hipGetLastError();                                                              \
     }
     LNM_CASE(1, 1) LNM_CASE(2, 1) LNM_CASE(3, 1) LNM_CASE(4, 1)
