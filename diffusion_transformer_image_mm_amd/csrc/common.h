@@ -71,13 +71,15 @@ MMDIT_DEV float group_sum(float v) {
 MMDIT_DEV float silu(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // GELU, tanh form: 0.5 x (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3).
-// tanh(u) = 1 - 2 / (e^{2u} + 1), so 0.5 (1 + tanh u) = 1 - 1/(e^{2u} + 1).
+// 0.5 (1 + tanh u) = 1 / (1 + e^{-2u}), and e^{-2u} = 2^{x (c1 + c2 x^2)} with
+// c1 = -2 log2(e) sqrt(2/pi), c2 = 0.044715 c1: one exp2, one reciprocal and
+// five multiplies and adds per value (the epilogue of the MLP-in projection runs
+// this while the compute unit's matrix cores wait). Saturates to 0 and x.
 MMDIT_DEV float gelu_tanh(float x) {
-    const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
-    const float k1 = 0.044715f;
-    float u = k0 * (x + k1 * x * x * x);
-    float e = __expf(2.0f * u);
-    return x * (1.0f - __builtin_amdgcn_rcpf(e + 1.0f));
+    const float c1 = -2.302208198144325f;
+    const float c2 = -0.1029432395800235f;
+    const float e = __builtin_amdgcn_exp2f(x * fmaf(c2, x * x, c1));
+    return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 }  // namespace mmdit
