@@ -149,6 +149,7 @@ def test_kernel_entry_validation():
     assert B.mmdit_k_ln_modulate(FAKE, 10, 256, 0, FAKE, FAKE, FAKE, FAKE, 0.0, FAKE) == B.MMDIT_E_ARG
     assert B.mmdit_k_attention(FAKE, FAKE, FAKE, 4, 100, 64, 96, FAKE, 256) == B.MMDIT_E_SHAPE  # l_pad % 64
     assert B.mmdit_k_attention(FAKE, FAKE, FAKE, 4, 100, 80, 128, FAKE, 320) == B.MMDIT_E_SHAPE
+    assert B.mmdit_k_attention(FAKE, FAKE, FAKE, 4, 100, 64, 1 << 24, FAKE, 256) == B.MMDIT_E_SHAPE  # 32-bit offsets
     assert B.mmdit_k_qknorm_rope(FAKE, 768, 100, 4, 64, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1e-6, 100,
                                  FAKE, FAKE, FAKE) == B.MMDIT_E_SHAPE
     g = B.mmdit_gemm(m=10, n=100, k=64, weight_dtype=0, a=FAKE, lda=64, w=_linear(), epilogue=0, out=FAKE, ldo=128)
@@ -156,6 +157,9 @@ def test_kernel_entry_validation():
     g.n = 128
     g.epilogue = 9
     assert B.mmdit_k_gemm(g) == B.MMDIT_E_ARG
+    for internal in (64, 65, 66):   # the blocks' attention-layout epilogues are not public
+        g.epilogue = internal
+        assert B.mmdit_k_gemm(g) == B.MMDIT_E_ARG
     g.epilogue = B.MMDIT_EPI_GATE_RESID
     assert B.mmdit_k_gemm(g) == B.MMDIT_E_NULL  # gate / resid missing
     g.epilogue, g.weight_dtype = 0, B.MMDIT_INT8
