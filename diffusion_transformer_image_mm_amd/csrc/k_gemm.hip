@@ -505,6 +505,23 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
             }
         }
         if (seg < 2) {
+            // RoPE table entries (cos, sin of the lane's two pairs) for the
+            // first half of the lane's rows, requested before the barriers of
+            // the reduction below so that their latency overlaps it; the second
+            // half is requested as the first half's registers free up.
+            constexpr int HM = TM / 2;
+            const int nsb0 = nb - seg * H;
+            float4 cs[HM][TN];
+            auto rope_at = [&](int im, int in) -> float4 {
+                const int m = mb + im * 16;
+                const size_t t = (size_t)(G.row0 + (m < M ? m : M - 1));
+                const int dl = (nsb0 + in * 16) % D;
+                return *reinterpret_cast<const float4*>(args.rope + (t * (D / 2) + dl / 2) * 2);
+            };
+#pragma unroll
+            for (int im = 0; im < HM; ++im)
+#pragma unroll
+                for (int in = 0; in < TN; ++in) cs[im][in] = rope_at(im, in);
             // RMSNorm over each head's D columns: lane sums over its 4 x TN
             // columns, then over the 4 lanes of its row (lane ^ 16, ^ 32), then
             // over the wavefronts that share the head, through LDS.
@@ -539,20 +556,26 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
 #pragma unroll
             for (int im = 0; im < TM; ++im) {
                 const int m = mb + im * 16;
-                if (m >= M) continue;
-                float ss = 0.f;
-                for (int w = 0; w < wph; ++w) ss += red[(w0 + w) * 256 + wm * 128 + im * 16 + lr];
-                const float rstd = 1.0f / sqrtf(ss * inv_d + args.rms_eps);
-                const size_t t = (size_t)(G.row0 + m);
+                const int hi = im % HM;   // this row's table entries sit in cs[hi]
+                if (m < M) {
+                    float ss = 0.f;
+                    for (int w = 0; w < wph; ++w) ss += red[(w0 + w) * 256 + wm * 128 + im * 16 + lr];
+                    const float rstd = 1.0f / sqrtf(ss * inv_d + args.rms_eps);
+                    const size_t t = (size_t)(G.row0 + m);
 #pragma unroll
-                for (int in = 0; in < TN; ++in) {
-                    const int dl = (nsb + in * 16) % D;   // 4 consecutive dims dl..dl+3: pairs dl/2, dl/2+1
-                    const float4 cs = *reinterpret_cast<const float4*>(args.rope + (t * (D / 2) + dl / 2) * 2);
-                    const float a0 = acc[in][im][0] * rstd * gs[in][0], b0 = acc[in][im][1] * rstd * gs[in][1];
-                    const float a1 = acc[in][im][2] * rstd * gs[in][2], b1 = acc[in][im][3] * rstd * gs[in][3];
-                    *reinterpret_cast<uint2*>(dst + ((size_t)h * args.l_pad + t) * D + dl) =
-                        make_uint2(pack2bf(a0 * cs.x - b0 * cs.y, a0 * cs.y + b0 * cs.x),
-                                   pack2bf(a1 * cs.z - b1 * cs.w, a1 * cs.w + b1 * cs.z));
+                    for (int in = 0; in < TN; ++in) {
+                        const int dl = (nsb + in * 16) % D;   // 4 consecutive dims dl..dl+3: pairs dl/2, dl/2+1
+                        const float4 c = cs[hi][in];
+                        const float a0 = acc[in][im][0] * rstd * gs[in][0], b0 = acc[in][im][1] * rstd * gs[in][1];
+                        const float a1 = acc[in][im][2] * rstd * gs[in][2], b1 = acc[in][im][3] * rstd * gs[in][3];
+                        *reinterpret_cast<uint2*>(dst + ((size_t)h * args.l_pad + t) * D + dl) =
+                            make_uint2(pack2bf(a0 * c.x - b0 * c.y, a0 * c.y + b0 * c.x),
+                                       pack2bf(a1 * c.z - b1 * c.w, a1 * c.w + b1 * c.z));
+                    }
+                }
+                if (im < HM) {
+#pragma unroll
+                    for (int in = 0; in < TN; ++in) cs[hi][in] = rope_at(im + HM, in);
                 }
             }
         } else {
