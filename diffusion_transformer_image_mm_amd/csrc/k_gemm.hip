@@ -18,7 +18,10 @@
 // stored in fp16 by the kernel that produced it: at FLUX size, bf16 storage
 // of these activations alone puts the block output at ~2e-2 of its RMS away
 // from the exact result, fp16 storage at ~4e-3. The fp16 and bf16 MFMA
-// rates are equal on gfx950.
+// rates are equal on gfx950. fp8 (OCP e4m3) operands take both A and W as
+// codes with an fp32 scale per row of each, 128 k per LDS stage, on
+// v_mfma_scale_f32_16x16x128_f8f6f4 with unit block scales; the two row
+// scales multiply the fp32 sum in the epilogue.
 //
 // Shape of the kernel (gfx950, 64-wide wavefronts):
 // * workgroup tile 256 (rows of A) x 256 (rows of W) x 64 (k), 8 wavefronts
@@ -30,7 +33,10 @@
 //   only with at least two wavefronts per SIMD;
 // * W is the MFMA's first operand and A the second, so the hardware result
 //   is the transposed tile and each lane ends up with 4 consecutive output
-//   columns of one row: 8-byte 16-bit / 16-byte fp32 epilogue stores;
+//   columns of one row: 8-byte 16-bit / 16-byte fp32 epilogue stores, issued
+//   row by row so that the pieces of each 128-byte output line leave back to
+//   back (stored column block by column block, they left eight stores apart
+//   and the output was written 1.7 times over);
 // * both operand tiles go HBM/L2 -> LDS with 16-byte direct-to-LDS loads
 //   (no VGPR staging), double-buffered; rows are 128 B in LDS with the
 //   16-byte chunk c of row r stored at position c ^ ((r >> 1) & 7), so the
@@ -51,7 +57,9 @@
 // * head tiles: in a grouped launch the text-stream group (at most two row
 //   tiles, weight slabs shared by only two tiles, so HBM-latency bound) can
 //   run as 128-wide tiles dispatched first (the rule is in launch_gemm_t);
-// * the double block's QKV epilogue (EPI_QKV_ATTN) does the per-head QK
+// * the epilogue of the projection that makes q, k and v (EPI_QKV_ATTN in
+//   the double block; EPI_SPLIT_GELU_ATTN / EPI_SPLIT_SWIGLU_ATTN for the
+//   first 3H columns of the single block's linear1) does the per-head QK
 //   RMSNorm and RoPE in fp32 on the accumulators (the row's sum of squares
 //   over a head: in-lane, then lanes ^16 and ^32, then the wavefronts that
 //   share the head through LDS) and writes q, k and v^T straight into the
