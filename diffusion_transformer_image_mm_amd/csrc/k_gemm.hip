@@ -513,28 +513,35 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
             }
         }
         if (seg < 2) {
-            // RoPE table entries (cos, sin of the lane's two pairs) for the
-            // first half of the lane's rows, requested before the barriers of
-            // the reduction below so that their latency overlaps it; the second
-            // half is requested as the first half's registers free up.
-            constexpr int HM = TM / 2;
-            const int nsb0 = nb - seg * H;
-            float4 cs[HM][TN];
-            auto rope_at = [&](int im, int in) -> float4 {
-                const int m = mb + im * 16;
-                const size_t t = (size_t)(G.row0 + (m < M ? m : M - 1));
-                const int dl = (nsb0 + in * 16) % D;
-                return *reinterpret_cast<const float4*>(args.rope + (t * (D / 2) + dl / 2) * 2);
-            };
-#pragma unroll
-            for (int im = 0; im < HM; ++im)
-#pragma unroll
-                for (int in = 0; in < TN; ++in) cs[im][in] = rope_at(im, in);
+            // The tile's slice of the RoPE table (its 256 rows x D floats: cos
+            // and sin of every pair) is staged in LDS once, with 16-byte
+            // direct-to-LDS loads of 1 KB per wavefront instruction; chunk c of
+            // row r sits at position c ^ (r & 15), so the 16 rows read together
+            // hit distinct bank groups. (Read per lane from L2 instead, every
+            // entry was fetched twice, once per head of the tile, and the
+            // latency sat behind the reduction's barriers.) Rows past the
+            // group's end load its last row. The partial sums follow the slice.
+            const int RB = D * 4;                                 // bytes per table row
+            const int CPR = D / 4;                                // 16-byte chunks per row
+            char* srope = smem;                                   // [256][RB]
+            float* red = reinterpret_cast<float*>(smem + 256 * RB);   // [4 column waves][256 rows]
+            __syncthreads();                                      // the main loop's LDS reads are done
+            {
+                const char* rtab = reinterpret_cast<const char*>(args.rope);
+                const int rpl = 1024 / RB;                        // rows per 1 KB load
+                const int loads = 256 / rpl / 8;                  // per wavefront
+                for (int j = 0; j < loads; ++j) {
+                    const int blk = wave * loads + j;
+                    const int r = blk * rpl + lane / CPR;
+                    const int c = (lane % CPR) ^ (r & 15);
+                    const int m = tc.m0 + r;
+                    const size_t t = (size_t)(G.row0 + (m < M ? m : M - 1));
+                    g2l_16_asm(rtab + t * RB + c * 16, (lds_void*)(srope + blk * 1024));
+                }
+            }
             // RMSNorm over each head's D columns: lane sums over its 4 x TN
             // columns, then over the 4 lanes of its row (lane ^ 16, ^ 32), then
             // over the wavefronts that share the head, through LDS.
-            float* red = reinterpret_cast<float*>(smem);   // [4 column waves][256 rows]
-            __syncthreads();                                // the main loop's LDS reads are done
 #pragma unroll
             for (int im = 0; im < TM; ++im) {
                 float p = 0.f;
@@ -546,6 +553,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
                 p += __shfl_xor(p, 32, 64);
                 if (lg == 0) red[wn * 256 + wm * 128 + im * 16 + lr] = p;
             }
+            wait_vmcnt0();   // this wavefront's slice loads have landed
             __syncthreads();
             const int wph = D / (16 * TNW);        // wavefronts per head: 1, 2 or 4
             const int w0 = (wn / wph) * wph;
@@ -564,26 +572,22 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
 #pragma unroll
             for (int im = 0; im < TM; ++im) {
                 const int m = mb + im * 16;
-                const int hi = im % HM;   // this row's table entries sit in cs[hi]
-                if (m < M) {
-                    float ss = 0.f;
-                    for (int w = 0; w < wph; ++w) ss += red[(w0 + w) * 256 + wm * 128 + im * 16 + lr];
-                    const float rstd = 1.0f / sqrtf(ss * inv_d + args.rms_eps);
-                    const size_t t = (size_t)(G.row0 + m);
+                if (m >= M) continue;
+                float ss = 0.f;
+                for (int w = 0; w < wph; ++w) ss += red[(w0 + w) * 256 + wm * 128 + im * 16 + lr];
+                const float rstd = 1.0f / sqrtf(ss * inv_d + args.rms_eps);
+                const size_t t = (size_t)(G.row0 + m);
+                const int r = wm * 128 + im * 16 + lr;   // the row within the tile
 #pragma unroll
-                    for (int in = 0; in < TN; ++in) {
-                        const int dl = (nsb + in * 16) % D;   // 4 consecutive dims dl..dl+3: pairs dl/2, dl/2+1
-                        const float4 c = cs[hi][in];
-                        const float a0 = acc[in][im][0] * rstd * gs[in][0], b0 = acc[in][im][1] * rstd * gs[in][1];
-                        const float a1 = acc[in][im][2] * rstd * gs[in][2], b1 = acc[in][im][3] * rstd * gs[in][3];
-                        *reinterpret_cast<uint2*>(dst + ((size_t)h * args.l_pad + t) * D + dl) =
-                            make_uint2(pack2bf(a0 * c.x - b0 * c.y, a0 * c.y + b0 * c.x),
-                                       pack2bf(a1 * c.z - b1 * c.w, a1 * c.w + b1 * c.z));
-                    }
-                }
-                if (im < HM) {
-#pragma unroll
-                    for (int in = 0; in < TN; ++in) cs[hi][in] = rope_at(im + HM, in);
+                for (int in = 0; in < TN; ++in) {
+                    const int dl = (nsb + in * 16) % D;   // 4 consecutive dims dl..dl+3: pairs dl/2, dl/2+1
+                    const float4 c =
+                        *reinterpret_cast<const float4*>(srope + r * RB + (((dl >> 2) ^ (r & 15)) << 4));
+                    const float a0 = acc[in][im][0] * rstd * gs[in][0], b0 = acc[in][im][1] * rstd * gs[in][1];
+                    const float a1 = acc[in][im][2] * rstd * gs[in][2], b1 = acc[in][im][3] * rstd * gs[in][3];
+                    *reinterpret_cast<uint2*>(dst + ((size_t)h * args.l_pad + t) * D + dl) =
+                        make_uint2(pack2bf(a0 * c.x - b0 * c.y, a0 * c.y + b0 * c.x),
+                                   pack2bf(a1 * c.z - b1 * c.w, a1 * c.w + b1 * c.z));
                 }
             }
         } else {
@@ -803,7 +807,13 @@ static hipError_t launch_gemm_t(const GemmArgs& a0, hipStream_t s) {
             tiles = a.full_tiles + tm0g * tn2;
         }
     }
-    const size_t lds = 2 * (size_t)(A_TILE_BYTES + (INT8 ? W_TILE_BYTES_I8 : W_TILE_BYTES_BF16));
+    // the attention-layout epilogues stage a 256 x D fp32 RoPE slice (D <= 128)
+    // and the RMSNorm partial sums in LDS after the main loop
+    const bool attn_epi = a.epilogue == EPI_QKV_ATTN || a.epilogue == EPI_SPLIT_GELU_ATTN ||
+                          a.epilogue == EPI_SPLIT_SWIGLU_ATTN;
+    const size_t lds_main = 2 * (size_t)(A_TILE_BYTES + (INT8 ? W_TILE_BYTES_I8 : W_TILE_BYTES_BF16));
+    const size_t lds_epi = 256 * 128 * 4 + 4 * 256 * 4;
+    const size_t lds = attn_epi && lds_epi > lds_main ? lds_epi : lds_main;
     dim3 grid(tiles), block(NTHREADS);
 #define GEMM_CASE(E)                                                                        \
     case E: if constexpr (WT == MMDIT_FP8 && (epi_base(E) == MMDIT_EPI_SWIGLU || epi_base(E) == MMDIT_EPI_SPLIT_SWIGLU)) { \
