@@ -8,11 +8,14 @@ import oracle as O
 from diffusion_transformer_image_mm_amd import binding as B
 from diffusion_transformer_image_mm_amd import synth
 from gpu_helpers import TOL, DeviceArena, rel_err, say, stream, sync
+from sharp_inputs import sharp_block_inputs, update_rms_err
 from diffusion_transformer_image_mm_amd.device import dims_for
 
 pytestmark = pytest.mark.gpu
 
 RAGGED = synth.custom_shape("ragged-h128-L68", 710, 128, 2, 256, 5, (7, 9))
+# bound on the RMS error of the update in test_block_sharp_attention_update
+SHARP_TOL = 2e-2
 RAGGED_D128 = synth.custom_shape("ragged-h256-d128-L203", 711, 256, 2, 512, 3, (10, 20))
 # SwiGLU with ragged lengths: 5 text tokens, a 7x9 image and its 7x9 reference
 RAGGED_SWIGLU = synth.custom_shape("ragged-swiglu-h256-d128-L131", 712, 256, 2, 384, 5, (7, 9),
@@ -95,6 +98,26 @@ def test_block_rerun_bit_exact_and_inplace(kind):
     np.testing.assert_array_equal(a, b)
     c = run_block(inp, inplace=True)
     np.testing.assert_array_equal(a, c)
+
+
+@pytest.mark.parametrize("shape,kind", [(RAGGED_D128, "double"), (synth.TINY, "double"), (RAGGED, "double"),
+                                        (RAGGED_D128, "single"), (synth.TINY, "single")])
+def test_block_sharp_attention_update(shape, kind):
+    """The block's update with sharp attention and (double block) the MLP
+    branch gated off, against the oracle's. With the synthetic N(0,1) inputs
+    a block's attention is nearly uniform and its output barely depends on q
+    and k, so the checks above would miss a mistake in the QK-RMSNorm / RoPE
+    stage (done in the QKV or linear1 epilogue when H is a multiple of 256,
+    by a separate kernel otherwise). Measured: 3-6e-3 of the update's RMS;
+    a RoPE mistake planted in the oracle moves it by more than 0.3
+    (test_oracle_pins.py::test_sharp_update_detects_rope_mistakes)."""
+    say(f"block sharp attention {kind} {shape.name}")
+    inp = sharp_block_inputs(shape, kind)
+    g = run_block(inp)
+    ref = oracle_block(inp)
+    e_rms = update_rms_err(g, ref, inp["x"])
+    say(f"  update: rms err / rms = {e_rms:.3e}, max err / rms = {rel_err(g - inp['x'], ref - inp['x']):.3e}")
+    assert e_rms <= SHARP_TOL, e_rms
 
 
 @pytest.mark.parametrize("kind", ["double", "single"])

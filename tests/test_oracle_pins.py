@@ -669,3 +669,25 @@ def test_fp8_block_close_to_exact_block_and_gate_identity(kind):
             lin.w[r0:r0 + H] = 0
             lin.b[r0:r0 + H] = 0
     np.testing.assert_array_equal(f(*args, fp8=True), inp["x"])
+
+
+@pytest.mark.parametrize("kind", ["double", "single"])
+def test_sharp_update_detects_rope_mistakes(kind):
+    """The GPU test of the block update under sharp attention
+    (test_gpu_blocks.py::test_block_sharp_attention_update, bound 2e-2) would
+    catch a mistake in the RoPE stage: planted here in the oracle's inputs,
+    on the CPU — image positions with the h and w axes swapped, or no
+    rotation at all (every position 0) — the update moves by far more than
+    that bound."""
+    from sharp_inputs import sharp_block_inputs, update_rms_err
+
+    shp = synth.custom_shape("ragged-h256-d128-L203", 711, 256, 2, 512, 3, (10, 20))
+    inp = sharp_block_inputs(shp, kind)
+    f = O.double_block if kind == "double" else O.single_block
+    ref = f(inp["x"], inp["vec"], inp["ids"], inp["w"], shp)
+    swapped = inp["ids"].copy()
+    swapped[:, [1, 2]] = swapped[:, [2, 1]]
+    zero = np.zeros_like(inp["ids"])
+    for ids in (swapped, zero):
+        bad = f(inp["x"], inp["vec"], ids, inp["w"], shp)
+        assert update_rms_err(bad, ref, inp["x"]) > 0.3
