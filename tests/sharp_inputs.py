@@ -6,16 +6,20 @@ zeroed, so that x_out - x_in is the gated attention branch alone."""
 from diffusion_transformer_image_mm_amd import synth
 
 
-def sharp_block_inputs(shape, kind):
-    inp = synth.block_inputs(shape, kind)
+def sharp_block_inputs(shape, kind, int8=False):
+    inp = synth.block_inputs(shape, kind, int8=int8)
     H = shape.hidden
     ws = [inp["w"][s] for s in ("txt", "img")] if kind == "double" else [inp["w"]]
     for w in ws:
         w["q_norm"] = w["q_norm"] * 2.0
         w["k_norm"] = w["k_norm"] * 2.0
         if kind == "double":   # gate2: modulation rows [5H, 6H)
-            w["mod"].w[5 * H:] = 0
-            w["mod"].b[5 * H:] = 0
+            lin = w["mod"]
+            if lin.w is not None:
+                lin.w[5 * H:] = 0
+            else:              # int8 layer: zero codes
+                lin.q[5 * H:] = 0
+            lin.b[5 * H:] = 0
     return inp
 
 

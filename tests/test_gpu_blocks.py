@@ -121,6 +121,25 @@ def test_block_sharp_attention_update(shape, kind):
 
 
 @pytest.mark.parametrize("kind", ["double", "single"])
+@pytest.mark.parametrize("wt", ["f16", "int8", "fp8"])
+def test_block_sharp_attention_update_formats(kind, wt):
+    """The sharp-attention update check above with fp16-encoded, int8 and fp8
+    weights: the attention-layout epilogue applies each format's scales
+    before the norm (the channel scale of int8; row and channel scales of
+    fp8, whose oracle quantises the same operands). Bars: 2e-2 of the
+    update's RMS for the 16-bit formats, 3e-2 for fp8 (as for the fp8 blocks,
+    whose codes can sit one step apart near rounding boundaries)."""
+    say(f"block sharp attention {kind} {RAGGED_D128.name} weights={wt}")
+    int8 = wt == "int8"
+    inp = sharp_block_inputs(RAGGED_D128, kind, int8=int8)
+    g = run_block(inp, int8, f16=wt == "f16", fp8=wt == "fp8")
+    ref = oracle_block(inp, fp8=wt == "fp8")
+    e_rms = update_rms_err(g, ref, inp["x"])
+    say(f"  update: rms err / rms = {e_rms:.3e}")
+    assert e_rms <= (FP8_UPDATE_RMS if wt == "fp8" else SHARP_TOL), e_rms
+
+
+@pytest.mark.parametrize("kind", ["double", "single"])
 def test_block_zero_gate_identity(kind):
     """Zero gate rows in the modulation weights and biases: the block returns
     its input bit for bit (gated residual path)."""
