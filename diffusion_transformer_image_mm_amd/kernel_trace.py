@@ -1,9 +1,11 @@
 """Text summary of a rocprofv3 kernel trace of ``bench.py --no-step``.
 
     cd /tmp && export TMPDIR=/tmp
-    rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/prof -o bench \\
+    rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/prof -o bench \\
         -- python3 $REPO/bench.py --steps 20 --no-cpu --no-step
-    python -m diffusion_transformer_image_mm_amd.kernel_trace gpurun_out/prof/bench_kernel_trace.csv
+    python -m diffusion_transformer_image_mm_amd.kernel_trace $OUT/prof/bench_kernel_trace.csv
+
+($REPO is the repository root, $OUT any output directory.)
 
 Durations are End - Start per dispatch. bench.py runs the block with bf16
 weights, then with fp16-encoded weights, then 3 untimed + K timed

@@ -4,12 +4,12 @@ Two counter runs of ``bench.py --probe`` (which launches the MLP-in GEMM ten
 times and then copies 1 GiB device-to-device three times):
 
     cd /tmp && export TMPDIR=/tmp
-    timeout -s KILL 90 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmc_fetch -o p -- python3 $REPO/bench.py --probe
-    timeout -s KILL 90 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmc_write -o p -- python3 $REPO/bench.py --probe
+    timeout -s KILL 90 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/pmc_fetch -o p -- python3 $REPO/bench.py --probe
+    timeout -s KILL 90 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/pmc_write -o p -- python3 $REPO/bench.py --probe
 
-``python -m diffusion_transformer_image_mm_amd.traffic gpurun_out/pmc_fetch
-gpurun_out/pmc_write`` then writes the summary that bench.py reads. Each
-counter (KiB per dispatch) is scaled by expected/measured for the copy of
+``python -m diffusion_transformer_image_mm_amd.traffic $OUT/pmc_fetch
+$OUT/pmc_write`` then writes the summary that bench.py reads ($REPO is the
+repository root, $OUT any output directory). Each counter (KiB per dispatch) is scaled by expected/measured for the copy of
 known size, and the result is tied to the SHA-256 of the kernel's sources
 (k_gemm.hip and common.h): once they change, bench.py reports the traffic as
 unknown (null).
@@ -55,12 +55,12 @@ def summarize(fetch_dir: str, write_dir: str) -> str:
     write = statistics.mean(gw) * w_fac * 1024
     lines = [
         "# HBM traffic of the MLP-in GEMM (gemm_kernel<F16, BIAS_GELU>, 4608x12288x3072, FLUX double block)",
-        "# commands (from /tmp, TMPDIR=/tmp; $REPO = the repository root):",
-        "#   timeout -s KILL 90 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmc_fetch -o p"
+        "# commands (from /tmp, TMPDIR=/tmp; $REPO = the repository root, $OUT = an output directory):",
+        "#   timeout -s KILL 90 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/pmc_fetch -o p"
         " -- python3 $REPO/bench.py --probe",
-        "#   timeout -s KILL 90 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmc_write -o p"
+        "#   timeout -s KILL 90 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/pmc_write -o p"
         " -- python3 $REPO/bench.py --probe",
-        "#   python -m diffusion_transformer_image_mm_amd.traffic gpurun_out/pmc_fetch gpurun_out/pmc_write",
+        "#   python -m diffusion_transformer_image_mm_amd.traffic $OUT/pmc_fetch $OUT/pmc_write",
         f"# calibration: 1 GiB copy reads FETCH_SIZE {statistics.mean(cf):.0f} KiB -> factor {f_fac:.4f};"
         f" WRITE_SIZE {statistics.mean(cw):.0f} KiB -> factor {w_fac:.4f}",
         f"# gemm dispatches: {len(gf)} (FETCH_SIZE mean {statistics.mean(gf):.0f} KiB),"
