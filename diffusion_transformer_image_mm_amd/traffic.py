@@ -9,8 +9,9 @@ times and then copies 1 GiB device-to-device three times):
 
 ``python -m diffusion_transformer_image_mm_amd.traffic $OUT/pmc_fetch
 $OUT/pmc_write`` then writes the summary that bench.py reads ($REPO is the
-repository root, $OUT any output directory). Each counter (KiB per dispatch) is scaled by expected/measured for the copy of
-known size, and the result is tied to the SHA-256 of the kernel's sources
+repository root, $OUT any output directory). Each counter (KiB per
+dispatch) is scaled by expected/measured for the copy of known size, and the
+result is tied to the SHA-256 of the kernel's sources
 (k_gemm.hip and common.h): once they change, bench.py reports the traffic as
 unknown (null).
 """
