@@ -104,8 +104,8 @@ def main() -> int:
                          "for hardware-counter runs")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the sharded path is described in the design notes, not built)", file=sys.stderr)
+        print(f"bench.py: the library runs on a single GPU; --gpus {args.gpus} is not supported "
+              "(there is no sharded path)", file=sys.stderr)
         return 2
 
     import numpy as np
