@@ -449,11 +449,9 @@ def fp8_weights(w):
 
 
 def linear_act_fp8(x, lin) -> np.ndarray:
-    """A projection of the fp8 path: the activation rows x quantised per token
-    (``quantize_rows_fp8``), times the fp8 weights. The codes are integer
-    decisions, so they are taken on the operand as the fp8 path holds it
-    before quantising: a 16-bit (fp16) activation, divided in fp32."""
-    x16 = np.asarray(x, dtype=np.float64).astype(np.float16)
-    assert np.all(np.isfinite(x16)), "activation outside the fp16 range"
-    codes, sc = quantize_rows_fp8(x16.astype(np.float32))
+    """A projection of the fp8 path: the activation rows x (the oracle's own
+    fp64 values) quantised per token (``quantize_rows_fp8``: scale and code
+    decided in fp32, the precision the kernels decide them in), times the fp8
+    weights."""
+    codes, sc = quantize_rows_fp8(np.asarray(x, dtype=np.float64))
     return linear_fp8(codes, sc, lin.q, lin.s, lin.b)
