@@ -22,7 +22,7 @@ int check_dims(const mmdit_dims* d) {
     if (d->head_dim != 64 && d->head_dim != 128) return MMDIT_E_SHAPE;
     if (d->heads < 1 || d->hidden != d->heads * d->head_dim) return MMDIT_E_SHAPE;
     if (d->hidden % 64 != 0 || d->hidden > 4096) return MMDIT_E_SHAPE;
-    if (d->mlp_hidden < 64 || d->mlp_hidden % 64 != 0) return MMDIT_E_SHAPE;
+    if (d->mlp_hidden < 64 || d->mlp_hidden % 64 != 0 || d->mlp_hidden > 65536) return MMDIT_E_SHAPE;
     if (d->txt_len < 1 || d->img_len < 1) return MMDIT_E_SHAPE;
     if ((int64_t)d->txt_len + d->img_len > (1 << 20)) return MMDIT_E_SHAPE;
     int sum = 0;
@@ -758,6 +758,16 @@ int mmdit_k_gemm(const mmdit_gemm* g, hipStream_t s) {
     if (!g) return MMDIT_E_NULL;
     if (g->m < 1 || g->n < 64 || g->n % 64 != 0 || g->k < 64 || g->k % 64 != 0) return MMDIT_E_SHAPE;
     if (g->lda < g->k || g->lda % 8 != 0) return MMDIT_E_SHAPE;
+    // per-lane operand offsets are 32-bit within a 256-row tile (SwiGLU: a
+    // tile's up rows lie n/2 weight rows past its gate rows)
+    {
+        const uint64_t es = g->weight_dtype == MMDIT_FP8 ? 1 : 2;
+        const uint64_t w_rows = g->epilogue == MMDIT_EPI_SWIGLU || g->epilogue == MMDIT_EPI_SPLIT_SWIGLU
+                                    ? (uint64_t)g->n / 2 + 256 : 256;
+        if (256 * (uint64_t)g->lda * es + (uint64_t)g->k * es >= (1ull << 32) ||
+            w_rows * (uint64_t)g->k * es + (uint64_t)g->k * es >= (1ull << 32))
+            return MMDIT_E_SHAPE;
+    }
     if (!dtype_ok(g->weight_dtype) && g->weight_dtype != MMDIT_FP8) return MMDIT_E_DTYPE;
     if (g->epilogue < MMDIT_EPI_BIAS || g->epilogue > MMDIT_EPI_SPLIT_SWIGLU) return MMDIT_E_ARG;
     if (g->weight_dtype == MMDIT_FP8) {

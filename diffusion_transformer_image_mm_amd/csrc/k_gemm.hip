@@ -75,6 +75,8 @@
 //   accumulators in registers;
 // * M and N tails: loads clamp to the last valid row, stores are guarded;
 // * deterministic (no atomics, fixed k order).
+#include <atomic>
+
 #include "common.h"
 
 namespace mmdit {
@@ -227,13 +229,15 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
     const int sw_from = EPI == MMDIT_EPI_SPLIT_SWIGLU ? args.split_n : 0;
     const int sw_half = (N - sw_from) >> 1;
 
-    // ---- load descriptors: a uniform base plus a 32-bit per-lane byte
-    // offset (so the loads use the scalar-base addressing form). A tile:
-    // 256 rows x 8 chunks; wavefront w issues loads j = 0..3 of 8 rows each:
-    // lane i covers row r = (4w + j)*8 + i/8 at LDS position p = i%8,
-    // fetching chunk c = p ^ ((r >> 1) & 7).
+    // ---- load descriptors: a wave-uniform 64-bit base at the tile's first
+    // row plus a 32-bit per-lane byte offset within the tile (so the loads
+    // use the scalar-base addressing form, and the offsets span at most 256
+    // rows whatever the matrix size). A tile: 256 rows x 8 chunks; wavefront
+    // w issues loads j = 0..3 of 8 rows each: lane i covers row
+    // r = (4w + j)*8 + i/8 at LDS position p = i%8, fetching chunk
+    // c = p ^ ((r >> 1) & 7).
     const int lrow = lane >> 3, lpos = lane & 7;
-    const char* a_g = reinterpret_cast<const char*>(args.a) + (size_t)G.row0 * args.lda * ES;
+    const char* a_g = reinterpret_cast<const char*>(args.a) + ((size_t)G.row0 + tc.m0) * args.lda * ES;
     uint32_t a_off_g[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -241,12 +245,15 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
         const int c = lpos ^ ((r >> 1) & 7);
         int gr = tc.m0 + r;
         gr = gr < M ? gr : M - 1;
-        a_off_g[j] = (uint32_t)gr * (uint32_t)args.lda * (uint32_t)ES + (uint32_t)c * 16u;
+        a_off_g[j] = (uint32_t)(gr - tc.m0) * (uint32_t)args.lda * (uint32_t)ES + (uint32_t)c * 16u;
     }
     // W tile. bf16: same pattern as A over N rows. int8: 64 B per row = 4
     // units of 16 codes; a load covers 16 rows (lane i: row (2w + j)*16 +
     // i/4, position i%4); unit u of row r is stored at position u ^ ((r >> 2) & 3).
-    const char* w_g = static_cast<const char*>(G.w);
+    // The base row is the tile's first weight row (for SwiGLU columns the
+    // first gate row; its up rows lie sw_half rows further).
+    const int w_row0 = (SWIGLU && tc.n0 >= sw_from) ? sw_from + ((tc.n0 - sw_from) >> 1) : tc.n0;
+    const char* w_g = static_cast<const char*>(G.w) + (size_t)w_row0 * K * (INT8 ? 1 : ES);
     uint32_t w_off_g[WL];
     if (!INT8) {
 #pragma unroll
@@ -256,7 +263,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
             int gn = tc.n0 + r;
             gn = gn < N ? gn : N - 1;
             if (SWIGLU) gn = weight_row(gn, sw_from, sw_half);
-            w_off_g[j] = (uint32_t)gn * (uint32_t)K * (uint32_t)ES + (uint32_t)c * 16u;
+            w_off_g[j] = (uint32_t)(gn - w_row0) * (uint32_t)K * (uint32_t)ES + (uint32_t)c * 16u;
         }
     } else {
 #pragma unroll
@@ -266,7 +273,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
             int gn = tc.n0 + r;
             gn = gn < N ? gn : N - 1;
             if (SWIGLU) gn = weight_row(gn, sw_from, sw_half);
-            w_off_g[j] = (uint32_t)gn * (uint32_t)K + (uint32_t)u * 16u;
+            w_off_g[j] = (uint32_t)(gn - w_row0) * (uint32_t)K + (uint32_t)u * 16u;
         }
     }
 
@@ -737,17 +744,42 @@ static int launch_half_units(int n_half, int n_full, int cus) {
     return end;
 }
 
-// Compute units of the current device (queried once per device).
+constexpr int kMaxDevices = 64;
+
+// Compute units of the current device. The only per-process values the
+// library keeps are caches of device properties like this one, per device
+// and thread-safe (a relaxed atomic: every thread that races here stores the
+// same number); results never depend on them.
 static int cu_count() {
-    static int cached[16] = {0};
+    static std::atomic<int> cached[kMaxDevices];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 256;
-    if (cached[dev] == 0) {
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev < 0 || dev >= kMaxDevices) {
+        int n = 0;
+        return hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+    }
+    int c = cached[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
         int n = 0;
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
+        c = n;
     }
-    return cached[dev];
+    return c;
+}
+
+// Sets a kernel's dynamic-LDS limit on the current device once per device
+// (the attribute is per device; setting it again is harmless, so a race only
+// repeats the call). done: one bit per device of that kernel.
+static hipError_t lds_attribute_once(const void* kfn, int lds, std::atomic<uint64_t>& done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev >= 0 && dev < kMaxDevices ? (uint64_t)1 << dev : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+    return e;
 }
 
 template <int WT>
@@ -820,14 +852,9 @@ static hipError_t launch_gemm_t(const GemmArgs& a0, hipStream_t s) {
         return hipErrorInvalidValue;                                                        \
     } else {                                                                                \
         auto kfn = pipe ? gemm_kernel<WT, E, (WT == MMDIT_F16 ? 1 : 0)> : gemm_kernel<WT, E, 0>; \
-        static bool attr_done[2] = {false, false};                                          \
-        if (!attr_done[pipe]) {                                                             \
-            hipError_t e = hipFuncSetAttribute((const void*)kfn,                            \
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, \
-                                               (int)lds);                                   \
-            if (e != hipSuccess) return e;                                                  \
-            attr_done[pipe] = true;                                                         \
-        }                                                                                   \
+        static std::atomic<uint64_t> attr_done[2];                                          \
+        hipError_t e = lds_attribute_once((const void*)kfn, (int)lds, attr_done[pipe]);     \
+        if (e != hipSuccess) return e;                                                      \
         hipLaunchKernelGGL(kfn, grid, block, lds, s, a);                                    \
         break;                                                                              \
     }

@@ -29,6 +29,7 @@ and the joint sequence holds the text tokens first.
 from __future__ import annotations
 
 import dataclasses
+import os
 from concurrent.futures import ThreadPoolExecutor
 from typing import Dict, List, Optional, Tuple
 
@@ -159,7 +160,19 @@ def f16_exact(x: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 # seeded draws
 # --------------------------------------------------------------------------
+def _workers() -> int:
+    """Threads for the draws: the CPUs this process may run on, at most 16.
+    Results do not depend on it (every chunk has its own seed stream)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def _draw(cid: int, tid: int, n: int, kind: str, a: float, b: float) -> np.ndarray:
+    """n seeded draws, each rounded to bf16 (elementwise, so the chunking
+    and the thread count do not change the values)."""
     out = np.empty(n, dtype=np.float32)
     n_chunks = (n + _CHUNK - 1) // _CHUNK
 
@@ -174,31 +187,47 @@ def _draw(cid: int, tid: int, n: int, kind: str, a: float, b: float) -> np.ndarr
                 v += np.float32(a)
         else:
             v = rng.uniform(a, b, hi - lo).astype(np.float32)
-        out[lo:hi] = v
+        out[lo:hi] = bf16_exact(v)
 
     if n_chunks == 1:
         fill(0)
     else:
-        with ThreadPoolExecutor(max_workers=8) as ex:
+        with ThreadPoolExecutor(max_workers=_workers()) as ex:
             list(ex.map(fill, range(n_chunks)))
     return out
 
 
 def normal(cid: int, tid: int, shape, std: float = 1.0, mean: float = 0.0) -> np.ndarray:
     n = int(np.prod(shape))
-    return bf16_exact(_draw(cid, tid, n, "normal", mean, std)).reshape(shape)
+    return _draw(cid, tid, n, "normal", mean, std).reshape(shape)
 
 
 def uniform(cid: int, tid: int, shape, lo: float, hi: float) -> np.ndarray:
     n = int(np.prod(shape))
-    return bf16_exact(_draw(cid, tid, n, "uniform", lo, hi)).reshape(shape)
+    return _draw(cid, tid, n, "uniform", lo, hi).reshape(shape)
 
 
 def quantize_int8(w: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
-    """Symmetric per-output-channel int8 codes and fp32 scales of ``w`` [N, K]."""
-    amax = np.abs(w).max(axis=1).astype(np.float32)
-    s = np.where(amax > 0, amax / np.float32(127.0), np.float32(1.0)).astype(np.float32)
-    q = np.clip(np.rint(w / s[:, None]), -127, 127).astype(np.int8)
+    """Symmetric per-output-channel int8 codes and fp32 scales of ``w`` [N, K]
+    (row by row, so blocks of rows are done in parallel)."""
+    N = w.shape[0]
+    q = np.empty(w.shape, dtype=np.int8)
+    s = np.empty(N, dtype=np.float32)
+
+    def rows(r0: int) -> None:
+        r1 = min(N, r0 + 1024)
+        blk = w[r0:r1]
+        amax = np.abs(blk).max(axis=1).astype(np.float32)
+        sc = np.where(amax > 0, amax / np.float32(127.0), np.float32(1.0)).astype(np.float32)
+        q[r0:r1] = np.clip(np.rint(blk / sc[:, None]), -127, 127).astype(np.int8)
+        s[r0:r1] = sc
+
+    starts = range(0, N, 1024)
+    if N <= 1024:
+        rows(0)
+    else:
+        with ThreadPoolExecutor(max_workers=_workers()) as ex:
+            list(ex.map(rows, starts))
     return q, s
 
 
@@ -317,11 +346,21 @@ def block_inputs(shp: Shape, kind: str = "double", int8: bool = False,
     return {"shape": shp, "kind": kind, "x": x, "vec": vec, "ids": position_ids(shp), "w": w}
 
 
-def model_weights(shp: Shape, int8: bool = True, variant: int = 0) -> Dict[str, object]:
-    """Weights of a whole denoiser: embedders, blocks and the final layer."""
+def model_weights(shp: Shape, int8: bool = True, variant: int = 0, progress=None) -> Dict[str, object]:
+    """Weights of a whole denoiser: embedders, blocks and the final layer.
+    ``progress(kind, i, n)``, if given, is called after each block."""
     cid = shp.cid * 16 + variant
     ids = _Ids(100)
     H, C = shp.hidden, shp.in_channels
+
+    def blocks(kind, make, n):
+        out = []
+        for i in range(n):
+            out.append(make(cid, ids, shp, int8))
+            if progress is not None:
+                progress(kind, i + 1, n)
+        return out
+
     m = {
         "img_in": make_linear(cid, ids, H, C, int8),
         "time_in": [make_linear(cid, ids, H, 256, int8), make_linear(cid, ids, H, H, int8)],
@@ -329,8 +368,8 @@ def model_weights(shp: Shape, int8: bool = True, variant: int = 0) -> Dict[str, 
                     if shp.guidance_embed else None),
         "final_mod": make_linear(cid, ids, 2 * H, H, int8),
         "final_out": make_linear(cid, ids, C, H, int8),
-        "double": [double_weights(cid, ids, shp, int8) for _ in range(shp.n_double)],
-        "single": [single_weights(cid, ids, shp, int8) for _ in range(shp.n_single)],
+        "double": blocks("double", double_weights, shp.n_double),
+        "single": blocks("single", single_weights, shp.n_single),
     }
     if shp.shared_mod:
         # every block of a type uses the first block's modulation weights

@@ -26,9 +26,20 @@
  *   and each weight fragment is converted to fp16 in registers (exact for
  *   bf16 weights of magnitude >= 2^-14 and for int8 codes); every sum
  *   accumulates in fp32.
+ * - Range: fp16 holds magnitudes up to 65504. An activation operand beyond
+ *   that (a LayerNorm output with |(1 + scale)| or |shift| in the
+ *   thousands, an attention output of a value row beyond it, a GELU hidden
+ *   beyond it) is stored as +-inf (IEEE conversion, no saturation), so the
+ *   block output turns non-finite rather than silently wrong. The residual
+ *   stream, vec and the latent are fp32 and have no such limit. (DiT
+ *   activations after LayerNorm are O(10); the synthetic workloads stay far
+ *   inside the range.)
  * - The caller owns every buffer (weights, activations, tables, workspace).
- *   The library allocates nothing, frees nothing and keeps no state between
- *   calls; calls on different streams with distinct workspaces may overlap.
+ *   The library allocates nothing and frees nothing. The only values it
+ *   keeps between calls are per-device caches of device properties (the
+ *   compute-unit count, whether a kernel's LDS limit is set), thread-safe
+ *   and never affecting results; calls on different streams with distinct
+ *   workspaces may overlap.
  * - Every call only enqueues work on `stream` and returns; nothing is
  *   synchronised. Outputs are defined once the stream has reached the work.
  * - Arguments are validated before anything is enqueued: on a non-zero
@@ -97,7 +108,8 @@ enum mmdit_weight_dtype {
 /* ------------------------------------------------------------------ sizes */
 /*
  * Sizes of one model. H = heads * head_dim.
- *   head_dim in {64, 128}; hidden and mlp_hidden multiples of 64;
+ *   head_dim in {64, 128}; hidden a multiple of 64 up to 4096; mlp_hidden a
+ *   multiple of 64 up to 65536; txt_len + img_len up to 2^20;
  *   rope_axes[] even, summing to head_dim (axial RoPE over (t, h, w));
  *   txt_len >= 1, img_len >= 1; in_channels a multiple of 64 (64 for FLUX);
  *   n_double / n_single: block counts of a whole model (denoise step only).
@@ -393,7 +405,10 @@ enum mmdit_epilogue {
 
 /*
  * out = epilogue(A W^T): A fp16 [m, k] (row stride lda), W = w.w [n, k] bf16,
- * fp16 or int8 (weight_dtype). k a multiple of 64, n a multiple of 64, m >= 1.
+ * fp16 or int8 (weight_dtype). k a multiple of 64, n a multiple of 64, m >= 1;
+ * 256 * lda and (256 + n/2 for SwiGLU epilogues, else 256) * k, in bytes, below
+ * 4 GiB (the kernel addresses each 256-row tile with 32-bit offsets from its
+ * first row), else MMDIT_E_SHAPE.
  * bf16 and int8 weight fragments are converted to fp16 in registers (see
  * above);
  * accumulation in fp32; the int8 per-channel scale multiplies the fp32 sum.

@@ -55,6 +55,7 @@ def _double():
     ({"txt_len": 0}, B.MMDIT_E_SHAPE),
     ({"img_len": 0}, B.MMDIT_E_SHAPE),
     ({"mlp_hidden": 1000}, B.MMDIT_E_SHAPE),
+    ({"mlp_hidden": 65536 + 64}, B.MMDIT_E_SHAPE),   # beyond the documented maximum
     ({"weight_dtype": 5}, B.MMDIT_E_DTYPE),
     ({"mlp_act": 2}, B.MMDIT_E_ARG),
     ({"guidance_embed": 2}, B.MMDIT_E_ARG),
@@ -181,6 +182,15 @@ def test_kernel_entry_validation():
     assert B.mmdit_k_gemm(g) == B.MMDIT_E_SHAPE  # ldo < n / 2
     g.epilogue, g.n, g.ldo, g.split_n, g.out2, g.ldo2, g.out2_col = B.MMDIT_EPI_SPLIT_SWIGLU, 768, 256, 192, FAKE, 512, 256
     assert B.mmdit_k_gemm(g) == B.MMDIT_E_SHAPE  # split at 192: a SwiGLU tile would straddle it
+    # 32-bit per-lane offsets within a 256-row tile: 256 * lda * 2 bytes and
+    # 256 (SwiGLU: 256 + n/2) weight rows of k * 2 bytes must stay below 4 GiB
+    g = B.mmdit_gemm(m=10, n=128, k=64, weight_dtype=0, a=FAKE, lda=(1 << 23), w=_linear(), epilogue=0,
+                     out=FAKE, ldo=128)
+    assert B.mmdit_k_gemm(g) == B.MMDIT_E_SHAPE
+    g.lda, g.k = 1 << 23, 1 << 23
+    assert B.mmdit_k_gemm(g) == B.MMDIT_E_SHAPE
+    g.lda, g.k, g.n, g.ldo, g.epilogue = 4096, 4096, 1 << 20, 1 << 19, B.MMDIT_EPI_SWIGLU
+    assert B.mmdit_k_gemm(g) == B.MMDIT_E_SHAPE  # (256 + n/2) rows x 8 KB > 4 GiB
     lin = _linear()
     assert B.mmdit_k_gemv(FAKE, 100, lin, 10, 0, 1, 0, FAKE) == B.MMDIT_E_SHAPE
     assert B.mmdit_k_gemv(FAKE, 128, lin, 10, 3, 1, 0, FAKE) == B.MMDIT_E_DTYPE

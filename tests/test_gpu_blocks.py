@@ -85,9 +85,9 @@ def test_block_small_full_compare(shape, kind, wt):
     g = run_block(inp, int8, f16=wt == "f16")
     ref = oracle_block(inp)
     eb = _check(g, ref, inp["x"], f"{kind} {shape.name}")
-    # the update (x_out - x_in) carries the bf16 rounding of every operand
-    # stage (h, qkv, q/k, P, O, MLP hidden); it stays within 5x the bar
-    assert eb <= 5 * TOL, eb
+    # the update (x_out - x_in) alone, without the N(0,1) residual that
+    # dilutes the output's error, is held to the same bar
+    assert eb <= TOL, eb
 
 
 @pytest.mark.parametrize("kind", ["double", "single"])
@@ -173,7 +173,7 @@ def test_block_full_size_sampled_rows(shape, kind, f16):
     rows = np.unique(np.r_[0, Lt - 1, Lt, Lt + 1, L - 1, 127, 128, np.random.default_rng(shape.cid).integers(0, L, 40)])
     ref = oracle_block(inp, rows=rows)
     eb = _check(g[rows], ref, inp["x"][rows], f"{kind} {shape.name} rows={len(rows)}")
-    assert eb <= 5 * TOL, eb
+    assert eb <= TOL, eb
 
 
 @pytest.mark.parametrize("shape,kind", [(synth.TINY, "double"), (RAGGED_D128, "single")])
@@ -400,13 +400,13 @@ def _check_fp8(g, ref, x, label, out_tol=TOL, rms_tol=FP8_UPDATE_RMS):
 def test_block_fp8_small_full_compare(shape, kind):
     """fp8 operands in every projection (weights per channel, activations per
     token): against the oracle's fp8 block to the bar on the output. Both
-    sides decide the activation codes from fp16 values divided in fp32, but
-    the values ahead of them still differ slightly (q, k, v are stored in
-    bf16 here, fp64 there), so an element near a rounding boundary lands one
+    sides decide the activation codes in fp32, but the values ahead of them
+    differ slightly (the path stores them in fp16, and q, k, v in bf16; the
+    oracle keeps fp64), so an element near a rounding boundary lands one
     e4m3 step (6-12% of it) apart. That noise is sparse but large per
-    element, so the update is held to an RMS bound (3e-2; measured 0.2-0.7%)
-    rather than the max-norm one of the 16-bit paths. The distance to the
-    exact block (the price of fp8) is reported."""
+    element, so the update is held to an RMS bound (3e-2) rather than the
+    max-norm one of the 16-bit paths. The distance to the exact block (the
+    price of fp8) is reported."""
     say(f"block fp8 {kind} {shape.name}")
     inp = synth.block_inputs(shape, kind)
     g = run_block(inp, fp8=True)
@@ -424,23 +424,59 @@ def test_block_fp8_rerun_bit_exact():
     np.testing.assert_array_equal(a, b)
 
 
+def _oracle_fp8_with_path_storage(inp, rows):
+    """The oracle's fp8 block with the 16-bit storage of the HIP path applied
+    to its own intermediates: every projection's activation rounded to fp16
+    before it is quantised, and q, k, v rounded to bf16 before attention.
+    This is the same method on inputs moved by one 16-bit rounding; how far
+    it lands from the unrounded oracle is the method's own sensitivity to
+    that storage (the planted roundings live in this test, not in the
+    oracle)."""
+    from oracle import mmdit_oracle as M
+    lin_orig, att_orig = M.linear_act_fp8, M.attention
+
+    def f16(a):
+        return np.asarray(a, np.float64).astype(np.float16).astype(np.float64)
+
+    def bf16(a):
+        return synth.bf16_exact(np.asarray(a, np.float32)).astype(np.float64)
+    try:
+        M.linear_act_fp8 = lambda x, lin: lin_orig(f16(x), lin)
+        M.attention = lambda q, k, v, heads, rows=None: att_orig(bf16(q), bf16(k), bf16(v), heads, rows)
+        return oracle_block(inp, rows=rows, fp8=True)
+    finally:
+        M.linear_act_fp8, M.attention = lin_orig, att_orig
+
+
 @pytest.mark.parametrize("shape,kind", [(synth.FLUX_DOUBLE, "double"), (synth.FLUX_SINGLE, "single")])
 def test_block_fp8_full_size_sampled_rows(shape, kind):
-    """At FLUX size the double block's fp8 output is ill-conditioned in the
-    max norm: a code flip moves its element by a whole e4m3 step, so a
-    perturbation d of the values ahead of a quantiser changes a fraction ~d
-    of the codes, an error ~sqrt(d) per stage; LN2 after the first gated
-    residual passes it on to two more quantised projections. Rounding the
-    oracle's own q, k and v to bf16 (the path's storage of them) moves its
-    output by 0.28 max / RMS and its update by 2.5% RMS. So the double block
-    is held to the RMS bound on the update (5e-2) and a max-norm bound of
-    0.5 (a wrong scale, group or operand is O(1) in both); the single block,
-    with one quantised stage after its LayerNorm, to the bar."""
+    """fp8 blocks at FLUX size against the oracle's fp8 block. A per-token
+    activation code is a rounding decision: when the value ahead of the
+    quantiser moves by a relative d (here: the path's fp16 / bf16 storage of
+    its intermediates, d ~ 2^-11..2^-8), a fraction ~d / 2^-3 of the codes
+    flips by one whole e4m3 step (6-12% of the element). In the double block
+    LN2 reads the residual after the first gated projection, so those flips
+    reach two more quantised projections: the output's max-norm error is
+    then set by the method's conditioning, not by the arithmetic. The bar
+    is therefore derived per case from the oracle itself: the same oracle
+    block with the path's 16-bit storage applied to its intermediates
+    (_oracle_fp8_with_path_storage) lands E_max (max / RMS) and E_rms (RMS of
+    the update) from the unrounded one; an implementation with that storage
+    is a second, independent draw of the same flips, so it must land within
+    2 E_max and 2 E_rms of the oracle (and within the 2e-2 / 3e-2 bars when
+    those are larger). A wrong scale, group or operand is O(1) in both. The
+    fp8 double block at FLUX size is outside the 2e-2 parity claim of the
+    16-bit path: that is the method's conditioning at this size."""
     say(f"block fp8 full {kind} {shape.name}")
     inp = synth.block_inputs(shape, kind)
     g = run_block(inp, fp8=True)
     L, Lt = shape.seq_len, shape.txt_len
     rows = np.unique(np.r_[0, Lt - 1, Lt, Lt + 1, L - 1, 127, 128, np.random.default_rng(shape.cid).integers(0, L, 24)])
     ref = oracle_block(inp, rows=rows, fp8=True)
-    tol = dict(out_tol=0.5, rms_tol=5e-2) if kind == "double" else {}
-    _check_fp8(g[rows], ref, inp["x"][rows], f"fp8 {kind} {shape.name} rows={len(rows)}", **tol)
+    per = _oracle_fp8_with_path_storage(inp, rows)
+    x = inp["x"][rows]
+    e_max = rel_err(per, ref)
+    e_rms = float(np.sqrt(np.mean((per - ref) ** 2)) / np.sqrt(np.mean((ref - x) ** 2)))
+    say(f"  oracle's own sensitivity to 16-bit storage: max/RMS {e_max:.3e}, update RMS {e_rms:.3e}")
+    _check_fp8(g[rows], ref, x, f"fp8 {kind} {shape.name} rows={len(rows)}",
+               out_tol=max(TOL, 2 * e_max), rms_tol=max(FP8_UPDATE_RMS, 2 * e_rms))
