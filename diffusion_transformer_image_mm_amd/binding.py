@@ -37,6 +37,8 @@ lib = ctypes.CDLL(LIB_PATH)
 MMDIT_ABI_VERSION = 3
 MMDIT_OK, MMDIT_E_NULL, MMDIT_E_ALIGN, MMDIT_E_SHAPE = 0, 1, 2, 3
 MMDIT_E_DTYPE, MMDIT_E_WORKSPACE, MMDIT_E_HIP, MMDIT_E_ARG = 4, 5, 6, 7
+MMDIT_E_SCRATCH = 8
+MMDIT_NOALLOC_SCRATCH_BYTES = 4 << 20
 MMDIT_BF16, MMDIT_INT8, MMDIT_F16, MMDIT_FP8 = 0, 1, 2, 3
 MMDIT_WS_DOUBLE, MMDIT_WS_SINGLE, MMDIT_WS_STEP = 0, 1, 2
 (MMDIT_EPI_BIAS, MMDIT_EPI_BIAS_GELU, MMDIT_EPI_GATE_RESID, MMDIT_EPI_SPLIT_GELU,
@@ -121,6 +123,8 @@ _SIGS = {
     "mmdit_modulation_workspace_bytes": (c_size_t, [POINTER(mmdit_dims), c_int]),
     "mmdit_modulation_batch": (c_int, [POINTER(mmdit_dims), POINTER(mmdit_model), POINTER(c_float), c_int, c_float,
                                        _P, _P, c_size_t, _P]),
+    "mmdit_modulation_batch_noalloc": (c_int, [POINTER(mmdit_dims), POINTER(mmdit_model), POINTER(c_float), c_int,
+                                               c_float, _P, _P]),
     "mmdit_denoise_step_premod": (c_int, [POINTER(mmdit_dims), POINTER(mmdit_model), _P, _P, _P, _P, c_float,
                                           c_float, _P, c_size_t, _P]),
     "mmdit_k_ln_modulate": (c_int, [_P, c_int, c_int, c_int, _P, _P, _P, _P, c_float, _P, _P]),
@@ -200,6 +204,14 @@ def mmdit_modulation_batch(dims, model, t, guidance, mod, ws, ws_bytes, stream=N
     arr = (c_float * max(n, 1))(*[float(v) for v in t])
     return lib.mmdit_modulation_batch(ctypes.byref(dims), ctypes.byref(model), arr, n, guidance, ptr(mod),
                                       ptr(ws), ws_bytes, stream_handle(stream))
+
+
+def mmdit_modulation_batch_noalloc(dims, model, t, guidance, mod, stream=None) -> int:
+    """t: a sequence of step times (host); marshalled to a float32 array."""
+    n = len(t)
+    arr = (c_float * max(n, 1))(*[float(v) for v in t])
+    return lib.mmdit_modulation_batch_noalloc(ctypes.byref(dims), ctypes.byref(model), arr, n, guidance, ptr(mod),
+                                              stream_handle(stream))
 
 
 def mmdit_denoise_step_premod(dims, model, mod, latent, txt, rope, t_cur, t_next, ws, ws_bytes,

@@ -1,5 +1,6 @@
 // C ABI of libmmdit.so: argument validation, workspace carving and the
 // orchestration of the block / step kernels on one stream.
+#include <atomic>
 #include <cmath>
 
 #include "common.h"
@@ -569,6 +570,7 @@ const char* mmdit_status_string(int st) {
         case MMDIT_E_WORKSPACE: return "workspace too small";
         case MMDIT_E_HIP: return "kernel launch failed";
         case MMDIT_E_ARG: return "invalid argument";
+        case MMDIT_E_SCRATCH: return "sizes exceed the fixed scratch of the no-allocation entry point";
         default: return "unknown status";
     }
 }
@@ -643,8 +645,13 @@ size_t mmdit_modulation_workspace_bytes(const mmdit_dims* d, int n_steps) {
     return c.off;
 }
 
-int mmdit_modulation_batch(const mmdit_dims* d, const mmdit_model* m, const float* t, int n_steps,
-                           float guidance, float* mod, void* ws, size_t ws_bytes, hipStream_t s) {
+}  // extern "C"
+
+namespace {
+
+// Arguments of a modulation batch, apart from its workspace.
+int modbatch_args_ok(const mmdit_dims* d, const mmdit_model* m, const float* t, int n_steps, float guidance,
+                     const float* mod) {
     MMDIT_TRY(check_dims(d));
     MMDIT_TRY(model_ok(d, m));
     if (!t) return MMDIT_E_NULL;
@@ -653,10 +660,16 @@ int mmdit_modulation_batch(const mmdit_dims* d, const mmdit_model* m, const floa
         if (!std::isfinite(t[i])) return MMDIT_E_ARG;
     if (!std::isfinite(guidance)) return MMDIT_E_ARG;
     MMDIT_TRY(check_ptr(mod));
-    MMDIT_TRY(check_ptr(ws));
+    return MMDIT_OK;
+}
+
+// The modulation batch after validation, on a workspace of at least
+// mmdit_modulation_workspace_bytes(d, n_steps) bytes. Every workspace byte it
+// reads it has written first in the same call.
+int run_modbatch(const mmdit_dims* d, const mmdit_model* m, const float* t, int n_steps, float guidance,
+                 float* mod, void* ws, hipStream_t s) {
     Carver c(ws);
     const ModBatchWs w = carve_modbatch(d, n_steps, c);
-    if (ws_bytes < c.off) return MMDIT_E_WORKSPACE;
     const int H = d->hidden, dt = d->weight_dtype;
     const int ld = (int)mod_floats(d);
     // conditioning vectors of every step, then SiLU(vec) as the fp16 operand
@@ -676,6 +689,53 @@ int mmdit_modulation_batch(const mmdit_dims* d, const mmdit_model* m, const floa
     for (int b = 0; b < d->n_single; ++b) MMDIT_TRY(mod_gemm(m->singles[b].mod, 3 * H, mod_single_off(d, b)));
     MMDIT_TRY(mod_gemm(m->final_mod, 2 * H, mod_final_off(d)));
     return MMDIT_OK;
+}
+
+// ---- the scratch of mmdit_modulation_batch_noalloc: a fixed device array
+// in the library's code object, one copy per GPU, held until the process
+// ends. Host code never uses the array's name as an address: the name is a
+// host-side stand-in, so each device's address is looked up once, with that
+// device current, and kept.
+__device__ __align__(256) char scratch[MMDIT_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kScratchDevices = 64;
+
+// This device's address of `scratch` (null on failure).
+void* scratch_on_current_device() {
+    static std::atomic<void*> addr[kScratchDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return nullptr;
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        addr[dev].store(p, std::memory_order_release);   // a racing thread stores the same address
+    }
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mmdit_modulation_batch(const mmdit_dims* d, const mmdit_model* m, const float* t, int n_steps,
+                           float guidance, float* mod, void* ws, size_t ws_bytes, hipStream_t s) {
+    MMDIT_TRY(modbatch_args_ok(d, m, t, n_steps, guidance, mod));
+    MMDIT_TRY(check_ptr(ws));
+    Carver c(nullptr);
+    carve_modbatch(d, n_steps, c);
+    if (ws_bytes < c.off) return MMDIT_E_WORKSPACE;
+    return run_modbatch(d, m, t, n_steps, guidance, mod, ws, s);
+}
+
+int mmdit_modulation_batch_noalloc(const mmdit_dims* d, const mmdit_model* m, const float* t, int n_steps,
+                                   float guidance, float* mod, hipStream_t s) {
+    MMDIT_TRY(modbatch_args_ok(d, m, t, n_steps, guidance, mod));
+    Carver c(nullptr);
+    carve_modbatch(d, n_steps, c);
+    if (c.off > MMDIT_NOALLOC_SCRATCH_BYTES) return MMDIT_E_SCRATCH;
+    void* ws = scratch_on_current_device();
+    if (!ws) return MMDIT_E_HIP;
+    return run_modbatch(d, m, t, n_steps, guidance, mod, ws, s);
 }
 
 int mmdit_denoise_step_premod(const mmdit_dims* d, const mmdit_model* m, const float* mod, float* latent,

@@ -76,7 +76,9 @@ enum mmdit_status {
     MMDIT_E_DTYPE = 4,     /* unknown weight dtype, or int8 weights without scales */
     MMDIT_E_WORKSPACE = 5, /* workspace too small */
     MMDIT_E_HIP = 6,       /* a kernel launch failed */
-    MMDIT_E_ARG = 7        /* another invalid argument (unknown enum value) */
+    MMDIT_E_ARG = 7,       /* another invalid argument (unknown enum value) */
+    MMDIT_E_SCRATCH = 8    /* sizes need more than the fixed scratch of a
+                              no-allocation entry point */
 };
 
 enum mmdit_weight_dtype {
@@ -295,6 +297,26 @@ size_t mmdit_modulation_workspace_bytes(const mmdit_dims* dims, int n_steps);
 int mmdit_modulation_batch(const mmdit_dims* dims, const mmdit_model* model,
                            const float* t, int n_steps, float guidance,
                            float* mod, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * mmdit_modulation_batch without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation). Its scratch is a fixed device
+ * array inside the library, MMDIT_NOALLOC_SCRATCH_BYTES per GPU, held from
+ * the library's load until the process ends; this entry point allocates and
+ * frees nothing. Sizes whose workspace (mmdit_modulation_workspace_bytes)
+ * exceeds it are rejected with MMDIT_E_SCRATCH before anything is enqueued:
+ * 4 MiB covers n_steps * hidden up to about 650 K (256 steps up to hidden
+ * 2560; 28 steps at any hidden size the library accepts). The result is
+ * bit-identical to mmdit_modulation_batch's. Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller. Each call writes every
+ * scratch byte before it reads it, so no clearing is needed.
+ */
+#define MMDIT_NOALLOC_SCRATCH_BYTES (4u << 20)
+int mmdit_modulation_batch_noalloc(const mmdit_dims* dims, const mmdit_model* model,
+                                   const float* t, int n_steps, float guidance,
+                                   float* mod, hipStream_t stream);
 
 /*
  * mmdit_denoise_step with the modulation given: mod is this step's row of

@@ -22,7 +22,7 @@ def test_exports_every_header_function():
 
 def test_abi_version_and_status_strings():
     assert B.mmdit_abi_version() == B.MMDIT_ABI_VERSION == 3
-    for st in range(8):
+    for st in range(9):
         assert B.mmdit_status_string(st)
     assert B.mmdit_status_string(99) == "unknown status"
 
@@ -238,3 +238,22 @@ def test_one_hip_runtime_per_process():
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
                        cwd=__import__("os").path.dirname(__import__("os").path.dirname(__file__)))
     assert r.stdout.strip() == "True", r.stderr
+
+
+def test_modulation_batch_noalloc_rejects_sizes_beyond_its_scratch():
+    shp = synth.custom_shape("noalloc-big-h4096", 732, 4096, 32, 4096, 8, (2, 2), n_double=1, n_single=1)
+    d = dims_for(shp, True)
+    need = B.mmdit_modulation_workspace_bytes(d, 256)
+    assert need > B.MMDIT_NOALLOC_SCRATCH_BYTES
+    m = B.mmdit_model()
+    lin = B.mmdit_linear(FAKE, FAKE, FAKE)
+    for k in ("img_in", "final_mod", "final_out"):
+        setattr(m, k, lin)
+    m.time_in[0] = m.time_in[1] = m.guid_in[0] = m.guid_in[1] = lin
+    s = B.mmdit_stream_weights(lin, lin, lin, lin, lin, FAKE, FAKE)
+    dbl = (B.mmdit_double_weights * 1)(B.mmdit_double_weights(s, s))
+    sgl = (B.mmdit_single_weights * 1)(B.mmdit_single_weights(lin, lin, lin, FAKE, FAKE))
+    m.doubles, m.singles = dbl, sgl
+    st = B.mmdit_modulation_batch_noalloc(d, m, [0.5] * 256, 3.5, FAKE)
+    assert st == B.MMDIT_E_SCRATCH, st
+    assert "scratch" in B.mmdit_status_string(st)
