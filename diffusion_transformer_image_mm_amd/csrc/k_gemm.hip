@@ -125,19 +125,30 @@ MMDIT_DEV f16x8_t bf16x8_to_f16x8(uint4 v) {
     return r;
 }
 
-// 8 int8 codes -> 8 fp16 (exact), pairwise.
+// 8 int8 codes -> 8 fp16 (exact) with 10 VALU operations. A code x biased
+// to the byte u = x + 128 (xor 0x80) and placed under the fp16 exponent
+// byte 0x64 is the fp16 number 1024 + u (ten mantissa bits hold u exactly);
+// one packed fp16 subtraction of 1152 then leaves x, exactly. Per dword of
+// four codes: one xor, two byte permutes, two packed subtractions (the
+// conversion through fp32 took ~3 operations per code, and that VALU work
+// delayed the matrix cores).
 MMDIT_DEV f16x8_t i8x8_to_f16x8(uint2 raw) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const uint32_t w[2] = {raw.x ^ 0x80808080u, raw.y ^ 0x80808080u};
+    const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
     f16x8_t r;
-    const int32_t w[2] = {(int32_t)raw.x, (int32_t)raw.y};
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const float a = (float)((w[h] << (24 - 16 * i)) >> 24);
-            const float b = (float)((w[h] << (16 - 16 * i)) >> 24);
-            r[4 * h + 2 * i] = static_cast<_Float16>(a);
-            r[4 * h + 2 * i + 1] = static_cast<_Float16>(b);
-        }
+    for (int h = 0; h < 2; ++h) {
+        // bytes [0x64, u1, 0x64, u0] and [0x64, u3, 0x64, u2]
+        const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, w[h], 0x04010400u);
+        const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, w[h], 0x04030402u);
+        const f16x2 a = __builtin_bit_cast(f16x2, lo) - bias;
+        const f16x2 b = __builtin_bit_cast(f16x2, hi) - bias;
+        r[4 * h] = a[0];
+        r[4 * h + 1] = a[1];
+        r[4 * h + 2] = b[0];
+        r[4 * h + 3] = b[1];
+    }
     return r;
 }
 
