@@ -379,14 +379,14 @@ def main() -> int:
     if not args.no_step:
         del A
         torch.cuda.empty_cache()
-        for key in ("f16", "int8"):
-            int8, f16 = key == "int8", key == "f16"
+        for key in ("f16", "int8", "fp8"):
+            int8, f16, fp8 = key == "int8", key == "f16", key == "fp8"
             sshp = synth.FLUX_STEP
             log(f"bench: generating full FLUX-shaped step weights on the device ({key})")
-            tm = TimingModel(sshp, int8=int8, seed=42, f16=f16)
+            tm = TimingModel(sshp, int8=int8, seed=42, f16=f16, fp8=fp8)
             mm = tm.model
             S = DeviceArena()
-            sd = dims_for(sshp, int8, f16)
+            sd = dims_for(sshp, int8, f16, fp8)
             srope = S.empty_f32(sshp.seq_len, sshp.head_dim // 2, 2)
             B.check(B.mmdit_rope_table(sd, S.i32(synth.position_ids(sshp)), srope, stream), "rope")
             st = synth.step_inputs(sshp)

@@ -490,11 +490,13 @@ ModBatchWs carve_modbatch(const mmdit_dims* d, int n_steps, Carver& c) {
     return w;
 }
 
+// Weight type of the step's patch embedding, final projection and batched
+// modulation GEMMs: their activation operands stay 16-bit, so an fp8 model's
+// weights there are decoded to fp16 in registers (fp8 weight-only).
+int io_wtype(int dt) { return dt == MMDIT_FP8 ? WT_FP8_W16A : dt; }
+
 int model_ok(const mmdit_dims* d, const mmdit_model* m) {
     if (!m) return MMDIT_E_NULL;
-    // fp8 operands are wired into the blocks only (the step's patch embedding
-    // and final projection take 16-bit operands)
-    if (d->weight_dtype == MMDIT_FP8) return MMDIT_E_DTYPE;
     if (d->in_channels < 64 || d->in_channels % 64 != 0) return MMDIT_E_SHAPE;
     if (d->n_double < 0 || d->n_single < 0) return MMDIT_E_SHAPE;
     const int dt = d->weight_dtype;
@@ -527,7 +529,7 @@ int run_step(const mmdit_dims* d, const mmdit_model* m, const float* premod, flo
         if (blocks > 4096) blocks = 4096;
         hipLaunchKernelGGL(f32_to_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, latent, sw.z16, n);
         MMDIT_HIP(hipGetLastError());
-        GemmArgs g = gemm_base(H, C, dt, sw.z16, C, MMDIT_EPI_BIAS_F32, sw.x + (size_t)Lt * H, H);
+        GemmArgs g = gemm_base(H, C, io_wtype(dt), sw.z16, C, MMDIT_EPI_BIAS_F32, sw.x + (size_t)Lt * H, H);
         MMDIT_HIP(gemm_1(g, group(0, Li, m->img_in), s));
     }
     Carver cb(sw.blocks);
@@ -546,7 +548,7 @@ int run_step(const mmdit_dims* d, const mmdit_model* m, const float* premod, flo
     MMDIT_HIP(launch_ln_modulate(sw.x + (size_t)Lt * H, Ln, H, 0, fmod, fmod + H, fmod, fmod + H, d->ln_eps,
                                  dws.h, s));
     {
-        GemmArgs g = gemm_base(C, H, dt, dws.h, H, MMDIT_EPI_EULER, latent, C);
+        GemmArgs g = gemm_base(C, H, io_wtype(dt), dws.h, H, MMDIT_EPI_EULER, latent, C);
         g.alpha = t_next - t_cur;
         MMDIT_HIP(gemm_1(g, group(0, Ln, m->final_out), s));
     }
@@ -678,7 +680,7 @@ int run_modbatch(const mmdit_dims* d, const mmdit_model* m, const float* t, int 
     MMDIT_HIP(launch_silu_to_f16(w.vecs, w.a16, (int64_t)n_steps * H, s));
     // one GEMM per modulation linear over all steps: each weight is read once
     auto mod_gemm = [&](const mmdit_linear& l, int n, size_t off) -> int {
-        GemmArgs g = gemm_base(n, H, dt, w.a16, H, MMDIT_EPI_BIAS_F32, mod + off, ld);
+        GemmArgs g = gemm_base(n, H, io_wtype(dt), w.a16, H, MMDIT_EPI_BIAS_F32, mod + off, ld);
         MMDIT_HIP(gemm_1(g, group(0, n_steps, l), s));
         return MMDIT_OK;
     };

@@ -119,6 +119,14 @@ struct GemmGroup {
 // per-kernel entry): columns [q | k | v] of the joint sequence; q and k get
 // per-head RMSNorm and RoPE and go to [heads, l_pad, D], v to the transposed,
 // quad-swapped [heads, D, l_pad] layout the attention kernel reads.
+// Internal weight type (not in the ABI's enum): OCP e4m3 weight codes with an
+// fp32 scale per output channel, against 16-bit (fp16) activations; each
+// weight fragment is decoded to fp16 in registers (exact) and the scale
+// multiplies the fp32 sum, as for int8 codes. The fp8 denoise step uses it
+// for its patch embedding, final projection and batched modulation, whose
+// activation operands stay 16-bit.
+constexpr int WT_FP8_W16A = 16;
+
 constexpr int EPI_QKV_ATTN = 64;
 // The single-stream block's linear1 ([q | k | v | mlp] columns): the split
 // GELU / SwiGLU epilogues whose first split_n = 3H columns take the

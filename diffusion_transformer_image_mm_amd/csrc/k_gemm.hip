@@ -152,6 +152,23 @@ MMDIT_DEV f16x8_t i8x8_to_f16x8(uint2 raw) {
     return r;
 }
 
+// 8 OCP e4m3 codes -> 8 fp16 (exact: every e4m3 value is an fp16 value), two
+// codes per conversion instruction through fp32.
+MMDIT_DEV f16x8_t fp8x8_to_f16x8(uint2 raw) {
+    f16x8_t r;
+    const uint32_t w[2] = {raw.x, raw.y};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[h], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[h], true);
+        r[4 * h] = static_cast<_Float16>(lo[0]);
+        r[4 * h + 1] = static_cast<_Float16>(lo[1]);
+        r[4 * h + 2] = static_cast<_Float16>(hi[0]);
+        r[4 * h + 3] = static_cast<_Float16>(hi[1]);
+    }
+    return r;
+}
+
 struct TileCoord {
     int g;       // group
     int m0;      // first row of the tile within the group
@@ -217,13 +234,15 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
     constexpr bool INT8 = WT == MMDIT_INT8;
     constexpr bool F16W = WT == MMDIT_F16;
     constexpr bool FP8 = WT == MMDIT_FP8;      // fp8 A and W, 128 k per stage
+    constexpr bool FP8W = WT == WT_FP8_W16A;   // fp8 W decoded to fp16 against fp16 A
+    constexpr bool W8 = INT8 || FP8W;          // one-byte weights in the int8 LDS layout
     constexpr bool SWIGLU = EPI == MMDIT_EPI_SWIGLU || EPI == MMDIT_EPI_SPLIT_SWIGLU;
     static_assert(PIPE == 0 || F16W, "the pipelined main loop reads plain fp16 weight fragments");
     static_assert(TNW == 4 || (TNW == 2 && PIPE == 0 && !SWIGLU), "tail tiles: plain loop, no SwiGLU");
     static_assert(!FP8 || (TNW == 4 && !SWIGLU), "fp8: 256-wide tiles, no SwiGLU epilogue");
     constexpr int ES = FP8 ? 1 : 2;            // bytes per element of A (and of 16-bit / fp8 W)
     constexpr int BNT = 64 * TNW;                                 // tile width (output columns)
-    constexpr int W_TILE = BNT * BK * (INT8 ? 1 : 2);             // fp16 weights: as bf16
+    constexpr int W_TILE = BNT * BK * (W8 ? 1 : 2);               // fp16 weights: as bf16
     constexpr int STAGE = A_TILE_BYTES + W_TILE;
     constexpr int TM = 8, TN = TNW;   // MFMA sub-tiles per wavefront (m, n)
     constexpr int WL = TNW, WL8 = TNW / 2;   // W loads per wavefront per stage (16-bit, int8)
@@ -264,9 +283,9 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
     // The base row is the tile's first weight row (for SwiGLU columns the
     // first gate row; its up rows lie sw_half rows further).
     const int w_row0 = (SWIGLU && tc.n0 >= sw_from) ? sw_from + ((tc.n0 - sw_from) >> 1) : tc.n0;
-    const char* w_g = static_cast<const char*>(G.w) + (size_t)w_row0 * K * (INT8 ? 1 : ES);
+    const char* w_g = static_cast<const char*>(G.w) + (size_t)w_row0 * K * (W8 ? 1 : ES);
     uint32_t w_off_g[WL];
-    if (!INT8) {
+    if (!W8) {
 #pragma unroll
         for (int j = 0; j < WL; ++j) {
             const int r = (wave * WL + j) * 8 + lrow;
@@ -299,7 +318,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
         for (int j = 0; j < 4; ++j)
             dma(a_g + (a_off_g[j] + ka), (lds_void*)(base + ((wave * 4 + j) * 8) * 128));
         char* wb = base + A_TILE_BYTES;
-        if (!INT8) {
+        if (!W8) {
 #pragma unroll
             for (int j = 0; j < WL; ++j)
                 dma(w_g + (w_off_g[j] + ka), (lds_void*)(wb + ((wave * WL + j) * 8) * 128));
@@ -319,7 +338,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
     for (int ks = 0; ks < 2; ++ks) {
         const int c = ks * 4 + lg;
         a_off[ks] = (wm * 128 + lr) * 128 + ((c ^ ((lr >> 1) & 7)) * 16);
-        if (!INT8)
+        if (!W8)
             w_off[ks] = (wn * 16 * TNW + lr) * 128 + ((c ^ ((lr >> 1) & 7)) * 16);
         else
             w_off[ks] = (wn * 16 * TNW + lr) * 64 + (((c >> 1) ^ ((lr >> 2) & 3)) * 16) + (c & 1) * 8;
@@ -439,10 +458,12 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
             for (int i = 0; i < TN; ++i) {
                 if (F16W)
                     fw[ks][i] = lds_frag_h(sw + w_off[ks] + i * 16 * 128);
-                else if (!INT8)
+                else if (!W8)
                     fw[ks][i] = bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(sw + w_off[ks] + i * 16 * 128));
-                else
+                else if (INT8)
                     fw[ks][i] = i8x8_to_f16x8(*reinterpret_cast<const uint2*>(sw + w_off[ks] + i * 16 * 64));
+                else
+                    fw[ks][i] = fp8x8_to_f16x8(*reinterpret_cast<const uint2*>(sw + w_off[ks] + i * 16 * 64));
             }
         }
         if (kt + 1 < nk) issue_stage(kt + 1, s ^ 1);
@@ -481,7 +502,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
             const float b_g[4] = {bf2f(bg.x & 0xffff), bf2f(bg.x >> 16), bf2f(bg.y & 0xffff), bf2f(bg.y >> 16)};
             const float b_u[4] = {bf2f(bu.x & 0xffff), bf2f(bu.x >> 16), bf2f(bu.y & 0xffff), bf2f(bu.y >> 16)};
             float s_g[4] = {1.f, 1.f, 1.f, 1.f}, s_u[4] = {1.f, 1.f, 1.f, 1.f};
-            if (INT8) {
+            if (INT8 || FP8W) {
                 const float4 a4 = *reinterpret_cast<const float4*>(G.scale + ng);
                 const float4 c4 = *reinterpret_cast<const float4*>(G.scale + nu);
                 s_g[0] = a4.x; s_g[1] = a4.y; s_g[2] = a4.z; s_g[3] = a4.w;
@@ -515,7 +536,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
             const uint2 braw = *reinterpret_cast<const uint2*>(G.bias + n);
             const float b[4] = {bf2f(braw.x & 0xffff), bf2f(braw.x >> 16), bf2f(braw.y & 0xffff), bf2f(braw.y >> 16)};
             float sc[4] = {1.f, 1.f, 1.f, 1.f};
-            if (INT8 || FP8) {
+            if (INT8 || FP8 || FP8W) {
                 const float4 s4 = *reinterpret_cast<const float4*>(G.scale + n);
                 sc[0] = s4.x; sc[1] = s4.y; sc[2] = s4.z; sc[3] = s4.w;
             }
@@ -644,7 +665,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
         b[in][2] = bf2f(braw.y & 0xffff); b[in][3] = bf2f(braw.y >> 16);
 #pragma unroll
         for (int j = 0; j < 4; ++j) { sc[in][j] = 1.f; gt[in][j] = 0.f; }
-        if (INT8 || FP8) {
+        if (INT8 || FP8 || FP8W) {
             const float4 s4 = *reinterpret_cast<const float4*>(G.scale + nc);
             sc[in][0] = s4.x; sc[in][1] = s4.y; sc[in][2] = s4.z; sc[in][3] = s4.w;
         }
@@ -795,7 +816,7 @@ static hipError_t lds_attribute_once(const void* kfn, int lds, std::atomic<uint6
 
 template <int WT>
 static hipError_t launch_gemm_t(const GemmArgs& a0, hipStream_t s) {
-    constexpr bool INT8 = WT == MMDIT_INT8;
+    constexpr bool W8 = WT == MMDIT_INT8 || WT == WT_FP8_W16A;   // one-byte weight tiles
     GemmArgs a = a0;
     const int tn = (a.n + BN - 1) / BN;
     int tmt = 0;
@@ -854,7 +875,7 @@ static hipError_t launch_gemm_t(const GemmArgs& a0, hipStream_t s) {
     // and the RMSNorm partial sums in LDS after the main loop
     const bool attn_epi = a.epilogue == EPI_QKV_ATTN || a.epilogue == EPI_SPLIT_GELU_ATTN ||
                           a.epilogue == EPI_SPLIT_SWIGLU_ATTN;
-    const size_t lds_main = 2 * (size_t)(A_TILE_BYTES + (INT8 ? W_TILE_BYTES_I8 : W_TILE_BYTES_BF16));
+    const size_t lds_main = 2 * (size_t)(A_TILE_BYTES + (W8 ? W_TILE_BYTES_I8 : W_TILE_BYTES_BF16));
     const size_t lds_epi = 256 * 128 * 4 + 4 * 256 * 4;
     const size_t lds = attn_epi && lds_epi > lds_main ? lds_epi : lds_main;
     dim3 grid(tiles), block(NTHREADS);
@@ -921,6 +942,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
         case MMDIT_INT8: return launch_gemm_t<MMDIT_INT8>(a, s);
         case MMDIT_F16: return launch_gemm_t<MMDIT_F16>(a, s);
         case MMDIT_FP8: return launch_gemm_t<MMDIT_FP8>(a, s);
+        case WT_FP8_W16A: return launch_gemm_t<WT_FP8_W16A>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

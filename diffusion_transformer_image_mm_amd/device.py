@@ -143,16 +143,19 @@ class TimingModel:
     device generator), for timing the full-depth step where host generation
     of ~12 B parameters would dominate. bf16 layers: N(0, 0.02) weights and
     biases; int8 layers: codes uniform on [-127, 127] with a per-channel scale
-    of 0.02 / 73.6 (the codes' standard deviation), so W has std 0.02;
+    of 0.02 / 73.6 (the codes' standard deviation), so W has std 0.02; fp8
+    layers: the bf16 draws quantised per output channel on the device;
     RMSNorm scales U(0.5, 1.5). Values are not checked against the oracle
     (the parity tests use the host generator)."""
 
-    def __init__(self, shp: synth.Shape, int8: bool, seed: int = 42, device: str = "cuda", f16: bool = False):
+    def __init__(self, shp: synth.Shape, int8: bool, seed: int = 42, device: str = "cuda", f16: bool = False,
+                 fp8: bool = False):
         self.dev = torch.device(device)
         self.gen = torch.Generator(device=self.dev)
         self.gen.manual_seed(seed)
         self.int8 = int8
         self.f16 = f16 and not int8
+        self.fp8 = fp8 and not int8 and not f16
         self.keep: List[torch.Tensor] = []
         H, M, C, D = shp.hidden, shp.mlp, shp.in_channels, shp.head_dim
         MO = shp.mlp_out
@@ -199,6 +202,9 @@ class TimingModel:
             s = self._hold(torch.full((n,), 0.02 / 73.6, device=self.dev, dtype=torch.float32))
             return B.mmdit_linear(q, s, b)
         w = (torch.randn(n, k, generator=self.gen, device=self.dev) * 0.02).to(torch.bfloat16)
+        if self.fp8:
+            codes, scales = to_fp8_weights(w)
+            return B.mmdit_linear(self._hold(codes), self._hold(scales), b)
         if self.f16:
             w = to_f16_weights(w)
         return B.mmdit_linear(self._hold(w), None, b)

@@ -104,7 +104,11 @@ enum mmdit_weight_dtype {
                        operand is quantised per token right before its GEMM
                        (LayerNorm outputs, attention output, GELU hidden);
                        attention and the residual stream are unchanged. The
-                       step entries do not accept it (MMDIT_E_DTYPE) */
+                       step entries accept it too: the blocks as above; the
+                       embedders, modulations, patch embedding and final
+                       projection keep 16-bit (fp32 for the GEMVs)
+                       activations against the fp8 weights, decoded exactly
+                       in registers (fp8 weight-only) */
 };
 
 /* ------------------------------------------------------------------ sizes */

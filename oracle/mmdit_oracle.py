@@ -352,29 +352,35 @@ def euler(z, v, t_cur: float, t_next: float) -> np.ndarray:
     return _f64(z) + (float(t_next) - float(t_cur)) * _f64(v)
 
 
-def velocity(z, txt, ids, m, shp, t_cur: float, guidance: float) -> np.ndarray:
+def velocity(z, txt, ids, m, shp, t_cur: float, guidance: float, fp8: bool = False) -> np.ndarray:
     """The denoiser's prediction v for latent z [L_i, C] and text states
     txt [L_t, H]: embed, run the double then the single blocks, and apply the
     final modulated LayerNorm and projection to the image rows. When editing,
     the last ``shp.ref_len`` rows of z are the encoded reference image: they
     are embedded and attended to like the others, and v covers only the rows
-    before them."""
+    before them. With ``fp8`` every linear takes its fp8 form
+    (``fp8_weights``): the blocks' projections on per-token fp8 activations
+    (``double_block`` / ``single_block`` with ``fp8``), the embedders, the
+    modulations and the final projection on the fp8 weights alone."""
+    if fp8:
+        m = fp8_weights(m)
     vec = conditioning(t_cur, guidance, m)
     x = np.concatenate([_f64(txt), linear(z, m["img_in"])], axis=0)
     for wd in m["double"]:
-        x = double_block(x, vec, ids, wd, shp)
+        x = double_block(x, vec, ids, wd, shp, fp8=fp8)
     for ws in m["single"]:
-        x = single_block(x, vec, ids, ws, shp)
+        x = single_block(x, vec, ids, ws, shp, fp8=fp8)
     sh, sc = modulation(vec, m["final_mod"], 2)
     n = shp.img_len - shp.ref_len
     h = ln_modulate(x[shp.txt_len:shp.txt_len + n], sh, sc, shp.ln_eps)
     return linear(h, m["final_out"])
 
 
-def denoise_step(z, txt, ids, m, shp, t_cur: float, t_next: float, guidance: float):
+def denoise_step(z, txt, ids, m, shp, t_cur: float, t_next: float, guidance: float, fp8: bool = False):
     """One flow-matching Euler step of the latent; returns (z_next, v). The
-    reference rows of an edit (the last shp.ref_len) are carried unchanged."""
-    v = velocity(z, txt, ids, m, shp, t_cur, guidance)
+    reference rows of an edit (the last shp.ref_len) are carried unchanged.
+    ``fp8`` as for ``velocity``."""
+    v = velocity(z, txt, ids, m, shp, t_cur, guidance, fp8=fp8)
     z_next = _f64(z).copy()
     n = shp.img_len - shp.ref_len
     z_next[:n] = euler(z[:n], v, t_cur, t_next)
@@ -438,10 +444,12 @@ def fp8_weights(w):
     """The fp8 form of a block's weights ("Architecture Deep Dive": fp8 on
     CDNA): every 16-bit weight matrix quantised per output channel exactly as
     activations are per token (``quantize_rows_fp8``); biases and norm scales
-    stay as they are. Nested dicts are mapped; layers already in fp8 form
-    (and int8 layers) pass through unchanged."""
+    stay as they are. Nested dicts and lists are mapped; layers already in
+    fp8 form (and int8 layers) pass through unchanged."""
     if isinstance(w, dict):
         return {k: fp8_weights(v) for k, v in w.items()}
+    if isinstance(w, list):
+        return [fp8_weights(v) for v in w]
     if getattr(w, "w", None) is None or not hasattr(w, "b"):
         return w
     codes, sc = quantize_rows_fp8(w.w)

@@ -198,15 +198,19 @@ def test_block_f16_weights_match_bf16(shape, kind):
 STEP = synth.custom_shape("step-h256-2d2s", 720, 256, 4, 1024, 64, (16, 16), n_double=2, n_single=2)
 
 
-@pytest.mark.parametrize("wt", ["bf16", "int8", "f16"])
+@pytest.mark.parametrize("wt", ["bf16", "int8", "f16", "fp8"])
 def test_denoise_step_tiny(wt):
+    """One denoise step of a 2 double + 2 single block model against the
+    oracle's step. fp8: the blocks' projections on fp8 weights and per-token
+    fp8 activations, the embedders, modulations and final layer on fp8
+    weights alone, against the oracle's fp8 step (same weight codes)."""
     say(f"denoise step tiny weights={wt}")
-    int8, f16 = wt == "int8", wt == "f16"
+    int8, f16, fp8 = wt == "int8", wt == "f16", wt == "fp8"
     shp = STEP
     m = synth.model_weights(shp, int8=int8)
     s = synth.step_inputs(shp)
-    A = DeviceArena(f16_weights=f16)
-    d = dims_for(shp, int8, f16)
+    A = DeviceArena(f16_weights=f16, fp8_weights=fp8)
+    d = dims_for(shp, int8, f16, fp8)
     mm = A.model(m)
     rope = _rope(A, d, shp)
     z = A.f32(s["z"])
@@ -216,7 +220,7 @@ def test_denoise_step_tiny(wt):
     B.check(B.mmdit_denoise_step(d, mm, z, txt, rope, t0, t1, 3.5, ws, ws.numel(), stream()), "step")
     sync()
     g = z.cpu().numpy()
-    z_ref, v_ref = O.denoise_step(s["z"], s["txt"], s["ids"], m, shp, t0, t1, 3.5)
+    z_ref, v_ref = O.denoise_step(s["z"], s["txt"], s["ids"], m, shp, t0, t1, 3.5, fp8=fp8)
     assert rel_err(g, z_ref) <= TOL
     v_gpu = (g.astype(np.float64) - s["z"]) / (t1 - t0)
     ev = rel_err(v_gpu, v_ref)
@@ -278,17 +282,18 @@ def _mod_oracle(m, shp, t, guidance):
     return np.concatenate(parts)
 
 
-@pytest.mark.parametrize("shape,wt", [(STEP, "f16"), (STEP, "int8"), (KLEIN_STEP, "bf16")])
+@pytest.mark.parametrize("shape,wt", [(STEP, "f16"), (STEP, "int8"), (KLEIN_STEP, "bf16"), (STEP, "fp8")])
 def test_modulation_batch_and_premod_steps(shape, wt):
     """All steps' modulation from one batched pass, then the premodulated
     step: the modulation rows against the oracle's, three steps against
-    three oracle steps, and a rerun bit for bit."""
+    three oracle steps, and a rerun bit for bit. fp8: the modulation on the
+    fp8 weights alone, the steps as the oracle's fp8 step."""
     say(f"modulation batch + premod steps {shape.name} weights={wt}")
-    int8, f16 = wt == "int8", wt == "f16"
+    int8, f16, fp8 = wt == "int8", wt == "f16", wt == "fp8"
     m = synth.model_weights(shape, int8=int8)
     s = synth.step_inputs(shape)
-    A = DeviceArena(f16_weights=f16)
-    d = dims_for(shape, int8, f16)
+    A = DeviceArena(f16_weights=f16, fp8_weights=fp8)
+    d = dims_for(shape, int8, f16, fp8)
     mm = A.model(m)
     rope = _rope(A, d, shape)
     n_steps = 3
@@ -300,8 +305,9 @@ def test_modulation_batch_and_premod_steps(shape, wt):
     B.check(B.mmdit_modulation_batch(d, mm, ts[:n_steps], g, mod, mws, mws.numel(), stream()), "modbatch")
     sync()
     got = mod.cpu().numpy()
+    m_mod = O.fp8_weights(m) if fp8 else m
     for i in range(n_steps):
-        ref = _mod_oracle(m, shape, ts[i], g)
+        ref = _mod_oracle(m_mod, shape, ts[i], g)
         e = rel_err(got[i], ref)
         say(f"  step {i}: modulation rel_err {e:.3e}")
         assert e <= 2e-3, e   # SiLU(vec) enters the matrix cores as fp16
@@ -320,7 +326,7 @@ def test_modulation_batch_and_premod_steps(shape, wt):
     g1 = run()
     z_ref = s["z"].astype(np.float64)
     for i in range(n_steps):
-        z_ref, _ = O.denoise_step(z_ref, s["txt"], s["ids"], m, shape, ts[i], ts[i + 1], g)
+        z_ref, _ = O.denoise_step(z_ref, s["txt"], s["ids"], m, shape, ts[i], ts[i + 1], g, fp8=fp8)
     e = rel_err(g1, z_ref)
     n = shape.img_len - shape.ref_len
     ev = rel_err(g1[:n] - s["z"][:n], z_ref[:n] - s["z"][:n])

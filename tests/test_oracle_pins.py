@@ -857,7 +857,7 @@ def test_step_closed_form_catches_planted_mistakes(monkeypatch):
     def cond_guidance_from_t(t, g, m):
         return good["conditioning"](t, t, m)
 
-    def velocity_wrong_rows(z, txt, ids, m, shp, t, g):
+    def velocity_wrong_rows(z, txt, ids, m, shp, t, g, fp8=False):
         vec = M.conditioning(t, g, m)
         x = np.concatenate([M._f64(txt), M.linear(z, m["img_in"])], axis=0)
         for wd in m["double"]:
@@ -868,7 +868,7 @@ def test_step_closed_form_catches_planted_mistakes(monkeypatch):
         h = M.ln_modulate(x[-shp.img_len:][::-1], sh, sc, shp.ln_eps)   # rows reversed
         return M.linear(h, m["final_out"])
 
-    def velocity_swapped_shift_scale(z, txt, ids, m, shp, t, g):
+    def velocity_swapped_shift_scale(z, txt, ids, m, shp, t, g, fp8=False):
         orig = M.modulation
 
         def swapped(vec, lin, chunks):
@@ -914,3 +914,44 @@ def test_step_closed_form_catches_planted_mistakes(monkeypatch):
     # and the unplanted oracle is back on the closed form
     gap, rms = _step_closed_form_gap()
     assert gap <= 1e-10 * max(rms, 1.0)
+
+
+def test_fp8_step_with_identity_blocks_is_the_step_on_decoded_weights():
+    """The fp8 denoise step (SGLang-AMD, Architecture Deep Dive: fp8 on CDNA):
+    with every block's gates zeroed the blocks return their input, and what
+    is left (embedders, patch embedding, modulations, final layer) runs on the
+    fp8 weights alone, so the step equals the plain step on the decoded
+    weights diag(s) e4m3(W / s). With the gates on, the blocks' per-token
+    activation quantisation moves v by a few percent of its RMS, not more."""
+    shp = synth.custom_shape("pin-fp8-step", 907, 128, 2, 256, 8, (4, 4), n_double=1, n_single=1, in_channels=16)
+    H = shp.hidden
+    s = synth.step_inputs(shp)
+    m = synth.model_weights(shp, int8=False)
+    exact = O.denoise_step(s["z"], s["txt"], s["ids"], m, shp, 0.9, 0.9 - 1 / 28, 3.5)[1]
+    q8 = O.denoise_step(s["z"], s["txt"], s["ids"], m, shp, 0.9, 0.9 - 1 / 28, 3.5, fp8=True)[1]
+    e = np.sqrt(np.mean((q8 - exact) ** 2)) / np.sqrt(np.mean(exact ** 2))
+    assert 1e-3 < e < 0.1, e
+    for wd in m["double"]:
+        for st in ("txt", "img"):
+            m_ = wd[st]["mod"]
+            for r0 in (2 * H, 5 * H):
+                m_.w[r0:r0 + H] = 0
+                m_.b[r0:r0 + H] = 0
+    for ws in m["single"]:
+        ws["mod"].w[2 * H:] = 0
+        ws["mod"].b[2 * H:] = 0
+
+    def decoded(o):
+        if isinstance(o, dict):
+            return {k: decoded(v) for k, v in o.items()}
+        if isinstance(o, list):
+            return [decoded(v) for v in o]
+        if isinstance(o, O.Fp8Linear):
+            return synth.Linear(np.asarray(o.s, np.float64)[:, None] * o.q, o.b)
+        return o
+    md = decoded(O.fp8_weights(m))
+    z8, v8 = O.denoise_step(s["z"], s["txt"], s["ids"], m, shp, 0.9, 0.9 - 1 / 28, 3.5, fp8=True)
+    z1, v1 = O.denoise_step(s["z"], s["txt"], s["ids"], md, shp, 0.9, 0.9 - 1 / 28, 3.5)
+    np.testing.assert_allclose(v8, v1, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(z8, z1, rtol=1e-12, atol=1e-12)
+    assert np.max(np.abs(md["img_in"].w - m["img_in"].w)) > 0      # the weights were quantised
