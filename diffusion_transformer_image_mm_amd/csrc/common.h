@@ -47,11 +47,21 @@ MMDIT_DEV uint32_t pack2h(float a, float b) {
 // fp16 bits -> fp32 (exact)
 MMDIT_DEV float h2f(uint16_t b) { return static_cast<float>(__builtin_bit_cast(_Float16, b)); }
 
-// Sum over all 64 lanes of a wavefront (butterfly; every lane gets the total).
+// Sum over all 64 lanes of a wavefront; every lane gets the total. Lane
+// exchanges without LDS round trips: DPP within each row of 16 lanes (swap
+// neighbours, swap pairs, mirror each half row, mirror the row: after each
+// step every lane holds the sum of a twice larger aligned group), then the
+// row swaps of gfx950 (permlane16 / permlane32) across rows. A fixed
+// sequence, so the result does not depend on timing.
 MMDIT_DEV float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0xB1, 0xF, 0xF, false));  // lane ^ 1
+    v += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x4E, 0xF, 0xF, false));  // lane ^ 2
+    v += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x141, 0xF, 0xF, false)); // half-row mirror
+    v += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x140, 0xF, 0xF, false)); // row mirror
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);   // rows 0+1, 2+3
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
 // Sum over aligned groups of G lanes (G a power of two <= 64).

@@ -52,24 +52,34 @@ __global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ x, 
             xs[i][4 * q] = v.x; xs[i][4 * q + 1] = v.y; xs[i][4 * q + 2] = v.z; xs[i][4 * q + 3] = v.w;
         }
     }
-    auto load = [&](int g, uint4 (&raw)[GEMV_RPW][NL]) {
+    // Loads from clamped, always valid addresses (a row past the end re-reads
+    // the last row and is not stored; columns past k meet act(x) = 0), so the
+    // loads are straight-line code. The row's bias, scale and (accumulating)
+    // previous output are loaded with its weights: a load issued later, in the
+    // reduction, would make the wait before it drain the next group's weight
+    // loads too (the counter of outstanding loads is in issue order).
+    struct RowExtra { float bias, scale, prev; };
+    auto load = [&](int g, uint4 (&raw)[GEMV_RPW][NL], RowExtra (&ex)[GEMV_RPW]) {
 #pragma unroll
         for (int rr = 0; rr < GEMV_RPW; ++rr) {
-            const int row = g * GEMV_RPW + rr;
+            int row = g * GEMV_RPW + rr;
+            row = row < rows ? row : rows - 1;
             const int s = row < n ? 0 : 1;
-            const char* wr = static_cast<const char*>(sets.s[s].w) + (size_t)(row - s * n) * k * ES;
+            const int r = row - s * n;
+            const char* wr = static_cast<const char*>(sets.s[s].w) + (size_t)r * k * ES;
 #pragma unroll
             for (int i = 0; i < NL; ++i) {
-                const int c = lane * E + i * 64 * E;
-                raw[rr][i] = make_uint4(0u, 0u, 0u, 0u);
-                if (row < rows && c < k) {
-                    const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wr + c * ES));
-                    raw[rr][i] = make_uint4(t.x, t.y, t.z, t.w);
-                }
+                int c = lane * E + i * 64 * E;
+                c = c < k ? c : 0;
+                const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wr + c * ES));
+                raw[rr][i] = make_uint4(t.x, t.y, t.z, t.w);
             }
+            ex[rr].bias = bf2f(sets.s[s].bias[r]);
+            ex[rr].scale = BYTE ? sets.s[s].scale[r] : 1.0f;
+            ex[rr].prev = accumulate ? sets.s[s].out[r] : 0.0f;
         }
     };
-    auto reduce = [&](int g, const uint4 (&raw)[GEMV_RPW][NL]) {
+    auto reduce = [&](int g, const uint4 (&raw)[GEMV_RPW][NL], const RowExtra (&ex)[GEMV_RPW]) {
 #pragma unroll
         for (int rr = 0; rr < GEMV_RPW; ++rr) {
             float acc = 0.f;
@@ -111,24 +121,27 @@ __global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ x, 
             const int row = g * GEMV_RPW + rr;
             if (lane == 0 && row < rows) {
                 const int s = row < n ? 0 : 1, r = row - s * n;
-                const GemvSet& st = sets.s[s];
-                const float y = (BYTE ? acc * st.scale[r] : acc) + bf2f(st.bias[r]);
-                st.out[r] = accumulate ? st.out[r] + y : y;
+                const float y = (BYTE ? acc * ex[rr].scale : acc) + ex[rr].bias;
+                sets.s[s].out[r] = accumulate ? ex[rr].prev + y : y;
             }
         }
     };
     // two register buffers in turn: the loads of group g + nw are in flight
     // while group g is reduced
+    // (A wave's last prefetch re-reads its current group when no next group
+    // is left: the loads stay unconditional, the re-read is never reduced.)
     uint4 ra[GEMV_RPW][NL], rb[GEMV_RPW][NL];
-    load(wv, ra);
+    RowExtra ea[GEMV_RPW], eb[GEMV_RPW];
+    load(wv, ra, ea);
     for (int g = wv; g < groups; g += 2 * nw) {
-        if (g + nw < groups) load(g + nw, rb);
-        reduce(g, ra);
+        load(g + nw < groups ? g + nw : g, rb, eb);
+        reduce(g, ra, ea);
         if (g + nw >= groups) break;
-        if (g + 2 * nw < groups) load(g + 2 * nw, ra);
-        reduce(g + nw, rb);
+        load(g + 2 * nw < groups ? g + 2 * nw : g + nw, ra, ea);
+        reduce(g + nw, rb, eb);
     }
 }
+
 
 hipError_t launch_gemv(const float* x, int k, int n, int wtype, int silu_input, int accumulate,
                        const GemvSets& sets, hipStream_t s) {
