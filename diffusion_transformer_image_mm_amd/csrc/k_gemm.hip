@@ -42,11 +42,12 @@
 //   16-byte chunk c of row r stored at position c ^ ((r >> 1) & 7), so the
 //   16 lanes that read one MFMA operand (16 rows, same chunk) hit 16
 //   distinct 16-byte bank groups;
-// * one barrier per k-step: all fragments of the current stage are read into
-//   registers before the next stage's loads are issued; for long
-//   contractions (K >= 8192, fp16 weights: the MLP-out and linear2
-//   projections) a half-stage register pipeline instead interleaves the
-//   fragment reads of one k-substep with the MFMAs of the other;
+// * one barrier per k-step: with bf16, int8 and fp8 weights all fragments of
+//   the current stage are read into registers before the next stage's loads
+//   are issued; with fp16 weights (the block's projections) a half-stage
+//   register pipeline instead interleaves the fragment reads of one
+//   k-substep with the MFMAs of the other (128-wide tail and head tiles keep
+//   the plain loop);
 // * grouped launch: up to two weight sets (text / image stream) over
 //   disjoint row ranges in one grid; tiles are laid out per XCD (tile_of);
 // * tail tiles: when the last round of 256-wide tiles would occupy at most
@@ -84,7 +85,6 @@ namespace mmdit {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;   // BN: the full tile; tail tiles are BN / 2 wide
-constexpr int PIPE_MIN_K = 8192;   // contractions at least this long use the pipelined loop
 constexpr int NTHREADS = 512;
 constexpr int A_TILE_BYTES = BM * BK * 2;   // 32 KB
 constexpr int W_TILE_BYTES_BF16 = BN * BK * 2;  // 32 KB
@@ -743,7 +743,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) 
             return;
         }
     }
-    if constexpr (!SWIGLU && PIPE == 0 && WT != MMDIT_FP8) {
+    if constexpr (!SWIGLU && WT != MMDIT_FP8) {
         if ((int)blockIdx.x >= nf) {
             gemm_tile<WT, EPI, 0, 2>(args, smem, blockIdx.x - nf, gridDim.x - nf, tmt - args.tail_rows,
                                      args.tail_rows);
@@ -823,16 +823,19 @@ static hipError_t launch_gemm_t(const GemmArgs& a0, hipStream_t s) {
     for (int g = 0; g < a.ngroups; ++g) tmt += (a.g[g].m + BM - 1) / BM;
     if (tmt == 0 || tn == 0) return hipSuccess;
     const bool swiglu = epi_base(a.epilogue) == MMDIT_EPI_SWIGLU || epi_base(a.epilogue) == MMDIT_EPI_SPLIT_SWIGLU;
-    // The pipelined loop pays off on long contractions (measured: +10% at
-    // K = 12288, +3% at K = 15360, -1% to 0 at K = 3072).
-    const bool pipe = WT == MMDIT_F16 && a.k >= PIPE_MIN_K;
+    // fp16 weights take the pipelined loop at every K (measured against the
+    // plain loop: +10% at K = 12288, +3% at K = 15360; at K = 3072 -1% to +1%
+    // alone, and the FLUX double block 1.351 -> 1.339 ms once the tail tiles
+    // (which keep the plain loop) run inside the pipelined kernels too,
+    // alternating processes on one box).
+    const bool pipe = WT == MMDIT_F16;
     // Tail tiles: when the last round of 256-wide tiles would fill at most
     // half of the compute units, and the last r row tiles can be cut off so
     // that the rest fills whole rounds, those r row tiles run as 128-wide
     // tiles instead (twice as many, each half as long).
     const int cus = cu_count();
     a.tail_rows = 0;
-    if (WT != MMDIT_FP8 && !swiglu && !pipe && (tmt * tn) % cus != 0 && (tmt * tn) % cus <= cus / 2) {
+    if (WT != MMDIT_FP8 && !swiglu && (tmt * tn) % cus != 0 && (tmt * tn) % cus <= cus / 2) {
         const int tn2 = (a.n + BN / 2 - 1) / (BN / 2);
         for (int r = 1; r < tmt; ++r) {
             if (((tmt - r) * tn) % cus == 0 && r * tn2 <= cus) {
