@@ -7,10 +7,14 @@
 // divide. The transformer's attention has no mask.
 //
 // gfx950 design:
-// * workgroup = 4 wavefronts x 32 query rows (128 rows of one head);
-//   key/value tiles of 64 keys; at most 256 registers per lane so that two
-//   workgroups share a CU (two wavefronts per SIMD: one wavefront per SIMD
-//   sustains only about half the LDS read rate these tiles need);
+// * workgroup = 8 wavefronts x 32 query rows (256 rows of one head), two
+//   wavefronts per SIMD (one wavefront per SIMD sustains only about half the
+//   LDS read rate these tiles need); key/value tiles of 64 keys, each staged
+//   in LDS once for all 256 rows: with 128-row workgroups (two per CU) every
+//   tile was staged twice per CU, and the LDS pipe, which carries the tile
+//   stores and ~125 B/clk of fragment reads, was the limit (FLUX double
+//   block 1.408 -> 1.379 ms, single block 1.309 -> 1.279 ms, alternating
+//   processes);
 // * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K from LDS as the first
 //   operand, Q^T from registers as the second), so each lane holds 32 scores
 //   of ONE query row: the row max needs one cross-lane exchange (lane ^ 32)
@@ -83,14 +87,14 @@ struct AttnTile {
     static constexpr int RB = D * 2;        // bytes per K row
     static constexpr int CPR = D / 8;       // 16-byte chunks per K row
     static constexpr int K_RPI = 64 / CPR;  // K rows per wavefront load
-    static constexpr int K_LPW = (KV / K_RPI) / 4;  // K loads per wavefront
-    static constexpr int V_LPW = (D / 8) / 4;       // V^T loads per wavefront (8 rows each)
+    static constexpr int K_LPW = (KV / K_RPI) / 8;  // K loads per wavefront
+    static constexpr int V_LPW = (D / 8) / 8;       // V^T loads per wavefront (8 rows each)
     static constexpr int K_BYTES = KV * RB;
     static constexpr int V_BYTES = D * KV * 2;
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(512, 1) void attention_kernel(const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ k,
                                                            const uint16_t* __restrict__ vt,
                                                            int seq_len, int l_pad, int heads,
@@ -106,14 +110,14 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
     // contiguous range of (head, query-tile) pairs, so that the keys and
     // values of a head are read through one XCD's L2 (2.4 MB per head at
     // 4608 tokens) instead of all eight.
-    const int nq = (seq_len + 127) / 128;
+    const int nq = (seq_len + 255) / 256;
     const int total = nq * heads;
     int bid = blockIdx.x;
     if (total % 8 == 0) bid = (bid % 8) * (total / 8) + bid / 8;
     const int h = bid / nq, qt = bid % nq;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 5, r32 = lane & 31;
-    const int qrow = qt * 128 + wave * 32 + r32;
+    const int qrow = qt * 256 + wave * 32 + r32;
 
     // ---- Q^T fragments (second MFMA operand): lane holds Q[qrow][ds*16 + 8g .. +7]
     const int qld = qrow < l_pad ? qrow : l_pad - 1;
@@ -302,7 +306,7 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
                             hipStream_t s) {
     if (seq_len <= 0) return hipSuccess;
     if (l_pad >= (1 << 24)) return hipErrorInvalidValue;   // 32-bit load offsets
-    dim3 grid(((seq_len + 127) / 128) * heads), block(256);
+    dim3 grid(((seq_len + 255) / 256) * heads), block(512);
     const float c_log2 = 1.4426950408889634f / sqrtf((float)head_dim);
     if (head_dim == 128)
         hipLaunchKernelGGL(attention_kernel<128>, grid, block, 0, s, q, k, vt, seq_len, l_pad, heads, out, ldo,
