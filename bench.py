@@ -277,8 +277,11 @@ def main() -> int:
 
     # ------------------------------------------------------------ dominant kernel: MLP-in GEMM
     L, H, M = shp.seq_len, shp.hidden, shp.mlp
-    a_in = A.empty_f16(L, H)
-    a_in.zero_()
+    # the activation operand holds LayerNorm-like values (N(0, 1), fp16): the
+    # matrix cores' power, and so the clock they run at, depends on the
+    # operands' bits (all-zero activations run this GEMM ~20% faster)
+    a_in = torch.randn(L, H, generator=torch.Generator(device="cuda").manual_seed(11), device="cuda").to(
+        torch.float16)
     a_out = A.empty_f16(L, M)
     g = B.mmdit_gemm(m=L, n=M, k=H, weight_dtype=B.MMDIT_F16, a=a_in.data_ptr(), lda=H,
                      w=w.img.fc1, epilogue=B.MMDIT_EPI_BIAS_GELU, out=a_out.data_ptr(), ldo=M)
