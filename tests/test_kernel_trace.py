@@ -9,9 +9,9 @@ import re
 from diffusion_transformer_image_mm_amd import kernel_trace as KT
 
 BLOCK = ["void mmdit::gemv_kernel<2, 6>(float const*)", "void mmdit::ln_modulate_kernel<3, 4, false>(float const*)",
-         "void mmdit::gemm_kernel<2, 64, 0>(mmdit::GemmArgs)", "void mmdit::attention_kernel<128>(unsigned short const*)",
-         "void mmdit::gemm_kernel<2, 2, 0>(mmdit::GemmArgs)", "void mmdit::ln_modulate_kernel<3, 4, false>(float const*)",
-         "void mmdit::gemm_kernel<2, 1, 0>(mmdit::GemmArgs)", "void mmdit::gemm_kernel<2, 2, 1>(mmdit::GemmArgs)"]
+         "void mmdit::gemm_kernel<2, 64, 1>(mmdit::GemmArgs)", "void mmdit::attention_kernel<128>(unsigned short const*)",
+         "void mmdit::gemm_kernel<2, 2, 1>(mmdit::GemmArgs)", "void mmdit::ln_modulate_kernel<3, 4, false>(float const*)",
+         "void mmdit::gemm_kernel<2, 1, 1>(mmdit::GemmArgs)", "void mmdit::gemm_kernel<2, 2, 1>(mmdit::GemmArgs)"]
 
 
 def _write(path, launches):
@@ -65,3 +65,30 @@ def test_blocks_with_another_sequence_are_left_out(tmp_path):
     _write(path, launches)
     text = KT.summarize(str(path))
     assert "median over 2 blocks" in text
+
+
+def test_counter_summary_of_synthetic_run(tmp_path):
+    """The hardware-counter summariser behind the committed counter profile:
+    medians per kernel, engine cycles per XCD (/8), matrix-core busy cycles
+    per SIMD (/1024) and the algorithmic cycles of the attention kernel."""
+    from diffusion_transformer_image_mm_amd import counters as C
+    path = tmp_path / "p_counter_collection.csv"
+    fields = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    alg = 4 * 4608 * 4608 * 3072 / 1024          # attention FLOPs / (1024 FLOP/clk) over the chip's SIMDs
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        for grbm in (8 * 500_000, 8 * 600_000, 8 * 550_000):
+            name = "void mmdit::attention_kernel<128>(unsigned short const*)"
+            w.writerow({"Kernel_Name": name, "Counter_Name": "GRBM_GUI_ACTIVE", "Counter_Value": grbm})
+            w.writerow({"Kernel_Name": name, "Counter_Name": "SQ_VALU_MFMA_BUSY_CYCLES", "Counter_Value": alg})
+            w.writerow({"Kernel_Name": name, "Counter_Name": "SQ_WAVE_CYCLES", "Counter_Value": 1000})
+            w.writerow({"Kernel_Name": name, "Counter_Name": "SQ_WAIT_INST_LDS", "Counter_Value": 50})
+    text = C.summarize(str(path))
+    line = next(l for l in text.splitlines() if l.startswith("mmdit::attention_kernel<128>"))
+    cells = line.split()
+    assert cells[1] == "3"                                     # dispatches
+    assert cells[2] == "550,000"                               # median GRBM / 8
+    assert cells[3] == cells[4] == f"{alg / 1024:,.0f}"        # busy = algorithmic per SIMD
+    assert cells[5] == f"{100 * (alg / 1024) / 550_000:.1f}%"
+    assert cells[7] == "5.0%"
