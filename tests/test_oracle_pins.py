@@ -955,3 +955,134 @@ def test_fp8_step_with_identity_blocks_is_the_step_on_decoded_weights():
     np.testing.assert_allclose(v8, v1, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(z8, z1, rtol=1e-12, atol=1e-12)
     assert np.max(np.abs(md["img_in"].w - m["img_in"].w)) > 0      # the weights were quantised
+
+
+# With a zero query projection (weights and bias) every query is the zero
+# vector after RMSNorm, every logit is 0 and attention is the plain mean of the
+# values over the whole joint sequence, whatever the keys and RoPE. The blocks
+# then have closed forms through their LayerNorm + modulation, value columns,
+# output projection and gates (Luminal blog, "What the compiler found on its
+# own": LN then a scale and a shift; joint attention over the concatenated
+# streams; a gate-and-residual add after each branch).
+def _double_value_path_gap():
+    """max |oracle - closed form| of the double block with uniform attention,
+    and the size of the branch."""
+    import torch.nn.functional as F
+    d = synth.block_inputs(TINY, "double", variant=6)
+    H, Lt = TINY.hidden, TINY.txt_len
+    w = d["w"]
+    for s in ("txt", "img"):
+        qkv = w[s]["qkv"]
+        wq, bq = qkv.w.copy(), qkv.b.copy()
+        wq[:H] = 0
+        bq[:H] = 0
+        w[s]["qkv"] = synth.Linear(wq, bq)
+        w[s]["mod"] = _scaled(w[s]["mod"], 10.0)
+        w[s]["mod"].w[5 * H:] = 0
+        w[s]["mod"].b[5 * H:] = 0
+        w[s]["proj"] = _scaled(w[s]["proj"], 25.0)
+    out = O.double_block(d["x"], d["vec"], d["ids"], w, TINY)
+    sv = F.silu(_t(d["vec"]))
+    x = _t(d["x"])
+    mods, vs = {}, []
+    for s, sl in (("txt", slice(0, Lt)), ("img", slice(Lt, None))):
+        m = _lin_t(sv, w[s]["mod"])
+        mods[s] = m
+        h = F.layer_norm(x[sl], (H,), eps=TINY.ln_eps) * (1 + m[H:2 * H]) + m[:H]
+        vs.append(_lin_t(h, w[s]["qkv"])[:, 2 * H:])
+    o = torch_cat(vs).mean(dim=0)
+    want = np.empty_like(out)
+    for s, sl in (("txt", slice(0, Lt)), ("img", slice(Lt, None))):
+        m = mods[s]
+        want[sl] = (x[sl] + m[2 * H:3 * H] * _lin_t(o, w[s]["proj"])).numpy()
+    return float(np.max(np.abs(out - want))), float(np.max(np.abs(want - d["x"])))
+
+
+def _single_uniform_gap():
+    import torch.nn.functional as F
+    d = synth.block_inputs(TINY, "single", variant=6)
+    H = TINY.hidden
+    w = d["w"]
+    l1 = w["linear1"]
+    w1, b1 = l1.w.copy() * 25.0, l1.b.copy() * 25.0
+    w1[:H] = 0
+    b1[:H] = 0
+    w["linear1"] = synth.Linear(w1, b1)
+    w["mod"] = _scaled(w["mod"], 10.0)
+    w["linear2"] = _scaled(w["linear2"], 25.0)
+    out = O.single_block(d["x"], d["vec"], d["ids"], w, TINY)
+    m = _lin_t(F.silu(_t(d["vec"])), w["mod"])
+    x = _t(d["x"])
+    h = F.layer_norm(x, (H,), eps=TINY.ln_eps) * (1 + m[H:2 * H]) + m[:H]
+    u = _lin_t(h, w["linear1"])
+    o = u[:, 2 * H:3 * H].mean(dim=0, keepdim=True).expand(x.shape[0], H)
+    cat = torch_cat([o, F.gelu(u[:, 3 * H:], approximate="tanh")], dim=1)
+    want = (x + m[2 * H:3 * H] * _lin_t(cat, w["linear2"])).numpy()
+    return float(np.max(np.abs(out - want))), float(np.max(np.abs(want - d["x"])))
+
+
+def test_double_block_value_path_closed_form():
+    """LN1 with shift1/scale1 per stream, the v columns of the qkv projection,
+    attention over both streams jointly, the out-projection and gate1
+    (MLP gate zeroed): x + gate1 (W_o mean_j v_j + b_o)."""
+    gap, size = _double_value_path_gap()
+    assert size > 0.05                      # the branch is not negligible
+    assert gap <= 1e-10 * max(size, 1.0), gap
+
+
+def test_single_block_closed_form_with_uniform_attention():
+    """The single block with a zero query projection: LN with (shift, scale),
+    linear1's v and MLP columns, attention as the mean of v, GELU on the MLP
+    columns, linear2 over [attention | GELU(mlp)] and the gate."""
+    gap, size = _single_uniform_gap()
+    assert size > 0.05
+    assert gap <= 1e-10 * max(size, 1.0), gap
+
+
+def test_block_closed_forms_catch_planted_mistakes(monkeypatch):
+    """Plausible mistakes planted in the oracle's blocks move them far from
+    the closed forms above: shift and scale swapped in the LayerNorm
+    modulation, attention restricted to each token's own stream, the
+    single block's linear2 input order swapped."""
+    from oracle import mmdit_oracle as M
+    ln_orig, att_orig, act_orig = M.ln_modulate, M.attention, M.mlp_activation
+
+    def ln_swapped(x, shift, scale, eps):
+        return ln_orig(x, scale, shift, eps)
+
+    def att_per_stream(q, k, v, heads, rows=None):
+        Lt = TINY.txt_len
+        r = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+        out = np.empty((len(r), q.shape[1]))
+        for sl in (slice(0, Lt), slice(Lt, None)):
+            idx = np.arange(q.shape[0])[sl]
+            sel = np.isin(r, idx)
+            out[sel] = att_orig(q[sl], k[sl], v[sl], heads, rows=r[sel] - idx[0])
+        return out
+    for name, fn, which in (("ln_modulate", ln_swapped, "both"), ("attention", att_per_stream, "double")):
+        with monkeypatch.context() as mp:
+            mp.setattr(M, name, fn)
+            for gapf in ([_double_value_path_gap, _single_uniform_gap] if which == "both"
+                         else [_double_value_path_gap]):
+                gap, size = gapf()
+                assert gap > 1e-3 * size, (name, gapf.__name__, gap, size)
+    # the single block's [attention | GELU(mlp)] input read in the other order
+    src = M.single_block
+
+    def single_swapped(x, vec, ids, w, shp, **kw):
+        H = shp.hidden
+        w2 = dict(w)
+        lw = w["linear2"].w
+        w2["linear2"] = synth.Linear(np.concatenate([lw[:, H:2 * H], lw[:, :H], lw[:, 2 * H:]], axis=1),
+                                     w["linear2"].b)
+        return src(x, vec, ids, w2, shp, **kw)
+    with monkeypatch.context() as mp:
+        mp.setattr(M, "single_block", single_swapped)
+        mp.setattr(O, "single_block", single_swapped)
+        gap, size = _single_uniform_gap()
+        assert gap > 1e-3 * size, gap
+
+
+def torch_cat(ts, dim=0):
+    import torch
+    return torch.cat(ts, dim=dim)
