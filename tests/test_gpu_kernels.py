@@ -46,6 +46,33 @@ def test_ln_modulate(rows, hidden, split):
     assert within_one_ulp(g, ref, "f16") <= 1.0  # one rounding of an fp32 result
 
 
+def test_ln_modulate_fp16_range_overflows_to_inf():
+    """The projections' activation operands are fp16 (range +-65504): a
+    LayerNorm output pushed past it by a huge modulation scale is stored as
+    +-inf (IEEE round to nearest: |y| >= 65520), not clamped, so the overflow
+    shows downstream as a non-finite result. Values inside the range stay
+    within one fp16 step of the oracle."""
+    say("ln_modulate fp16 range")
+    rows, hidden = 8, 256
+    A = DeviceArena()
+    x = rnd(1, (rows, hidden))
+    sh = np.zeros((2, hidden))
+    sc = np.zeros((2, hidden))
+    sc[:, :32] = 1e5                       # (1 + scale) * LN(x): up to ~3e5 in these columns
+    dx, dsh, dsc = A.f32(x), A.f32(sh), A.f32(sc)
+    out = A.empty_f16(rows, hidden)
+    B.check(B.mmdit_k_ln_modulate(dx, rows, hidden, rows, dsh[0], dsc[0], dsh[1], dsc[1], 1e-6, out, stream()))
+    sync()
+    g = to_numpy_f32(out)
+    ref = O.ln_modulate(x, sh[0], sc[0], 1e-6)
+    over = np.abs(ref) >= 65520.0 * (1 + 1e-6)
+    under = np.abs(ref) <= 65504.0 * (1 - 1e-6)
+    assert over.sum() > 10 and under.sum() > 0
+    assert np.all(np.isinf(g[over])) and np.all(np.sign(g[over]) == np.sign(ref[over]))
+    assert np.all(np.isfinite(g[under]))
+    assert within_one_ulp(g[under], ref[under], "f16") <= 1.0
+
+
 # ------------------------------------------------------------------ RoPE table
 @pytest.mark.parametrize("shape", [synth.TINY, synth.QWEN_DOUBLE])
 def test_rope_table(shape):
