@@ -7,12 +7,12 @@
 //
 // The output is the activation operand of the next projection, stored as
 // fp16 (10-bit significand; LayerNorm outputs are O(10), far inside fp16's
-// range). HBM-bound: each row is read once (4 B/elem), written once (2 B/elem).
+// range; a value beyond +-65504 is stored as +-inf, the IEEE conversion).
+// HBM-bound: each row is read once (4 B/elem), written once (2 B/elem).
 // A row is held in registers by one, two or four wavefronts (up to four float4
 // per lane), so the two-pass mean/variance costs no second HBM read. Wide rows
-// (FLUX's 3072) take a whole workgroup per row: 4608 short workgroups keep more
-// loads in flight per CU than one row per wavefront. 128-bit loads, 64-bit
-// stores, butterfly reductions within the wavefront.
+// (FLUX's 3072) take a whole workgroup per row. 128-bit loads, 64-bit stores,
+// DPP reductions within the wavefront.
 #include "common.h"
 
 namespace mmdit {
