@@ -463,3 +463,71 @@ def linear_act_fp8(x, lin) -> np.ndarray:
     weights."""
     codes, sc = quantize_rows_fp8(np.asarray(x, dtype=np.float64))
     return linear_fp8(codes, sc, lin.q, lin.s, lin.b)
+
+
+# --------------------------------------------------------------------------
+# fp8 attention (SGLang-AMD, "Architecture Deep Dive": fp8 on CDNA; the
+# fp8 path runs the attention products on fp8 operands as well)
+# --------------------------------------------------------------------------
+def qk_fp8_exponent(norm_scales, head_dim: int) -> int:
+    """Exponent e of the power-of-two per-tensor scale 2^e of the fp8
+    queries (or keys). After RMSNorm a row's mean square is below 1, so its
+    2-norm is below sqrt(D); the norm scale g multiplies each element by at
+    most max|g|, and RoPE rotates pairs without changing the norm. Every
+    element therefore satisfies |x_d| <= sqrt(D) max|g|, and e is the
+    smallest integer with 2^e >= b, b = fl32(fl32(sqrt(D) / 448) * max|g|)
+    over all the given norm-scale vectors (both streams of a double block):
+    no code can exceed 448."""
+    gmax = np.float32(max(float(np.max(np.abs(_f64(g)))) for g in norm_scales))
+    f = np.float32(math.sqrt(head_dim) / E4M3_MAX)
+    b = float(np.float32(f * gmax))
+    m, e = math.frexp(b)            # b = m 2^e, 0.5 <= m < 1 (m = 0 for b = 0)
+    return e - 1 if m == 0.5 else e
+
+
+def quantize_pow2_fp8(x, e: int) -> np.ndarray:
+    """e4m3 code values of x at the scale 2^e: e4m3(x 2^-e), the scaling exact
+    (x taken as fp32, the precision the kernels hold it in before this)."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    return e4m3_round(x * 2.0 ** (-e))
+
+
+def quantize_cols_fp8(v):
+    """Per-channel fp8 quantisation of v [L, C]: one scale per column,
+    max over the column's rows of |v| / 448, codes e4m3(v / scale) (both in
+    fp32, as ``quantize_rows_fp8`` on v^T). Returns (codes [L, C], scales [C])."""
+    codes, sc = quantize_rows_fp8(np.asarray(v, dtype=np.float64).T)
+    return codes.T, sc
+
+
+def attention_fp8(q, k, v, heads: int, eq: int, ek: int,
+                  rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Multi-head attention of the fp8 path over [L, heads*D] tensors:
+      * q and k as e4m3 codes at the per-tensor scales 2^eq and 2^ek
+        (``quantize_pow2_fp8``), v as e4m3 codes with one fp32 scale per
+        channel (``quantize_cols_fp8``);
+      * logits in log2 units t_ij = (q8_i . k8_j) 2^(eq+ek) log2(e) / sqrt(D);
+      * the exponentials p_ij = 2^(t_ij - M_i + 8), M_i the smallest integer
+        >= max_j t_ij, so p lies in [0, 256]; the probabilities enter the
+        second product as their e4m3 code values P8 = e4m3(p);
+      * O_i = sum_j P8_ij v8_j diag(sv) / sum_j p_ij, the row sum over the
+        unquantised exponentials.
+    Reading: the pages name fp8 only as a capability of the stack; the integer
+    reference M_i makes the codes independent of which integer at or above
+    the maximum a tiled evaluation uses (scaling by a power of two commutes
+    with e4m3 rounding in its normal range)."""
+    SITE_COUNTS["attention"] += 1
+    qc, kc = quantize_pow2_fp8(q, eq), quantize_pow2_fp8(k, ek)
+    vc, sv = quantize_cols_fp8(v)
+    L, HD = kc.shape
+    D = HD // heads
+    r = np.arange(qc.shape[0]) if rows is None else np.asarray(rows)
+    c = math.log2(math.e) / math.sqrt(D) * 2.0 ** (eq + ek)
+    out = np.empty((len(r), HD), dtype=np.float64)
+    for h in range(heads):
+        sl = slice(h * D, (h + 1) * D)
+        t = (qc[r, sl] @ kc[:, sl].T) * c
+        M = np.ceil(t.max(axis=1, keepdims=True))
+        p = np.exp2(t - M + 8.0)
+        out[:, sl] = (e4m3_round(p) @ (vc[:, sl] * _f64(sv[sl])[None, :])) / p.sum(axis=1, keepdims=True)
+    return out

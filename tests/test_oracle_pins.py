@@ -1086,3 +1086,210 @@ def test_block_closed_forms_catch_planted_mistakes(monkeypatch):
 def torch_cat(ts, dim=0):
     import torch
     return torch.cat(ts, dim=dim)
+
+
+# ---------------------------------------------------------------- fp8 attention
+def _e4m3_nearest(x: float) -> float:
+    """Nearest finite e4m3 value by a search over the code table, ties to the
+    even code (independent of the oracle's arithmetic rounding)."""
+    best = None
+    for c in range(127):                 # 0x00 .. 0x7e: the non-negative finite codes
+        v = _e4m3_decode(c)
+        d = abs(abs(x) - v)
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, c, v)
+    return math.copysign(best[2], x)
+
+
+def _rms_rows(x, heads):
+    """Rows normalised to unit mean square per head (what RMSNorm with g = 1
+    hands to the attention)."""
+    L = x.shape[0]
+    y = x.reshape(L, heads, -1)
+    return (y / np.sqrt((y ** 2).mean(-1, keepdims=True))).reshape(L, -1)
+
+
+def _attention_fp8_brute(q, k, v, heads, eq, ek, rows):
+    """Scalar loops, math.ceil / 2.0 ** / math.fsum and the table rounding."""
+    f32 = np.float32
+    L, HD = k.shape
+    D = HD // heads
+    qc = {(i, j): _e4m3_nearest(float(f32(q[i, j])) * 2.0 ** -eq) for i in rows for j in range(HD)}
+    kc = [[_e4m3_nearest(float(f32(k[i, j])) * 2.0 ** -ek) for j in range(HD)] for i in range(L)]
+    sv, vc = [], [[0.0] * HD for _ in range(L)]
+    for j in range(HD):
+        amax = max(abs(f32(v[i, j])) for i in range(L))
+        s = f32(f32(amax) / f32(448.0))
+        sv.append(float(s))
+        for i in range(L):
+            vc[i][j] = _e4m3_nearest(float(f32(f32(v[i, j]) / s))) if s > 0 else 0.0
+    out = np.zeros((len(rows), HD))
+    for h in range(heads):
+        for n, i in enumerate(rows):
+            t = [math.fsum(qc[i, h * D + d] * kc[j][h * D + d] for d in range(D))
+                 * 2.0 ** (eq + ek) * math.log2(math.e) / math.sqrt(D) for j in range(L)]
+            M = math.ceil(max(t))
+            p = [2.0 ** (tj - M + 8) for tj in t]
+            den = math.fsum(p)
+            for d in range(D):
+                col = h * D + d
+                out[n, col] = math.fsum(_e4m3_nearest(p[j]) * vc[j][col] * sv[col] for j in range(L)) / den
+    return out
+
+
+def test_attention_fp8_brute_force_tiny():
+    """attention_fp8 against scalar loops on a tiny case (SGLang-AMD,
+    Architecture Deep Dive: fp8 on CDNA): codes of q and k at power-of-two
+    scales, per-channel v codes (an all-zero channel gets scale 0 and zero
+    output), logits in log2 units, exponentials against the integer ceiling
+    of the row maximum, their e4m3 codes in the value product and their exact
+    sum in the denominator; a row subset equals the same rows of the whole."""
+    g = np.random.default_rng(71)
+    L, heads, D = 9, 2, 8
+    q = _rms_rows(g.standard_normal((L, heads * D)), heads) * 1.3
+    k = _rms_rows(g.standard_normal((L, heads * D)), heads) * 0.7
+    v = g.standard_normal((L, heads * D))
+    v[:, 5] = 0.0
+    eq = O.qk_fp8_exponent([np.full(D, 1.3)], D)
+    ek = O.qk_fp8_exponent([np.full(D, 0.7)], D)
+    rows = [0, 3, 8]
+    got = O.attention_fp8(q, k, v, heads, eq, ek)
+    np.testing.assert_allclose(got[rows], _attention_fp8_brute(q, k, v, heads, eq, ek, rows), rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(O.attention_fp8(q, k, v, heads, eq, ek, rows=np.array(rows)), got[rows])
+    assert np.all(got[:, 5] == 0.0)
+
+
+def _fp8_exact_channels(L, C, g):
+    """v whose every channel is e4m3 values times a power of two, with the top
+    code in each channel: per-channel quantisation is the identity on it."""
+    vals = np.array(sorted({_e4m3_decode(c) for c in range(256) if not math.isnan(_e4m3_decode(c))}))
+    v = g.choice(vals, size=(L, C))
+    v[g.integers(0, L, size=C), np.arange(C)] = 448.0
+    return v * np.exp2(g.integers(-9, -3, size=(1, C)))
+
+
+def test_attention_fp8_zero_queries_give_the_mean_of_the_values():
+    """q = 0: every logit is 0, M = 0, every exponential is exactly 256 (an
+    e4m3 value), so the output is the plain mean of the values over the keys
+    when v is fp8-exact per channel."""
+    g = np.random.default_rng(72)
+    L, heads, D = 37, 3, 64
+    v = _fp8_exact_channels(L, heads * D, g)
+    k = _rms_rows(g.standard_normal((L, heads * D)), heads)
+    out = O.attention_fp8(np.zeros((L, heads * D)), k, v, heads, -3, -3)
+    np.testing.assert_allclose(out, np.tile(v.mean(axis=0), (L, 1)), rtol=1e-14, atol=0)
+
+
+def test_attention_fp8_single_key_closed_form():
+    """L = 1: t = c q.k, M = ceil(t), p = 2^(8 + t - M) in (128, 256], whose
+    e4m3 code lies on the grid of step 16 there; the output is v * code / p.
+    The integer reference and the exact denominator are what set the factor."""
+    heads, D = 1, 64
+    g = np.random.default_rng(73)
+    for trial in range(20):
+        q = g.choice([-1.0, -0.5, 0.5, 1.0, 2.0], size=(1, D)) * 2.0 ** -3
+        k = g.choice([-1.0, 0.5, 1.0, 1.5], size=(1, D)) * 2.0 ** -2
+        v = _fp8_exact_channels(1, D, g)
+        t = float(np.dot(q[0], k[0])) * math.log2(math.e) / math.sqrt(D)
+        p = 2.0 ** (8 + t - math.ceil(t))
+        code = round(p / 16.0) * 16.0 if abs(p / 16.0 - math.floor(p / 16.0) - 0.5) > 1e-12 else None
+        if code is None:
+            continue
+        want = v * code / p
+        np.testing.assert_allclose(O.attention_fp8(q, k, v, heads, -3, -2), want, rtol=1e-13)
+
+
+def test_attention_fp8_invariances_and_distance_from_exact_attention():
+    """Doubling one value channel doubles that output channel exactly (its
+    scale doubles, its codes stay); permuting the keys with their values
+    leaves the output unchanged; the result stays within the fp8 noise of the
+    exact attention (each operand rounded to 3 mantissa bits: a few percent
+    of the output RMS here) and is not the exact attention."""
+    g = np.random.default_rng(74)
+    L, heads, D = 96, 2, 64
+    q = _rms_rows(g.standard_normal((L, heads * D)), heads)
+    k = _rms_rows(g.standard_normal((L, heads * D)), heads)
+    v = g.standard_normal((L, heads * D))
+    e = O.qk_fp8_exponent([np.ones(D)], D)
+    base = O.attention_fp8(q, k, v, heads, e, e)
+    v2 = v.copy(); v2[:, 17] *= 2.0
+    o2 = O.attention_fp8(q, k, v2, heads, e, e)
+    np.testing.assert_array_equal(o2[:, 17], 2.0 * base[:, 17])
+    np.testing.assert_array_equal(np.delete(o2, 17, axis=1), np.delete(base, 17, axis=1))
+    perm = g.permutation(L)
+    np.testing.assert_allclose(O.attention_fp8(q, k[perm], v[perm], heads, e, e), base, rtol=1e-12, atol=1e-14)
+    exact = O.attention(q, k, v, heads)
+    rms = np.sqrt((exact ** 2).mean())
+    err = np.sqrt(((base - exact) ** 2).mean()) / rms
+    assert 5e-3 < err < 0.1, err
+
+
+def test_qk_fp8_exponent_is_the_smallest_safe_power_of_two():
+    """After RMSNorm and a norm scale g, even a row with all its energy in one
+    element (|x_d| = sqrt(D) |g_d|) quantises within 448 at 2^e, and 2^(e-1)
+    would not be safe for the bound; both streams' scales are covered."""
+    g = np.random.default_rng(75)
+    for D in (64, 128):
+        for trial in range(6):
+            ga = (g.uniform(0.2, 3.0, D) * g.choice([-1, 1], D)).astype(np.float32)
+            gb = (g.uniform(0.2, 3.0, D)).astype(np.float32)
+            e = O.qk_fp8_exponent([ga, gb], D)
+            gmax = max(np.max(np.abs(ga)), np.max(np.abs(gb)))
+            bound = float(np.float32(np.float32(math.sqrt(D) / 448.0) * np.float32(gmax)))
+            assert 2.0 ** (e - 1) < bound <= 2.0 ** e
+            d = int(np.argmax(np.abs(np.concatenate([ga, gb]))) % D)
+            gsel = ga if np.max(np.abs(ga)) >= np.max(np.abs(gb)) else gb
+            x = np.zeros((1, D)); x[0, d] = math.sqrt(D) * float(gsel[d])
+            codes = O.quantize_pow2_fp8(x, e)
+            assert np.max(np.abs(codes)) <= 448.0
+    assert O.qk_fp8_exponent([np.full(64, 0.5)], 64) == -6       # 8 * 0.5 / 448 = 2^-6.807...
+    assert O.qk_fp8_exponent([np.full(16, 112.0)], 16) == 0      # 4 * 112 / 448 = 1 exactly
+
+
+def test_attention_fp8_pins_catch_planted_mistakes():
+    """Mistaken versions of the fp8 attention (floor for the integer ceiling,
+    the exact maximum as reference, quantised exponentials in the
+    denominator, one scale for all value channels, the scale exponent's sign
+    flipped) each fail one of the closed forms above."""
+    def make(mut):
+        def att(q, k, v, heads, eq, ek, rows=None):
+            if mut == "sign":     # codes taken at 2^-e instead of 2^e
+                qc = O.quantize_pow2_fp8(q, -eq) if abs(eq) < 4 else O.quantize_pow2_fp8(q * 0, 0)
+                kc = O.quantize_pow2_fp8(k, -ek) if abs(ek) < 4 else O.quantize_pow2_fp8(k * 0, 0)
+            else:
+                qc, kc = O.quantize_pow2_fp8(q, eq), O.quantize_pow2_fp8(k, ek)
+            if mut == "tensor_v":
+                s = np.float32(np.max(np.abs(v)) / 448.0)
+                vc, sv = O.e4m3_round(np.asarray(v, np.float32) / s), np.full(v.shape[1], s)
+            else:
+                vc, sv = O.quantize_cols_fp8(v)
+            L, HD = kc.shape
+            D = HD // heads
+            r = np.arange(qc.shape[0]) if rows is None else np.asarray(rows)
+            c = math.log2(math.e) / math.sqrt(D) * 2.0 ** (eq + ek)
+            out = np.empty((len(r), HD))
+            for h in range(heads):
+                sl = slice(h * D, (h + 1) * D)
+                t = (qc[r, sl] @ kc[:, sl].T) * c
+                M = {"floor": np.floor, "exact": lambda a: a}.get(mut, np.ceil)(t.max(axis=1, keepdims=True))
+                p = np.exp2(t - M + 8.0)
+                p8 = O.e4m3_round(np.minimum(p, 448.0))
+                den = p8.sum(axis=1, keepdims=True) if mut == "den" else p.sum(axis=1, keepdims=True)
+                out[:, sl] = (p8 @ (vc[:, sl] * sv[sl][None, :])) / den
+            return out
+        return att
+
+    def fails(fn):
+        try:
+            with pytest.MonkeyPatch.context() as mp:
+                mp.setattr(O, "attention_fp8", fn)
+                for t in (test_attention_fp8_zero_queries_give_the_mean_of_the_values,
+                          test_attention_fp8_single_key_closed_form,
+                          test_attention_fp8_brute_force_tiny):
+                    t()
+        except AssertionError:
+            return True
+        return False
+    assert not fails(O.attention_fp8)
+    for mut in ("floor", "exact", "den", "tensor_v", "sign"):
+        assert fails(make(mut)), mut
