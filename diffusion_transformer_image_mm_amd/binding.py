@@ -131,6 +131,9 @@ _SIGS = {
     "mmdit_k_qknorm_rope": (c_int, [_P, c_int, c_int, c_int, c_int, c_int, _P, _P, _P, _P, _P, c_float,
                                     c_int, _P, _P, _P, _P]),
     "mmdit_k_attention": (c_int, [_P, _P, _P, c_int, c_int, c_int, c_int, _P, c_int, _P]),
+    "mmdit_k_quantize_attention_fp8": (c_int, [_P, _P, _P, c_int, c_int, c_int, _P, _P, _P, _P, _P, _P, _P, _P,
+                                               _P, _P]),
+    "mmdit_k_attention_fp8": (c_int, [_P, _P, _P, _P, _P, c_int, c_int, c_int, c_int, _P, c_int, _P]),
     "mmdit_k_gemm": (c_int, [POINTER(mmdit_gemm), _P]),
     "mmdit_k_gemv": (c_int, [_P, c_int, POINTER(mmdit_linear), c_int, c_int, c_int, c_int, _P, _P]),
     "mmdit_k_time_embed": (c_int, [POINTER(mmdit_dims), POINTER(mmdit_model), c_float, c_float, _P, _P,
@@ -246,6 +249,18 @@ def mmdit_k_qknorm_rope(qkv, ld, seq_len, heads, head_dim, split, qn0, kn0, qn1,
 def mmdit_k_attention(q, k, vt, heads, seq_len, head_dim, l_pad, out, ldo, stream=None) -> int:
     return lib.mmdit_k_attention(ptr(q), ptr(k), ptr(vt), heads, seq_len, head_dim, l_pad, ptr(out), ldo,
                                  stream_handle(stream))
+
+
+def mmdit_k_quantize_attention_fp8(q, k, vt, heads, head_dim, l_pad, q_norm0, q_norm1, k_norm0, k_norm1,
+                                   q8, k8, vt8, v_scale, exps, stream=None) -> int:
+    return lib.mmdit_k_quantize_attention_fp8(ptr(q), ptr(k), ptr(vt), heads, head_dim, l_pad, ptr(q_norm0),
+                                              ptr(q_norm1), ptr(k_norm0), ptr(k_norm1), ptr(q8), ptr(k8), ptr(vt8),
+                                              ptr(v_scale), ptr(exps), stream_handle(stream))
+
+
+def mmdit_k_attention_fp8(q8, k8, vt8, v_scale, exps, heads, seq_len, head_dim, l_pad, out, ldo, stream=None) -> int:
+    return lib.mmdit_k_attention_fp8(ptr(q8), ptr(k8), ptr(vt8), ptr(v_scale), ptr(exps), heads, seq_len, head_dim,
+                                     l_pad, ptr(out), ldo, stream_handle(stream))
 
 
 def mmdit_k_gemm(g: mmdit_gemm, stream=None) -> int:

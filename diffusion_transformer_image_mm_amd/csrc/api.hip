@@ -816,6 +816,33 @@ int mmdit_k_attention(const mmdit_bf16* q, const mmdit_bf16* k, const mmdit_bf16
     return MMDIT_OK;
 }
 
+int mmdit_k_quantize_attention_fp8(const mmdit_bf16* q, const mmdit_bf16* k, const mmdit_bf16* vt, int heads,
+                                   int head_dim, int l_pad, const mmdit_bf16* q_norm0, const mmdit_bf16* q_norm1,
+                                   const mmdit_bf16* k_norm0, const mmdit_bf16* k_norm1, uint8_t* q8, uint8_t* k8,
+                                   uint8_t* vt8, float* v_scale, int32_t* exps, hipStream_t s) {
+    if (head_dim != 64 && head_dim != 128) return MMDIT_E_SHAPE;
+    if (heads < 1 || l_pad < 64 || l_pad % 64 != 0 || l_pad >= (1 << 24)) return MMDIT_E_SHAPE;
+    for (const void* p : {(const void*)q, (const void*)k, (const void*)vt, (const void*)q_norm0, (const void*)k_norm0,
+                          (const void*)q8, (const void*)k8, (const void*)vt8, (const void*)v_scale, (const void*)exps})
+        MMDIT_TRY(check_ptr(p));
+    MMDIT_HIP(launch_quantize_attention_fp8(q, k, vt, heads, head_dim, l_pad, q_norm0, q_norm1, k_norm0, k_norm1, q8,
+                                            k8, vt8, v_scale, exps, s));
+    return MMDIT_OK;
+}
+
+int mmdit_k_attention_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* vt8, const float* v_scale,
+                          const int32_t* exps, int heads, int seq, int head_dim, int l_pad, mmdit_f16* out, int ldo,
+                          hipStream_t s) {
+    if (head_dim != 64 && head_dim != 128) return MMDIT_E_SHAPE;
+    if (seq < 1 || heads < 1 || l_pad < seq || l_pad % 64 != 0 || l_pad >= (1 << 24)) return MMDIT_E_SHAPE;
+    if (ldo < heads * head_dim || ldo % 8 != 0) return MMDIT_E_SHAPE;
+    for (const void* p : {(const void*)q8, (const void*)k8, (const void*)vt8, (const void*)v_scale, (const void*)exps,
+                          (const void*)out})
+        MMDIT_TRY(check_ptr(p));
+    MMDIT_HIP(launch_attention_fp8(q8, k8, vt8, v_scale, exps, heads, seq, head_dim, l_pad, out, ldo, s));
+    return MMDIT_OK;
+}
+
 int mmdit_k_gemm(const mmdit_gemm* g, hipStream_t s) {
     if (!g) return MMDIT_E_NULL;
     if (g->m < 1 || g->n < 64 || g->n % 64 != 0 || g->k < 64 || g->k % 64 != 0) return MMDIT_E_SHAPE;

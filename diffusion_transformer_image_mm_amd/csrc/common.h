@@ -222,6 +222,15 @@ hipError_t launch_quantize_fp8_rows(const uint16_t* x, bool x_bf16, int rows, in
                                     uint8_t* codes, int ldc, float* scales, hipStream_t s);
 
 // y fp16 = SiLU(x fp32), n elements
+// fp8 attention (k_attention_fp8.hip): q, k, v^T to e4m3 (exps[0..1] = eq, ek),
+// then the attention on the codes
+hipError_t launch_quantize_attention_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int heads,
+                                         int head_dim, int l_pad, const uint16_t* gq0, const uint16_t* gq1,
+                                         const uint16_t* gk0, const uint16_t* gk1, uint8_t* q8, uint8_t* k8,
+                                         uint8_t* vt8, float* sv, int* exps, hipStream_t s);
+hipError_t launch_attention_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* vt8, const float* sv,
+                                const int* exps, int heads, int seq_len, int head_dim, int l_pad, uint16_t* out,
+                                int ldo, hipStream_t s);
 hipError_t launch_silu_to_f16(const float* x, uint16_t* y, int64_t n, hipStream_t s);
 
 }  // namespace mmdit

@@ -17,8 +17,9 @@
 //   processes);
 // * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K from LDS as the first
 //   operand, Q^T from registers as the second), so each lane holds 32 scores
-//   of ONE query row: the row max needs one cross-lane exchange (lane ^ 32)
-//   and the row sum none until the end;
+//   of ONE query row: the row max needs one exchange between the wavefront's
+//   halves (lane ^ 32, a register swap, no LDS round trip) and the row sum
+//   none until the end;
 // * online softmax in fp32 with exp2: scores are scaled by log2(e)/sqrt(D)
 //   in one multiply-subtract; O is rescaled only by the lane's own factor,
 //   and only on tiles where some row's maximum grew by more than 2^8;
@@ -229,7 +230,10 @@ __global__ __launch_bounds__(512, 1) void attention_kernel(const uint16_t* __res
         for (int st = 0; st < 2; ++st)
 #pragma unroll
             for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[st][i]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+            tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
         // Lazy rescaling: the running max only moves when a row's new max
         // exceeds it by more than 8 (log2 units). O / l does not depend on
         // which reference max is used; a stale one bounds P by 2^8.

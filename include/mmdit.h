@@ -409,6 +409,49 @@ int mmdit_k_attention(const mmdit_bf16* q, const mmdit_bf16* k, const mmdit_bf16
                       int heads, int seq_len, int head_dim, int l_pad,
                       mmdit_f16* out, int ldo, hipStream_t stream);
 
+/*
+ * fp8 attention (SGLang-AMD, "Architecture Deep Dive": fp8 quantisation on
+ * the CDNA stack; the attention products of the Luminal blog's "What the
+ * compiler found on its own" on the fp8 matrix cores). Two calls:
+ *
+ * mmdit_k_quantize_attention_fp8: q, k (bf16 [heads, l_pad, D]) and vt (bf16
+ *   [heads, D, l_pad], the order mmdit_k_qknorm_rope writes) to OCP e4m3:
+ *   - q and k at one power-of-two scale per tensor, 2^eq and 2^ek: e is the
+ *     smallest integer with 2^e >= fl32(fl32(sqrt(D)/448) * max|g|), max over
+ *     the RMSNorm scales q_norm0/q_norm1 (k_norm0/k_norm1; the second of each
+ *     may be NULL, as for a single-stream block). After RMSNorm and RoPE
+ *     every element is at most sqrt(D) max|g| in magnitude, so no code
+ *     overflows; inputs that are not RMS-normalised with these scales may
+ *     exceed 448 and are outside this contract.
+ *     q8, k8: codes [heads, l_pad, D] (1 byte each); exps: int32[2] = (eq, ek).
+ *   - vt with one fp32 scale per channel (row of vt): v_scale[h*D + d] =
+ *     max over the row of |v| / 448, code = e4m3(v / scale) (both in fp32;
+ *     0 for an all-zero row). vt8: codes [heads, D, l_pad] with the keys of
+ *     each 64-key tile in the order of the fp8 kernel's operand slots: slot
+ *     32g + 16s + 4a + b holds key 32s + 8a + 4g + b (g, s < 2; a, b < 4).
+ *   Rounding to nearest even throughout; the caller owns every buffer.
+ *
+ * mmdit_k_attention_fp8: O = softmax attention on those codes:
+ *   logits in log2 units t = (q8 . k8) 2^(eq+ek) log2(e) / sqrt(D); the
+ *   exponentials p = 2^(t - M + 8) with M the smallest integer at or above
+ *   the row's maximum t, so p lies in [0, 256]; the value product takes the
+ *   e4m3 codes of p, the row sum the fp32 p:
+ *   O[i, h*D + d] = v_scale[h*D + d] * sum_j e4m3(p_ij) v8[j, d] / sum_j p_ij.
+ *   (The kernel tracks M tile by tile; M being an integer makes the codes the
+ *   same as against the final M up to exact powers of two.) out: fp16
+ *   [seq_len, ldo]. Shapes as for mmdit_k_attention.
+ */
+int mmdit_k_quantize_attention_fp8(const mmdit_bf16* q, const mmdit_bf16* k, const mmdit_bf16* vt,
+                                   int heads, int head_dim, int l_pad,
+                                   const mmdit_bf16* q_norm0, const mmdit_bf16* q_norm1,
+                                   const mmdit_bf16* k_norm0, const mmdit_bf16* k_norm1,
+                                   uint8_t* q8, uint8_t* k8, uint8_t* vt8, float* v_scale,
+                                   int32_t* exps, hipStream_t stream);
+int mmdit_k_attention_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* vt8,
+                          const float* v_scale, const int32_t* exps,
+                          int heads, int seq_len, int head_dim, int l_pad,
+                          mmdit_f16* out, int ldo, hipStream_t stream);
+
 /* GEMM epilogues (bias is always added first: y = acc * s + b, s = 1 for bf16) */
 enum mmdit_epilogue {
     MMDIT_EPI_BIAS = 0,       /* out bf16 [m, ldo] = y (q, k, v for attention) */
