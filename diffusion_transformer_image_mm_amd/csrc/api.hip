@@ -142,6 +142,12 @@ struct DoubleWs {
     float* sh;       // [L]
     float* so;       // [L]
     float* sa;       // [L]
+    // fp8 attention operands: q, k, v^T codes, per-channel v scales, exponents
+    uint8_t* q8;     // [heads, l_pad, D]
+    uint8_t* k8;
+    uint8_t* vt8;    // [heads, D, l_pad]
+    float* sv;       // [H]
+    int* exps;       // [2]
 };
 
 DoubleWs carve_double(const mmdit_dims* d, Carver& c) {
@@ -164,6 +170,15 @@ DoubleWs carve_double(const mmdit_dims* d, Carver& c) {
         w.sh = c.take<float>(L);
         w.so = c.take<float>(L);
         w.sa = c.take<float>(L);
+        w.q8 = c.take<uint8_t>(LP * H);
+        w.k8 = c.take<uint8_t>(LP * H);
+        w.vt8 = c.take<uint8_t>(LP * H);
+        w.sv = c.take<float>(H);
+        w.exps = c.take<int>(2);
+    } else {
+        w.q8 = w.k8 = w.vt8 = nullptr;
+        w.sv = nullptr;
+        w.exps = nullptr;
     }
     return w;
 }
@@ -180,6 +195,11 @@ struct SingleWs {
     uint8_t* cat8;
     float* sh;
     float* sc;
+    uint8_t* q8;     // fp8 attention operands, as in the double block
+    uint8_t* k8;
+    uint8_t* vt8;
+    float* sv;
+    int* exps;
 };
 
 SingleWs carve_single(const mmdit_dims* d, Carver& c) {
@@ -199,6 +219,15 @@ SingleWs carve_single(const mmdit_dims* d, Carver& c) {
         w.cat8 = c.take<uint8_t>(L * (H + M));
         w.sh = c.take<float>(L);
         w.sc = c.take<float>(L);
+        w.q8 = c.take<uint8_t>(LP * H);
+        w.k8 = c.take<uint8_t>(LP * H);
+        w.vt8 = c.take<uint8_t>(LP * H);
+        w.sv = c.take<float>(H);
+        w.exps = c.take<int>(2);
+    } else {
+        w.q8 = w.k8 = w.vt8 = nullptr;
+        w.sv = nullptr;
+        w.exps = nullptr;
     }
     return w;
 }
@@ -367,8 +396,18 @@ int run_double(const mmdit_dims* d, const mmdit_double_weights* w, const float* 
                                      w->txt.q_norm, w->txt.k_norm, w->img.q_norm, w->img.k_norm, rope,
                                      d->rms_eps, LP, ws.q, ws.k, ws.vt, s));
     }
-    // a5: joint attention
-    MMDIT_HIP(launch_attention(ws.q, ws.k, ws.vt, d->heads, L, d->head_dim, LP, ws.o, H, s));
+    // a5: joint attention (fp8 blocks: on e4m3 q, k, v^T, the q/k scales
+    // bounded by both streams' norm scales)
+    if (fp8) {
+        const uint16_t* qn1 = w->img.q_norm ? w->img.q_norm : w->txt.q_norm;
+        const uint16_t* kn1 = w->img.k_norm ? w->img.k_norm : w->txt.k_norm;
+        MMDIT_HIP(launch_quantize_attention_fp8(ws.q, ws.k, ws.vt, d->heads, d->head_dim, LP, w->txt.q_norm, qn1,
+                                                w->txt.k_norm, kn1, ws.q8, ws.k8, ws.vt8, ws.sv, ws.exps, s));
+        MMDIT_HIP(launch_attention_fp8(ws.q8, ws.k8, ws.vt8, ws.sv, ws.exps, d->heads, L, d->head_dim, LP, ws.o, H,
+                                       s));
+    } else {
+        MMDIT_HIP(launch_attention(ws.q, ws.k, ws.vt, d->heads, L, d->head_dim, LP, ws.o, H, s));
+    }
     // a6: out projection + gated residual
     if (fp8) MMDIT_HIP(quant_rows(ws.o, L, H, ws.o8, ws.so, s));
     {
@@ -437,7 +476,14 @@ int run_single(const mmdit_dims* d, const mmdit_single_weights* w, const float* 
             MMDIT_HIP(launch_qknorm_rope(ws.qkv, 3 * H, L, d->heads, d->head_dim, L, w->q_norm, w->k_norm,
                                          w->q_norm, w->k_norm, rope, d->rms_eps, LP, ws.q, ws.k, ws.vt, s));
     }
-    MMDIT_HIP(launch_attention(ws.q, ws.k, ws.vt, d->heads, L, d->head_dim, LP, ws.cat, H + M, s));
+    if (fp8) {
+        MMDIT_HIP(launch_quantize_attention_fp8(ws.q, ws.k, ws.vt, d->heads, d->head_dim, LP, w->q_norm, nullptr,
+                                                w->k_norm, nullptr, ws.q8, ws.k8, ws.vt8, ws.sv, ws.exps, s));
+        MMDIT_HIP(launch_attention_fp8(ws.q8, ws.k8, ws.vt8, ws.sv, ws.exps, d->heads, L, d->head_dim, LP, ws.cat,
+                                       H + M, s));
+    } else {
+        MMDIT_HIP(launch_attention(ws.q, ws.k, ws.vt, d->heads, L, d->head_dim, LP, ws.cat, H + M, s));
+    }
     if (fp8) MMDIT_HIP(quant_rows(ws.cat, L, H + M, ws.cat8, ws.sc, s));
     {
         GemmArgs g = proj_base(d, H, H + M, ws.cat, ws.cat8, ws.sc, MMDIT_EPI_GATE_RESID, x_out, H);

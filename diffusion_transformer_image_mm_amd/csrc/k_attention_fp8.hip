@@ -322,11 +322,18 @@ __global__ __launch_bounds__(256) void quantize_qk_fp8_kernel(const uint16_t* __
         const uint4 a = src[0], b = src[1];
         const uint32_t wv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
         uint32_t pk[4];
+        // |x| 2^-e <= 448 by the RMSNorm bound; the clamp only keeps a value
+        // that its own bf16 rounding pushed just past 448 (below 464, where
+        // rounding to nearest gives 448 anyway) out of the conversion's
+        // overflow range
+        auto c448 = [](float x) { return fminf(fmaxf(x, -448.0f), 448.0f); };
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const uint32_t w0 = wv[2 * u], w1 = wv[2 * u + 1];
-            uint32_t p = __builtin_amdgcn_cvt_pk_fp8_f32(bf2f(w0 & 0xffffu) * sc, bf2f(w0 >> 16) * sc, 0u, false);
-            pk[u] = __builtin_amdgcn_cvt_pk_fp8_f32(bf2f(w1 & 0xffffu) * sc, bf2f(w1 >> 16) * sc, p, true);
+            uint32_t p = __builtin_amdgcn_cvt_pk_fp8_f32(c448(bf2f(w0 & 0xffffu) * sc), c448(bf2f(w0 >> 16) * sc),
+                                                         0u, false);
+            pk[u] = __builtin_amdgcn_cvt_pk_fp8_f32(c448(bf2f(w1 & 0xffffu) * sc), c448(bf2f(w1 >> 16) * sc), p,
+                                                    true);
         }
         reinterpret_cast<uint4*>(isq ? q8 : k8)[j] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
     }

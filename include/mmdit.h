@@ -102,8 +102,12 @@ enum mmdit_weight_dtype {
                        come from mmdit_quantize_fp8_rows. The block entries
                        accept it for GELU MLPs: every projection's activation
                        operand is quantised per token right before its GEMM
-                       (LayerNorm outputs, attention output, GELU hidden);
-                       attention and the residual stream are unchanged. The
+                       (LayerNorm outputs, attention output, GELU hidden), and
+                       the attention runs on e4m3 q, k, v and probabilities
+                       (mmdit_k_quantize_attention_fp8 and
+                       mmdit_k_attention_fp8, with the q/k scales bounded by
+                       the block's q/k norm scales); the residual stream is
+                       unchanged. The
                        step entries accept it too: the blocks as above; the
                        embedders, modulations, patch embedding and final
                        projection keep 16-bit (fp32 for the GEMVs)

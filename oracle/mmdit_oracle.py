@@ -242,7 +242,9 @@ def double_block(x, vec, ids, w, shp, rows: Optional[np.ndarray] = None,
     With ``rows`` only those output rows are returned (all keys and values
     are still computed). With ``fp8`` every linear takes its fp8 form
     (``fp8_weights``, ``linear_act_fp8``): projections on per-token fp8
-    activations, the modulation on the fp8 weights alone.
+    activations, the modulation on the fp8 weights alone; the attention is
+    ``attention_fp8`` with the power-of-two scales the two streams' q and k
+    norm scales bound (``qk_fp8_exponent``).
     """
     H, heads, L_t = shp.hidden, shp.heads, shp.txt_len
     lin = linear_act_fp8 if fp8 else linear
@@ -269,7 +271,13 @@ def double_block(x, vec, ids, w, shp, rows: Optional[np.ndarray] = None,
         k[sl] = norm_rope_heads(k[sl], w[s]["k_norm"], phi[sl], heads, shp.rms_eps)
     stages["q"], stages["k"], stages["v"] = q, k, v
     out_rows = np.arange(L) if rows is None else np.asarray(rows)
-    o = attention(q, k, v, heads, out_rows)
+    if fp8:
+        D = H // heads
+        eq = qk_fp8_exponent([w["txt"]["q_norm"], w["img"]["q_norm"]], D)
+        ek = qk_fp8_exponent([w["txt"]["k_norm"], w["img"]["k_norm"]], D)
+        o = attention_fp8(q, k, v, heads, eq, ek, out_rows)
+    else:
+        o = attention(q, k, v, heads, out_rows)
     stages["attn"] = o
     xo = x[out_rows].copy()
     is_txt = out_rows < L_t
@@ -311,7 +319,12 @@ def single_block(x, vec, ids, w, shp, rows: Optional[np.ndarray] = None,
     q = norm_rope_heads(q, w["q_norm"], phi, heads, shp.rms_eps)
     k = norm_rope_heads(k, w["k_norm"], phi, heads, shp.rms_eps)
     out_rows = np.arange(L) if rows is None else np.asarray(rows)
-    o = attention(q, k, v, heads, out_rows)
+    if fp8:
+        D = H // heads
+        o = attention_fp8(q, k, v, heads, qk_fp8_exponent([w["q_norm"]], D),
+                          qk_fp8_exponent([w["k_norm"]], D), out_rows)
+    else:
+        o = attention(q, k, v, heads, out_rows)
     cat = np.concatenate([o, mlp_activation(m[out_rows], shp.mlp_act)], axis=1)
     xo = x[out_rows] + g * lin(cat, w["linear2"])
     if return_stages:

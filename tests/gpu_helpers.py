@@ -86,3 +86,41 @@ def sync():
 
 def stream():
     return torch.cuda.current_stream()
+
+
+# The fp8 matrix cores do not sum exactly: products far below the largest one
+# of a dot product lose their low bits (measured on the GPU with exact e4m3
+# operands: up to 2.4e-4 of the largest product, exact when all products share
+# an exponent). With sharp attention a logit moved that much flips the e4m3
+# code of a dominant probability by a whole step (6-12% of it).
+MFMA_F8_SUM_ERR = 2.5e-4
+
+
+def attention_fp8_perturbed(q, k, v, heads, eq, ek, rows=None, rng=None, bf16_inputs=True):
+    """The oracle's fp8 attention (oracle.attention_fp8, SGLang-AMD
+    "Architecture Deep Dive": fp8 on CDNA) with the two perturbations the HIP
+    path applies to it: q, k, v stored in bf16 ahead of the quantiser, and
+    every logit moved uniformly within the fp8 matrix cores' summation error.
+    Built from the oracle's own quantisers; how far it lands from the plain
+    oracle is the method's sensitivity to that arithmetic."""
+    import math
+    import oracle as O
+    from diffusion_transformer_image_mm_amd import synth
+    rng = rng or np.random.default_rng(0)
+    if bf16_inputs:
+        q, k, v = (synth.bf16_exact(np.asarray(a, np.float32)).astype(np.float64) for a in (q, k, v))
+    qc, kc = O.quantize_pow2_fp8(q, eq), O.quantize_pow2_fp8(k, ek)
+    vc, sv = O.quantize_cols_fp8(v)
+    L, HD = kc.shape
+    D = HD // heads
+    r = np.arange(qc.shape[0]) if rows is None else np.asarray(rows)
+    c = math.log2(math.e) / math.sqrt(D) * 2.0 ** (eq + ek)
+    out = np.empty((len(r), HD))
+    for h in range(heads):
+        sl = slice(h * D, (h + 1) * D)
+        qs, ks = qc[r, sl], kc[:, sl]
+        big = np.abs(qs[:, None, :].astype(np.float32) * ks[None, :, :].astype(np.float32)).max(-1)
+        t = (qs @ ks.T + rng.uniform(-1.0, 1.0, big.shape) * MFMA_F8_SUM_ERR * big) * c
+        pp = np.exp2(t - np.ceil(t.max(axis=1, keepdims=True)) + 8.0)
+        out[:, sl] = (O.e4m3_round(pp) @ (vc[:, sl] * sv[sl][None, :])) / pp.sum(axis=1, keepdims=True)
+    return out

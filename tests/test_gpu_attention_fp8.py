@@ -14,7 +14,8 @@ import torch
 import oracle as O
 from diffusion_transformer_image_mm_amd import binding as B
 from diffusion_transformer_image_mm_amd import synth
-from gpu_helpers import TOL, DeviceArena, rel_err_rounded_out, say, stream, sync, to_numpy_f32, vt_layout
+from gpu_helpers import (TOL, DeviceArena, attention_fp8_perturbed, rel_err_rounded_out, say, stream, sync,
+                         to_numpy_f32, vt_layout)
 
 pytestmark = pytest.mark.gpu
 CID = 720
@@ -57,38 +58,16 @@ def _normed(tid, heads, L, D, g):
     return synth.bf16_exact((x * g[None, None, :]).astype(np.float32))
 
 
-# The fp8 matrix cores do not sum exactly: products far below the largest one
-# of a dot product lose their low bits (measured on the GPU with exact e4m3
-# operands: up to 2.4e-4 of the largest product, exact when all products share
-# an exponent). With sharp attention a logit moved that much flips the e4m3
-# code of a dominant probability by a whole step (6-12% of it).
-MFMA_F8_SUM_ERR = 2.5e-4
-
-
 def _fp8_sensitivity(qf, kf, vf, heads, eq, ek, rows, draws=3, seed=0):
     """How far the oracle's fp8 attention moves (max |diff| / RMS) when each
-    logit is perturbed uniformly within the matrix cores' summation error:
-    an implementation that sums like the hardware is one more such draw."""
+    logit is perturbed within the matrix cores' summation error
+    (gpu_helpers.attention_fp8_perturbed; the inputs are bf16 already): an
+    implementation that sums like the hardware is one more such draw."""
     g = np.random.default_rng(seed)
-    qc, kc = O.quantize_pow2_fp8(qf, eq), O.quantize_pow2_fp8(kf, ek)
-    vc, sv = O.quantize_cols_fp8(vf)
-    L, HD = kc.shape
-    D = HD // heads
-    c = math.log2(math.e) / math.sqrt(D) * 2.0 ** (eq + ek)
     base = O.attention_fp8(qf, kf, vf, heads, eq, ek, rows=rows)
     rms = np.sqrt((base ** 2).mean())
-    worst = 0.0
-    for _ in range(draws):
-        out = np.empty_like(base)
-        for h in range(heads):
-            sl = slice(h * D, (h + 1) * D)
-            qs, ks = qc[rows, sl], kc[:, sl]
-            big = np.abs(qs[:, None, :].astype(np.float32) * ks[None, :, :].astype(np.float32)).max(-1)
-            t = (qs @ ks.T + g.uniform(-1.0, 1.0, big.shape) * MFMA_F8_SUM_ERR * big) * c
-            pp = np.exp2(t - np.ceil(t.max(axis=1, keepdims=True)) + 8.0)
-            out[:, sl] = (O.e4m3_round(pp) @ (vc[:, sl] * sv[sl][None, :])) / pp.sum(axis=1, keepdims=True)
-        worst = max(worst, float(np.abs(out - base).max() / rms))
-    return worst
+    return max(float(np.abs(attention_fp8_perturbed(qf, kf, vf, heads, eq, ek, rows, g, bf16_inputs=False)
+                            - base).max() / rms) for _ in range(draws))
 
 
 def _case(D, heads, L, gq=(1.0, 1.0), gk=(1.0, 1.0), tid=10, rows=None, q=None, k=None, check_codes=True,

@@ -7,7 +7,7 @@ import pytest
 import oracle as O
 from diffusion_transformer_image_mm_amd import binding as B
 from diffusion_transformer_image_mm_amd import synth
-from gpu_helpers import TOL, DeviceArena, rel_err, say, stream, sync
+from gpu_helpers import TOL, DeviceArena, attention_fp8_perturbed, rel_err, say, stream, sync
 from sharp_inputs import sharp_block_inputs, update_rms_err
 from diffusion_transformer_image_mm_amd.device import dims_for
 
@@ -127,8 +127,10 @@ def test_block_sharp_attention_update_formats(kind, wt):
     weights: the attention-layout epilogue applies each format's scales
     before the norm (the channel scale of int8; row and channel scales of
     fp8, whose oracle quantises the same operands). Bars: 2e-2 of the
-    update's RMS for the 16-bit formats, 3e-2 for fp8 (as for the fp8 blocks,
-    whose codes can sit one step apart near rounding boundaries)."""
+    update's RMS for the 16-bit formats; for fp8 3e-2, or twice the oracle's
+    own movement under the path's arithmetic where that is larger (sharp
+    attention puts dominant keys' e4m3 probability codes near rounding
+    boundaries, which the fp8 matrix cores' summation error can cross)."""
     say(f"block sharp attention {kind} {RAGGED_D128.name} weights={wt}")
     int8 = wt == "int8"
     inp = sharp_block_inputs(RAGGED_D128, kind, int8=int8)
@@ -136,7 +138,16 @@ def test_block_sharp_attention_update_formats(kind, wt):
     ref = oracle_block(inp, fp8=wt == "fp8")
     e_rms = update_rms_err(g, ref, inp["x"])
     say(f"  update: rms err / rms = {e_rms:.3e}")
-    assert e_rms <= (FP8_UPDATE_RMS if wt == "fp8" else SHARP_TOL), e_rms
+    bar = SHARP_TOL
+    if wt == "fp8":
+        # sharp attention makes the fp8 attention's probability codes flip
+        # under the path's arithmetic: the bar is also twice the oracle's own
+        # movement under it (two draws), as for the FLUX-size fp8 blocks
+        sens = max(update_rms_err(_oracle_fp8_with_path_storage(inp, None, seed=s_), ref, inp["x"])
+                   for s_ in (0, 1))
+        bar = max(FP8_UPDATE_RMS, 2.0 * sens)
+        say(f"  oracle's own movement under the path's arithmetic: update RMS {sens:.3e}")
+    assert e_rms <= bar, (e_rms, bar)
 
 
 @pytest.mark.parametrize("kind", ["double", "single"])
@@ -430,28 +441,28 @@ def test_block_fp8_rerun_bit_exact():
     np.testing.assert_array_equal(a, b)
 
 
-def _oracle_fp8_with_path_storage(inp, rows):
-    """The oracle's fp8 block with the 16-bit storage of the HIP path applied
-    to its own intermediates: every projection's activation rounded to fp16
-    before it is quantised, and q, k, v rounded to bf16 before attention.
-    This is the same method on inputs moved by one 16-bit rounding; how far
-    it lands from the unrounded oracle is the method's own sensitivity to
-    that storage (the planted roundings live in this test, not in the
-    oracle)."""
+def _oracle_fp8_with_path_storage(inp, rows, seed=0):
+    """The oracle's fp8 block with the HIP path's arithmetic applied to its
+    own intermediates: every projection's activation rounded to fp16 before
+    it is quantised, q, k, v rounded to bf16 before the fp8 attention, and
+    the attention logits moved within the fp8 matrix cores' summation error
+    (gpu_helpers.attention_fp8_perturbed). This is the same method on inputs
+    moved by one rounding; how far it lands from the plain oracle is the
+    method's own sensitivity to that arithmetic (the planted roundings live
+    in this test, not in the oracle)."""
     from oracle import mmdit_oracle as M
-    lin_orig, att_orig = M.linear_act_fp8, M.attention
+    lin_orig, att_orig = M.linear_act_fp8, M.attention_fp8
+    g = np.random.default_rng(seed)
 
     def f16(a):
         return np.asarray(a, np.float64).astype(np.float16).astype(np.float64)
-
-    def bf16(a):
-        return synth.bf16_exact(np.asarray(a, np.float32)).astype(np.float64)
     try:
         M.linear_act_fp8 = lambda x, lin: lin_orig(f16(x), lin)
-        M.attention = lambda q, k, v, heads, rows=None: att_orig(bf16(q), bf16(k), bf16(v), heads, rows)
+        M.attention_fp8 = lambda q, k, v, heads, eq, ek, rows=None: attention_fp8_perturbed(q, k, v, heads, eq, ek,
+                                                                                            rows, g)
         return oracle_block(inp, rows=rows, fp8=True)
     finally:
-        M.linear_act_fp8, M.attention = lin_orig, att_orig
+        M.linear_act_fp8, M.attention_fp8 = lin_orig, att_orig
 
 
 @pytest.mark.parametrize("shape,kind", [(synth.FLUX_DOUBLE, "double"), (synth.FLUX_SINGLE, "single")])
