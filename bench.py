@@ -88,6 +88,7 @@ def roofline_kernels(shp, A, w, stream, log) -> list:
     """The block's bandwidth-bound kernels against the HBM peak (algorithmic
     bytes: compulsory reads + writes) and attention against the MFMA peak,
     each timed alone through its per-kernel entry at the FLUX block's shapes."""
+    import numpy as np
     import torch
 
     from diffusion_transformer_image_mm_amd import binding as B
@@ -96,15 +97,15 @@ def roofline_kernels(shp, A, w, stream, log) -> list:
     lp = (L + 127) // 128 * 128
     out = []
 
-    def line(kernel, bound, work, ms, unit_note):
+    def line(kernel, bound, work, ms, unit_note, peak=PEAK_BF16_TFLOPS):
         if bound == "hbm":
             ach = work / (ms * 1e-3) / 1e9
             e = {"kernel": kernel, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                  "frac": round(ach / PEAK_HBM_GBS, 4), "bytes_per_launch": int(work)}
         else:
             ach = work / (ms * 1e-3) / 1e12
-            e = {"kernel": kernel, "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-                 "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "flops_per_launch": work}
+            e = {"kernel": kernel, "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
+                 "unit": "TFLOP/s", "frac": round(ach / peak, 4), "flops_per_launch": work}
         e["avg_us"] = round(ms * 1e3, 2)
         e["note"] = unit_note
         log(f"bench: {kernel}: {e['achieved']} {e['unit']} ({100 * e['frac']:.1f}% of peak), {e['avg_us']} us")
@@ -146,7 +147,22 @@ def roofline_kernels(shp, A, w, stream, log) -> list:
                         stream)
     line("attention_kernel (joint attention, 24 heads x 4608 x 128)", "mfma", 4.0 * L * L * H, ms,
          "4 L^2 H (QK^T and PV)")
-    del x, h, qkv, q, k, vt, o
+    # the fp8 path's attention: its operand quantiser, then the kernel on e4m3 codes
+    q8 = A._hold(torch.empty(heads, lp, D, dtype=torch.uint8, device="cuda"))
+    k8 = A._hold(torch.empty(heads, lp, D, dtype=torch.uint8, device="cuda"))
+    vt8 = A._hold(torch.empty(heads, D, lp, dtype=torch.uint8, device="cuda"))
+    sv = A.empty_f32(H)
+    exps = A.i32(np.zeros(2))
+    ms = _time_launches(lambda: B.check(B.mmdit_k_quantize_attention_fp8(q, k, vt, heads, D, lp, gq, gq, gq, gq, q8, k8,
+                                                                         vt8, sv, exps, stream), "quant8"), stream)
+    line("quantize_qk_fp8 + quantize_vt_fp8 (fp8 attention operands, 24 heads x 4608 x 128)", "hbm",
+         3 * heads * lp * D * (2 + 1), ms,
+         "read q, k, v^T bf16 + write their e4m3 codes (v^T's second read, after its row maximum, hits L2)")
+    ms = _time_launches(lambda: B.check(B.mmdit_k_attention_fp8(q8, k8, vt8, sv, exps, heads, L, D, lp, o, H, stream),
+                                        "attn8"), stream)
+    line("attention_fp8_kernel (joint attention on e4m3 q, k, v, P; 24 heads x 4608 x 128)", "mfma",
+         4.0 * L * L * H, ms, "4 L^2 H on the fp8 matrix cores (dense fp8 peak)", peak=PEAK_FP8_TFLOPS)
+    del x, h, qkv, q, k, vt, o, q8, k8, vt8
     torch.cuda.empty_cache()
     return out
 
@@ -372,7 +388,7 @@ def main() -> int:
                             "frac": round(tf8 / PEAK_FP8_TFLOPS, 4), "avg_us": round(ms_g8 * 1e3, 2),
                             "activation_quantisation_us": round(ms_q8 * 1e3, 2)},
         "fp8_double_block": {"weights": "e4m3 per output channel; activations e4m3 per token before each "
-                                        "projection (quantiser launches included)",
+                                        "projection; attention on e4m3 q, k, v, P (quantiser launches included)",
                              "ms": round(ms_block_fp8, 4), "ms_p90": round(float(np.percentile(per8, 90)), 4),
                              "effective_tflops": round(flops / (ms_block_fp8 * 1e-3) / 1e12, 2),
                              "speedup_vs_fp16_operands": round(ms_block / ms_block_fp8, 3)},
