@@ -94,6 +94,90 @@ struct AttnTile {
     static constexpr int V_BYTES = D * KV * 2;
 };
 
+// One 64-key tile of the online softmax for the lane's query row (lane (r32, g)
+// of a wavefront owning 32 query rows): S^T = K Q^T, the lazily rescaled
+// exponentials, O^T += V^T P^T. K and V^T of tile t are in LDS (sK, sV).
+template <int D>
+MMDIT_DEV void attn_tile(int t, int seq_len, int g, const char* sK, const char* sV, const int (&k_off)[2][D / 16],
+                         const int (&v_off)[D / 32][4], const bf16x8_t (&qf)[D / 16], f32x16_t (&o)[D / 32],
+                         float& m_run, float& l_run, float c_log2) {
+    using T = AttnTile<D>;
+    // S^T = K Q^T for the two 32-key halves of the tile
+    f32x16_t s[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
+#pragma unroll
+        for (int ds = 0; ds < D / 16; ++ds) {
+            const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(sK + k_off[st][ds]);
+            s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s[st], 0, 0, 0);
+        }
+    }
+    if constexpr (D == 128) read_ahead_schedule();
+    // the first V^T fragments, read now so that the PV phase does not
+    // start on an LDS round trip after the softmax
+    bf16x8_t vpre[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) vpre[u] = *reinterpret_cast<const bf16x8_t*>(sV + v_off[0][u]);
+    // element i of s[st]: key t*64 + st*32 + 8*(i/4) + 4g + i%4
+    const int kv0 = t * T::KV;
+    if (kv0 + T::KV > seq_len) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = kv0 + st * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+                if (key >= seq_len) s[st][i] = -INFINITY;
+            }
+    }
+    float tmax = s[0][0];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[st][i]);
+    {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+        tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    // Lazy rescaling: the running max only moves when a row's new max
+    // exceeds it by more than 8 (log2 units). O / l does not depend on
+    // which reference max is used; a stale one bounds P by 2^8.
+    const float cand = tmax * c_log2;
+    const bool move = cand > m_run + 8.0f;
+    const float m_new = move ? cand : m_run;
+    const bool any_move = __ballot(move) != 0ull;   // wave-uniform
+    float alpha = 1.0f;
+    if (any_move) alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.f;
+    bf16x8_t pf[4];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float p = __builtin_amdgcn_exp2f(s[st][i] * c_log2 - m_new);
+            psum += p;
+            pf[st * 2 + (i >> 3)][i & 7] = static_cast<__bf16>(p);
+        }
+    l_run = l_run * alpha + psum;
+    if (any_move) {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+    }
+    // O^T += V^T P^T
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bf16x8_t vf = dt == 0 ? vpre[u] : *reinterpret_cast<const bf16x8_t*>(sV + v_off[dt][u]);
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[u], o[dt], 0, 0, 0);
+        }
+    if constexpr (D == 128) pv_schedule();
+}
+
 template <int D>
 __global__ __launch_bounds__(512, 1) void attention_kernel(const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ k,
@@ -196,80 +280,7 @@ __global__ __launch_bounds__(512, 1) void attention_kernel(const uint16_t* __res
     const int nkv = (seq_len + T::KV - 1) / T::KV;
 
     auto compute = [&](int t, const char* sK, const char* sV) {
-        // S^T = K Q^T for the two 32-key halves of the tile
-        f32x16_t s[2];
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
-#pragma unroll
-            for (int ds = 0; ds < D / 16; ++ds) {
-                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(sK + k_off[st][ds]);
-                s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s[st], 0, 0, 0);
-            }
-        }
-        if constexpr (D == 128) read_ahead_schedule();
-        // the first V^T fragments, read now so that the PV phase does not
-        // start on an LDS round trip after the softmax
-        bf16x8_t vpre[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) vpre[u] = *reinterpret_cast<const bf16x8_t*>(sV + v_off[0][u]);
-        // element i of s[st]: key t*64 + st*32 + 8*(i/4) + 4g + i%4
-        const int kv0 = t * T::KV;
-        if (kv0 + T::KV > seq_len) {
-#pragma unroll
-            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = kv0 + st * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-                    if (key >= seq_len) s[st][i] = -INFINITY;
-                }
-        }
-        float tmax = s[0][0];
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[st][i]);
-        {
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-            tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        }
-        // Lazy rescaling: the running max only moves when a row's new max
-        // exceeds it by more than 8 (log2 units). O / l does not depend on
-        // which reference max is used; a stale one bounds P by 2^8.
-        const float cand = tmax * c_log2;
-        const bool move = cand > m_run + 8.0f;
-        const float m_new = move ? cand : m_run;
-        const bool any_move = __ballot(move) != 0ull;   // wave-uniform
-        float alpha = 1.0f;
-        if (any_move) alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        float psum = 0.f;
-        bf16x8_t pf[4];
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = __builtin_amdgcn_exp2f(s[st][i] * c_log2 - m_new);
-                psum += p;
-                pf[st * 2 + (i >> 3)][i & 7] = static_cast<__bf16>(p);
-            }
-        l_run = l_run * alpha + psum;
-        if (any_move) {
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
-        }
-        // O^T += V^T P^T
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const bf16x8_t vf = dt == 0 ? vpre[u] : *reinterpret_cast<const bf16x8_t*>(sV + v_off[dt][u]);
-                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[u], o[dt], 0, 0, 0);
-            }
-        if constexpr (D == 128) pv_schedule();
+        attn_tile<D>(t, seq_len, g, sK, sV, k_off, v_off, qf, o, m_run, l_run, c_log2);
     };
 
     issue(0, sK0, sV0);
