@@ -21,8 +21,13 @@
 //   halves (lane ^ 32, a register swap, no LDS round trip) and the row sum
 //   none until the end;
 // * online softmax in fp32 with exp2: scores are scaled by log2(e)/sqrt(D)
-//   in one multiply-subtract; O is rescaled only by the lane's own factor,
-//   and only on tiles where some row's maximum grew by more than 2^8;
+//   in one multiply-subtract against the row's current reference; the row
+//   maximum is only taken (and the reference moved, when it grew by more than
+//   2^8) on tiles where a lane's sum reaches 2^60 or is not finite: bf16
+//   probabilities keep their precision at any magnitude, and most tiles skip
+//   the maximum's ~25 VALU operations (attention alone 287 -> 279-285 us);
+//   O is rescaled only by the lane's own factor, and only when the reference
+//   moves;
 // * O^T += V^T P^T: the probabilities are already in the second operand's
 //   register layout (the key order inside one MFMA is free as long as both
 //   operands agree); V^T is stored with the middle quads of every 16 keys
@@ -131,35 +136,54 @@ MMDIT_DEV void attn_tile(int t, int seq_len, int g, const char* sK, const char* 
                 if (key >= seq_len) s[st][i] = -INFINITY;
             }
     }
-    float tmax = s[0][0];
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[st][i]);
-    {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-        tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    // Lazy rescaling: the running max only moves when a row's new max
-    // exceeds it by more than 8 (log2 units). O / l does not depend on
-    // which reference max is used; a stale one bounds P by 2^8.
-    const float cand = tmax * c_log2;
-    const bool move = cand > m_run + 8.0f;
-    const float m_new = move ? cand : m_run;
-    const bool any_move = __ballot(move) != 0ull;   // wave-uniform
-    float alpha = 1.0f;
-    if (any_move) alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    // Exponentials against the current reference first. bf16 and fp32 share
+    // their exponent range, so probabilities up to 2^60 above the reference
+    // lose nothing; the row maximum (and a move of the reference) is only
+    // needed when a lane's sum reaches 2^60 or is not finite (the first
+    // tile, whose reference is -inf, or logits that jumped by ~60 in log2
+    // units). O / l does not depend on which reference is used.
+    float p[2][16];
     float psum = 0.f;
-    bf16x8_t pf[4];
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const float p = __builtin_amdgcn_exp2f(s[st][i] * c_log2 - m_new);
-            psum += p;
-            pf[st * 2 + (i >> 3)][i & 7] = static_cast<__bf16>(p);
+            p[st][i] = __builtin_amdgcn_exp2f(s[st][i] * c_log2 - m_run);
+            psum += p[st][i];
         }
+    float alpha = 1.0f;
+    bool any_move = false;
+    if (__ballot(!(psum < 0x1p60f)) != 0ull) {   // wave-uniform
+        float tmax = s[0][0];
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[st][i]);
+        {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false,
+                                                             false);
+            tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const float cand = tmax * c_log2;
+        const bool move = cand > m_run + 8.0f;
+        const float m_new = move ? cand : m_run;
+        any_move = __ballot(move) != 0ull;
+        alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        psum = 0.f;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                p[st][i] = __builtin_amdgcn_exp2f(s[st][i] * c_log2 - m_new);
+                psum += p[st][i];
+            }
+    }
+    bf16x8_t pf[4];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pf[st * 2 + (i >> 3)][i & 7] = static_cast<__bf16>(p[st][i]);
     l_run = l_run * alpha + psum;
     if (any_move) {
 #pragma unroll
