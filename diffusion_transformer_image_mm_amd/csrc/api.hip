@@ -350,6 +350,21 @@ __global__ void f32_to_f16_kernel(const float* __restrict__ x, uint16_t* __restr
         y[i] = f2h(x[i]);
 }
 
+// fp8 blocks: the attention-layout epilogue writes q and k as e4m3 codes at
+// the power-of-two scales bounded by these norm scales (the fp8 attention's
+// operand quantiser, fused) and stores the exponents
+void set_fp8_qk(GemmArgs& g, const mmdit_dims* d, uint8_t* q8, uint8_t* k8, int* exps, const uint16_t* qn0,
+                const uint16_t* qn1, const uint16_t* kn0, const uint16_t* kn1) {
+    g.q8_out = q8;
+    g.k8_out = k8;
+    g.fp8_norms[0] = qn0;
+    g.fp8_norms[1] = qn1;
+    g.fp8_norms[2] = kn0;
+    g.fp8_norms[3] = kn1;
+    g.fp8_bound = (float)(sqrt((double)d->head_dim) / 448.0);
+    g.fp8_exps = exps;
+}
+
 // ---------------------------------------------------------------- blocks
 // premod: the block's modulation [txt 6H | img 6H] computed beforehand
 // (mmdit_modulation_batch), or null to compute it here from vec
@@ -385,6 +400,7 @@ int run_double(const mmdit_dims* d, const mmdit_double_weights* w, const float* 
         gt.kn = w->txt.k_norm;
         gi.qn = w->img.q_norm ? w->img.q_norm : w->txt.q_norm;
         gi.kn = w->img.k_norm ? w->img.k_norm : w->txt.k_norm;
+        if (fp8) set_fp8_qk(g, d, ws.q8, ws.k8, ws.exps, gt.qn, gi.qn, gt.kn, gi.kn);
         MMDIT_HIP(gemm_2(g, gt, gi, s));
         MMDIT_HIP(launch_zero_attn_pad(ws.q, ws.k, ws.vt, d->heads, d->head_dim, L, LP, s));
     } else {
@@ -401,8 +417,12 @@ int run_double(const mmdit_dims* d, const mmdit_double_weights* w, const float* 
     if (fp8) {
         const uint16_t* qn1 = w->img.q_norm ? w->img.q_norm : w->txt.q_norm;
         const uint16_t* kn1 = w->img.k_norm ? w->img.k_norm : w->txt.k_norm;
-        MMDIT_HIP(launch_quantize_attention_fp8(ws.q, ws.k, ws.vt, d->heads, d->head_dim, LP, w->txt.q_norm, qn1,
-                                                w->txt.k_norm, kn1, ws.q8, ws.k8, ws.vt8, ws.sv, ws.exps, s));
+        if (H % 256 == 0)   // q, k codes came from the QKV epilogue; v^T needs its per-channel maxima
+            MMDIT_HIP(launch_quantize_vt_fp8(ws.vt, d->heads, d->head_dim, LP, ws.vt8, ws.sv, s));
+        else
+            MMDIT_HIP(launch_quantize_attention_fp8(ws.q, ws.k, ws.vt, d->heads, d->head_dim, LP, w->txt.q_norm,
+                                                    qn1, w->txt.k_norm, kn1, ws.q8, ws.k8, ws.vt8, ws.sv, ws.exps,
+                                                    s));
         MMDIT_HIP(launch_attention_fp8(ws.q8, ws.k8, ws.vt8, ws.sv, ws.exps, d->heads, L, d->head_dim, LP, ws.o, H,
                                        s));
     } else {
@@ -469,6 +489,7 @@ int run_single(const mmdit_dims* d, const mmdit_single_weights* w, const float* 
             g.rms_eps = d->rms_eps;
             g0.qn = w->q_norm;
             g0.kn = w->k_norm;
+            if (fp8) set_fp8_qk(g, d, ws.q8, ws.k8, ws.exps, w->q_norm, w->q_norm, w->k_norm, w->k_norm);
         }
         MMDIT_HIP(gemm_1(g, g0, s));
         if (fused) MMDIT_HIP(launch_zero_attn_pad(ws.q, ws.k, ws.vt, d->heads, d->head_dim, L, LP, s));
@@ -477,8 +498,12 @@ int run_single(const mmdit_dims* d, const mmdit_single_weights* w, const float* 
                                          w->q_norm, w->k_norm, rope, d->rms_eps, LP, ws.q, ws.k, ws.vt, s));
     }
     if (fp8) {
-        MMDIT_HIP(launch_quantize_attention_fp8(ws.q, ws.k, ws.vt, d->heads, d->head_dim, LP, w->q_norm, nullptr,
-                                                w->k_norm, nullptr, ws.q8, ws.k8, ws.vt8, ws.sv, ws.exps, s));
+        if (H % 256 == 0)   // q, k codes came from linear1's epilogue
+            MMDIT_HIP(launch_quantize_vt_fp8(ws.vt, d->heads, d->head_dim, LP, ws.vt8, ws.sv, s));
+        else
+            MMDIT_HIP(launch_quantize_attention_fp8(ws.q, ws.k, ws.vt, d->heads, d->head_dim, LP, w->q_norm,
+                                                    nullptr, w->k_norm, nullptr, ws.q8, ws.k8, ws.vt8, ws.sv,
+                                                    ws.exps, s));
         MMDIT_HIP(launch_attention_fp8(ws.q8, ws.k8, ws.vt8, ws.sv, ws.exps, d->heads, L, d->head_dim, LP, ws.cat,
                                        H + M, s));
     } else {

@@ -53,6 +53,13 @@ MMDIT_DEV float h2f(uint16_t b) { return static_cast<float>(__builtin_bit_cast(_
 // step every lane holds the sum of a twice larger aligned group), then the
 // row swaps of gfx950 (permlane16 / permlane32) across rows. A fixed
 // sequence, so the result does not depend on timing.
+// Smallest e with 2^e >= b for b >= 0 (0 for b = 0): frexp is exact.
+MMDIT_DEV int ceil_log2_exp(float b) {
+    int e = 0;
+    const float m = frexpf(b, &e);
+    return m == 0.5f ? e - 1 : (m == 0.0f ? 0 : e);
+}
+
 MMDIT_DEV float wave_sum(float v) {
     v += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0xB1, 0xF, 0xF, false));  // lane ^ 1
     v += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x4E, 0xF, 0xF, false));  // lane ^ 2
@@ -181,6 +188,14 @@ struct GemmArgs {
     int l_pad, head_dim;
     const float* rope;      // [L, D/2, 2] fp32 (cos, sin) per pair
     float rms_eps;
+    // fp8 operands only: q and k written as e4m3 codes ([heads, l_pad, D]
+    // bytes, q_out / k_out unused) at the power-of-two scales 2^eq, 2^ek
+    // that the q / k norm scales bound (the fp8 attention's operands)
+    uint8_t* q8_out;
+    uint8_t* k8_out;
+    const uint16_t* fp8_norms[4];   // q text, q image, k text, k image ([D] bf16)
+    float fp8_bound;                // fl32(sqrt(D) / 448)
+    int* fp8_exps;                  // (eq, ek), written by the first column tiles
 };
 
 // Rows [seq_len, l_pad) of the attention operands as zeros.
@@ -224,6 +239,8 @@ hipError_t launch_quantize_fp8_rows(const uint16_t* x, bool x_bf16, int rows, in
 // y fp16 = SiLU(x fp32), n elements
 // fp8 attention (k_attention_fp8.hip): q, k, v^T to e4m3 (exps[0..1] = eq, ek),
 // then the attention on the codes
+hipError_t launch_quantize_vt_fp8(const uint16_t* vt, int heads, int head_dim, int l_pad, uint8_t* vt8, float* sv,
+                                  hipStream_t s);
 hipError_t launch_quantize_attention_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int heads,
                                          int head_dim, int l_pad, const uint16_t* gq0, const uint16_t* gq1,
                                          const uint16_t* gk0, const uint16_t* gk1, uint8_t* q8, uint8_t* k8,

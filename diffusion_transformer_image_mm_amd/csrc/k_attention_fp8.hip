@@ -49,12 +49,6 @@ MMDIT_DEV i32x8_t lds32(const char* p0, const char* p1) {
     const uint4 hi = *reinterpret_cast<const uint4*>(p1);
     return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
-// smallest e with 2^e >= b (b >= 0 finite); 0 for b = 0
-MMDIT_DEV int ceil_log2_exp(float b) {
-    int e = 0;
-    const float m = frexpf(b, &e);
-    return m == 0.5f ? e - 1 : (m == 0.0f ? 0 : e);
-}
 // max|g| over one or two norm-scale vectors of n <= 256 entries, reduced over
 // a 256-thread workgroup (every thread gets the result)
 MMDIT_DEV float block_absmax_bf16(const uint16_t* g0, const uint16_t* g1, int n, float* red) {
@@ -397,6 +391,14 @@ hipError_t launch_quantize_attention_fp8(const uint16_t* q, const uint16_t* k, c
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(quantize_vt_fp8_kernel, dim3(heads * head_dim), block, 0, s, vt, l_pad, vt8, sv);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_vt_fp8(const uint16_t* vt, int heads, int head_dim, int l_pad, uint8_t* vt8, float* sv,
+                                  hipStream_t s) {
+    if ((head_dim != 64 && head_dim != 128) || l_pad <= 0 || l_pad % 64 != 0 || heads <= 0)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(quantize_vt_fp8_kernel, dim3(heads * head_dim), dim3(256), 0, s, vt, l_pad, vt8, sv);
     return hipGetLastError();
 }
 

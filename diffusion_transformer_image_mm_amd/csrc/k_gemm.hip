@@ -592,8 +592,47 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
                 p += __shfl_xor(p, 32, 64);
                 if (lg == 0) red[wn * 256 + wm * 128 + im * 16 + lr] = p;
             }
+            // fp8 operands: the exponents of q's and k's power-of-two scales,
+            // from max|g| over both streams' norm scales (partial maxima of
+            // the wavefronts that hold norm entries, through LDS)
+            float* gpart = red + 4 * 256;            // [8 wavefronts][2]
+            if constexpr (FP8) {
+                if (args.q8_out) {
+                    float gq = 0.f, gk = 0.f;
+                    if (tid < D) {
+                        gq = fmaxf(fabsf(bf2f(args.fp8_norms[0][tid])), fabsf(bf2f(args.fp8_norms[1][tid])));
+                        gk = fmaxf(fabsf(bf2f(args.fp8_norms[2][tid])), fabsf(bf2f(args.fp8_norms[3][tid])));
+                    }
+#pragma unroll
+                    for (int o = 32; o >= 1; o >>= 1) {
+                        gq = fmaxf(gq, __shfl_xor(gq, o, 64));
+                        gk = fmaxf(gk, __shfl_xor(gk, o, 64));
+                    }
+                    if (lane == 0) {
+                        gpart[2 * wave] = gq;
+                        gpart[2 * wave + 1] = gk;
+                    }
+                }
+            }
             wait_vmcnt0();   // this wavefront's slice loads have landed
             __syncthreads();
+            int e8 = 0;                              // this segment's exponent (fp8 operands)
+            if constexpr (FP8) {
+                if (args.q8_out) {
+                    float gq = 0.f, gk = 0.f;
+#pragma unroll
+                    for (int w = 0; w < 8; ++w) {
+                        gq = fmaxf(gq, gpart[2 * w]);
+                        gk = fmaxf(gk, gpart[2 * w + 1]);
+                    }
+                    const int eq = ceil_log2_exp(args.fp8_bound * gq), ek = ceil_log2_exp(args.fp8_bound * gk);
+                    e8 = seg == 0 ? eq : ek;
+                    if (tid == 0 && tc.n0 == 0) {    // every first column tile stores the same pair
+                        args.fp8_exps[0] = eq;
+                        args.fp8_exps[1] = ek;
+                    }
+                }
+            }
             const int wph = D / (16 * TNW);        // wavefronts per head: 1, 2 or 4
             const int w0 = (wn / wph) * wph;
             const uint16_t* gsc = seg == 0 ? G.qn : G.kn;
@@ -624,9 +663,20 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
                         *reinterpret_cast<const float4*>(srope + r * RB + (((dl >> 2) ^ (r & 15)) << 4));
                     const float a0 = acc[in][im][0] * rstd * gs[in][0], b0 = acc[in][im][1] * rstd * gs[in][1];
                     const float a1 = acc[in][im][2] * rstd * gs[in][2], b1 = acc[in][im][3] * rstd * gs[in][3];
-                    *reinterpret_cast<uint2*>(dst + ((size_t)h * args.l_pad + t) * D + dl) =
-                        make_uint2(pack2bf(a0 * c.x - b0 * c.y, a0 * c.y + b0 * c.x),
-                                   pack2bf(a1 * c.z - b1 * c.w, a1 * c.w + b1 * c.z));
+                    const float y0 = a0 * c.x - b0 * c.y, y1 = a0 * c.y + b0 * c.x;
+                    const float y2 = a1 * c.z - b1 * c.w, y3 = a1 * c.w + b1 * c.z;
+                    if (FP8 && args.q8_out) {
+                        // e4m3 codes of the fp32 values at 2^e8 (the RMSNorm bound keeps
+                        // them within 448; the clamp only guards the conversion)
+                        auto q8 = [&](float x) { return fminf(fmaxf(ldexpf(x, -e8), -448.0f), 448.0f); };
+                        uint32_t pk = __builtin_amdgcn_cvt_pk_fp8_f32(q8(y0), q8(y1), 0u, false);
+                        pk = __builtin_amdgcn_cvt_pk_fp8_f32(q8(y2), q8(y3), pk, true);
+                        uint8_t* dst8 = seg == 0 ? args.q8_out : args.k8_out;
+                        *reinterpret_cast<uint32_t*>(dst8 + ((size_t)h * args.l_pad + t) * D + dl) = pk;
+                    } else {
+                        *reinterpret_cast<uint2*>(dst + ((size_t)h * args.l_pad + t) * D + dl) =
+                            make_uint2(pack2bf(y0, y1), pack2bf(y2, y3));
+                    }
                 }
             }
         } else {
@@ -879,7 +929,7 @@ static hipError_t launch_gemm_t(const GemmArgs& a0, hipStream_t s) {
     const bool attn_epi = a.epilogue == EPI_QKV_ATTN || a.epilogue == EPI_SPLIT_GELU_ATTN ||
                           a.epilogue == EPI_SPLIT_SWIGLU_ATTN;
     const size_t lds_main = 2 * (size_t)(A_TILE_BYTES + (W8 ? W_TILE_BYTES_I8 : W_TILE_BYTES_BF16));
-    const size_t lds_epi = 256 * 128 * 4 + 4 * 256 * 4;
+    const size_t lds_epi = 256 * 128 * 4 + 4 * 256 * 4 + 16 * 4;   // + the fp8 exponents' partial maxima
     const size_t lds = attn_epi && lds_epi > lds_main ? lds_epi : lds_main;
     dim3 grid(tiles), block(NTHREADS);
 #define GEMM_CASE(E)                                                                        \

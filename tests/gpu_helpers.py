@@ -96,19 +96,23 @@ def stream():
 MFMA_F8_SUM_ERR = 2.5e-4
 
 
-def attention_fp8_perturbed(q, k, v, heads, eq, ek, rows=None, rng=None, bf16_inputs=True):
+def attention_fp8_perturbed(q, k, v, heads, eq, ek, rows=None, rng=None, bf16_inputs=True, bf16_qk=True):
     """The oracle's fp8 attention (oracle.attention_fp8, SGLang-AMD
-    "Architecture Deep Dive": fp8 on CDNA) with the two perturbations the HIP
-    path applies to it: q, k, v stored in bf16 ahead of the quantiser, and
-    every logit moved uniformly within the fp8 matrix cores' summation error.
-    Built from the oracle's own quantisers; how far it lands from the plain
-    oracle is the method's sensitivity to that arithmetic."""
+    "Architecture Deep Dive": fp8 on CDNA) with the perturbations the HIP
+    path applies to it: v (and, where q and k are not quantised in the QKV
+    projection's epilogue, q and k) stored in bf16 ahead of the quantiser,
+    and every logit moved uniformly within the fp8 matrix cores' summation
+    error. Built from the oracle's own quantisers; how far it lands from the
+    plain oracle is the method's sensitivity to that arithmetic."""
     import math
     import oracle as O
     from diffusion_transformer_image_mm_amd import synth
     rng = rng or np.random.default_rng(0)
+    bf = lambda a: synth.bf16_exact(np.asarray(a, np.float32)).astype(np.float64)
     if bf16_inputs:
-        q, k, v = (synth.bf16_exact(np.asarray(a, np.float32)).astype(np.float64) for a in (q, k, v))
+        v = bf(v)
+        if bf16_qk:
+            q, k = bf(q), bf(k)
     qc, kc = O.quantize_pow2_fp8(q, eq), O.quantize_pow2_fp8(k, ek)
     vc, sv = O.quantize_cols_fp8(v)
     L, HD = kc.shape

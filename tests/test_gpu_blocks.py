@@ -444,8 +444,10 @@ def test_block_fp8_rerun_bit_exact():
 def _oracle_fp8_with_path_storage(inp, rows, seed=0):
     """The oracle's fp8 block with the HIP path's arithmetic applied to its
     own intermediates: every projection's activation rounded to fp16 before
-    it is quantised, q, k, v rounded to bf16 before the fp8 attention, and
-    the attention logits moved within the fp8 matrix cores' summation error
+    it is quantised, v (and q, k where the QKV projection's epilogue does not
+    quantise them: hidden sizes not a multiple of 256) rounded to bf16 before
+    the fp8 attention, and the attention logits moved within the fp8 matrix
+    cores' summation error
     (gpu_helpers.attention_fp8_perturbed). This is the same method on inputs
     moved by one rounding; how far it lands from the plain oracle is the
     method's own sensitivity to that arithmetic (the planted roundings live
@@ -458,8 +460,10 @@ def _oracle_fp8_with_path_storage(inp, rows, seed=0):
         return np.asarray(a, np.float64).astype(np.float16).astype(np.float64)
     try:
         M.linear_act_fp8 = lambda x, lin: lin_orig(f16(x), lin)
+        round_qk = inp["shape"].hidden % 256 != 0
         M.attention_fp8 = lambda q, k, v, heads, eq, ek, rows=None: attention_fp8_perturbed(q, k, v, heads, eq, ek,
-                                                                                            rows, g)
+                                                                                            rows, g,
+                                                                                            bf16_qk=round_qk)
         return oracle_block(inp, rows=rows, fp8=True)
     finally:
         M.linear_act_fp8, M.attention_fp8 = lin_orig, att_orig
