@@ -105,9 +105,12 @@ MMDIT_DEV void g2l_16(const void* gsrc, lds_void* lds_base) {
 // fragment reads that follow (with the builtin it waits for all of them
 // before the first MFMA); the caller orders the LDS accesses itself with
 // s_waitcnt and barriers.
-MMDIT_DEV void g2l_16_asm(const void* gsrc, lds_void* lds_base) {
-    const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+MMDIT_DEV void g2l_16_asm(const void* gsrc, uint32_t lds_addr) {
+    const uint32_t l = __builtin_amdgcn_readfirstlane(lds_addr);
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(l), "v"(gsrc) : "memory", "m0");
+}
+MMDIT_DEV void g2l_16_asm(const void* gsrc, lds_void* lds_base) {
+    g2l_16_asm(gsrc, (uint32_t)(uintptr_t)lds_base);
 }
 
 // Read an activation fragment (8 fp16) from LDS.
@@ -307,26 +310,31 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
         }
     }
 
+    // LDS addresses as 32-bit offsets from the stage base (converting the
+    // generic shared pointer per load cost a 64-bit round trip and a null
+    // check per instruction)
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)smem;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     auto issue_stage = [&](int kt, int s) {
-        char* base = smem + s * STAGE;
+        const uint32_t base = lds0 + (uint32_t)(s * STAGE);
         const uint32_t ka = (uint32_t)kt * (BK * 2);
-        auto dma = [&](const void* g, lds_void* l) {
+        auto dma = [&](const void* g, uint32_t l) {
             if (PIPE) g2l_16_asm(g, l);
-            else g2l_16(g, l);
+            else g2l_16(g, (lds_void*)(uintptr_t)l);
         };
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            dma(a_g + (a_off_g[j] + ka), (lds_void*)(base + ((wave * 4 + j) * 8) * 128));
-        char* wb = base + A_TILE_BYTES;
+            dma(a_g + (a_off_g[j] + ka), base + (uint32_t)(((wave_s * 4 + j) * 8) * 128));
+        const uint32_t wb = base + A_TILE_BYTES;
         if (!W8) {
 #pragma unroll
             for (int j = 0; j < WL; ++j)
-                dma(w_g + (w_off_g[j] + ka), (lds_void*)(wb + ((wave * WL + j) * 8) * 128));
+                dma(w_g + (w_off_g[j] + ka), wb + (uint32_t)(((wave_s * WL + j) * 8) * 128));
         } else {
             const uint32_t kw = (uint32_t)kt * BK;
 #pragma unroll
             for (int j = 0; j < WL8; ++j)
-                g2l_16(w_g + (w_off_g[j] + kw), (lds_void*)(wb + ((wave * WL8 + j) * 16) * 64));
+                g2l_16(w_g + (w_off_g[j] + kw), (lds_void*)(uintptr_t)(wb + (uint32_t)(((wave_s * WL8 + j) * 16) * 64)));
         }
     };
 
