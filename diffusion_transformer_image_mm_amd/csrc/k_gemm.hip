@@ -112,6 +112,14 @@ MMDIT_DEV void g2l_16_asm(const void* gsrc, uint32_t lds_addr) {
 MMDIT_DEV void g2l_16_asm(const void* gsrc, lds_void* lds_base) {
     g2l_16_asm(gsrc, (uint32_t)(uintptr_t)lds_base);
 }
+// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// byte offset (the instruction's scalar-base form: no 64-bit address
+// arithmetic per lane).
+MMDIT_DEV void g2l_16_asm(const char* sbase, uint32_t voff, uint32_t lds_addr) {
+    const uint32_t l = __builtin_amdgcn_readfirstlane(lds_addr);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(l), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
 
 // Read an activation fragment (8 fp16) from LDS.
 MMDIT_DEV f16x8_t lds_frag_h(const char* p) { return *reinterpret_cast<const f16x8_t*>(p); }
@@ -318,18 +326,18 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
     auto issue_stage = [&](int kt, int s) {
         const uint32_t base = lds0 + (uint32_t)(s * STAGE);
         const uint32_t ka = (uint32_t)kt * (BK * 2);
-        auto dma = [&](const void* g, uint32_t l) {
-            if (PIPE) g2l_16_asm(g, l);
-            else g2l_16(g, (lds_void*)(uintptr_t)l);
+        auto dma = [&](const char* g, uint32_t off, uint32_t l) {
+            if (PIPE) g2l_16_asm(g, off, l);
+            else g2l_16(g + off, (lds_void*)(uintptr_t)l);
         };
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            dma(a_g + (a_off_g[j] + ka), base + (uint32_t)(((wave_s * 4 + j) * 8) * 128));
+            dma(a_g, a_off_g[j] + ka, base + (uint32_t)(((wave_s * 4 + j) * 8) * 128));
         const uint32_t wb = base + A_TILE_BYTES;
         if (!W8) {
 #pragma unroll
             for (int j = 0; j < WL; ++j)
-                dma(w_g + (w_off_g[j] + ka), wb + (uint32_t)(((wave_s * WL + j) * 8) * 128));
+                dma(w_g, w_off_g[j] + ka, wb + (uint32_t)(((wave_s * WL + j) * 8) * 128));
         } else {
             const uint32_t kw = (uint32_t)kt * BK;
 #pragma unroll
