@@ -326,10 +326,10 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
     auto issue_stage = [&](int kt, int s) {
         const uint32_t base = lds0 + (uint32_t)(s * STAGE);
         const uint32_t ka = (uint32_t)kt * (BK * 2);
-        auto dma = [&](const char* g, uint32_t off, uint32_t l) {
-            if (PIPE) g2l_16_asm(g, off, l);
-            else g2l_16(g + off, (lds_void*)(uintptr_t)l);
-        };
+        // (the loops order their LDS accesses themselves: a wait for every
+        // load and a barrier before a stage is read, so the compiler need
+        // not see these writes)
+        auto dma = [&](const char* g, uint32_t off, uint32_t l) { g2l_16_asm(g, off, l); };
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             dma(a_g, a_off_g[j] + ka, base + (uint32_t)(((wave_s * 4 + j) * 8) * 128));
@@ -342,7 +342,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
             const uint32_t kw = (uint32_t)kt * BK;
 #pragma unroll
             for (int j = 0; j < WL8; ++j)
-                g2l_16(w_g + (w_off_g[j] + kw), (lds_void*)(uintptr_t)(wb + (uint32_t)(((wave_s * WL8 + j) * 16) * 64)));
+                dma(w_g, w_off_g[j] + kw, wb + (uint32_t)(((wave_s * WL8 + j) * 16) * 64));
         }
     };
 
