@@ -725,7 +725,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
 #pragma unroll
     for (int in = 0; in < TN; ++in) {
         const int n = nb + in * 16;
-        const int nc = n < N ? n : nb;   // out-of-range columns are not stored
+        const int nc = n < N ? n : N - 4;   // out-of-range columns: read a valid column group, store nothing
         const uint2 braw = *reinterpret_cast<const uint2*>(G.bias + nc);
         b[in][0] = bf2f(braw.x & 0xffff); b[in][1] = bf2f(braw.x >> 16);
         b[in][2] = bf2f(braw.y & 0xffff); b[in][3] = bf2f(braw.y >> 16);
@@ -739,6 +739,50 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
             const float4 g4 = *reinterpret_cast<const float4*>(G.gate + nc);
             gt[in][0] = g4.x; gt[in][1] = g4.y; gt[in][2] = g4.z; gt[in][3] = g4.w;
         }
+    }
+    if constexpr (EPI == MMDIT_EPI_GATE_RESID) {
+        // out = resid + gate * y, out possibly aliasing resid: the residual
+        // loads of 2-4 rows are issued together (clamped addresses, so the
+        // loads are straight-line and stay in bounds) before those rows are
+        // stored; loaded one by one between the stores (which may alias
+        // them) they were 32 serial round trips per lane
+        constexpr int RB = (INT8 || FP8 || FP8W) ? 2 : 4;   // (those formats hold per-column scales too)
+#pragma unroll
+        for (int i0 = 0; i0 < TM; i0 += RB) {
+            float4 r[RB][TN];
+#pragma unroll
+            for (int ii = 0; ii < RB; ++ii) {
+                const int m = mb + (i0 + ii) * 16;
+                const size_t grow = (size_t)(G.row0 + (m < M ? m : M - 1));
+#pragma unroll
+                for (int in = 0; in < TN; ++in) {
+                    const int n = nb + in * 16;
+                    r[ii][in] = *reinterpret_cast<const float4*>(args.resid + grow * args.ldr + (n < N ? n : N - 4));
+                }
+            }
+#pragma unroll
+            for (int ii = 0; ii < RB; ++ii) {
+                const int m = mb + (i0 + ii) * 16;
+                if (m >= M) continue;
+                const size_t grow = (size_t)(G.row0 + m);
+                const float sa = FP8 ? args.a_scale[grow] : 1.f;
+#pragma unroll
+                for (int in = 0; in < TN; ++in) {
+                    const int n = nb + in * 16;
+                    if (n >= N) continue;
+                    float y[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        y[j] = FP8 ? (acc[in][i0 + ii][j] * sa) * sc[in][j] + b[in][j]
+                                   : acc[in][i0 + ii][j] * sc[in][j] + b[in][j];
+                    const float4 rr = r[ii][in];
+                    *reinterpret_cast<float4*>(static_cast<float*>(args.out) + grow * args.ldo + n) =
+                        make_float4(rr.x + gt[in][0] * y[0], rr.y + gt[in][1] * y[1], rr.z + gt[in][2] * y[2],
+                                    rr.w + gt[in][3] * y[3]);
+                }
+            }
+        }
+        return;
     }
 #pragma unroll
     for (int im = 0; im < TM; ++im) {
