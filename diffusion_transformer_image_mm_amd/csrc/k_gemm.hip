@@ -77,6 +77,7 @@
 // * M and N tails: loads clamp to the last valid row, stores are guarded;
 // * deterministic (no atomics, fixed k order).
 #include <atomic>
+#include <type_traits>
 
 #include "common.h"
 
@@ -93,6 +94,16 @@ constexpr int W_TILE_BYTES_I8 = BN * BK;        // 16 KB
 typedef __attribute__((address_space(3))) void lds_void;
 
 MMDIT_DEV void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// f(integral_constant<int, I>) for I = B .. E-1 in order, as straight-line
+// code: every index the body derives from I is a constant expression.
+template <int B, int E, class F>
+MMDIT_DEV void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 
 // 16-byte direct global -> LDS load: lane i of the wavefront writes
 // lds_base + 16 * i.
@@ -248,15 +259,20 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
     constexpr bool FP8W = WT == WT_FP8_W16A;   // fp8 W decoded to fp16 against fp16 A
     constexpr bool W8 = INT8 || FP8W;          // one-byte weights in the int8 LDS layout
     constexpr bool SWIGLU = EPI == MMDIT_EPI_SWIGLU || EPI == MMDIT_EPI_SPLIT_SWIGLU;
-    static_assert(PIPE == 0 || F16W, "the pipelined main loop reads plain fp16 weight fragments");
-    static_assert(TNW == 4 || (TNW == 2 && PIPE == 0 && !SWIGLU), "tail tiles: plain loop, no SwiGLU");
+    static_assert(PIPE == 0 || F16W, "the pipelined main loops read plain fp16 weight fragments");
+    static_assert(TNW == 4 || (TNW == 2 && PIPE != 1 && !SWIGLU), "tail tiles: plain or 4-wavefront loop, no SwiGLU");
     static_assert(!FP8 || (TNW == 4 && !SWIGLU), "fp8: 256-wide tiles, no SwiGLU epilogue");
     constexpr int ES = FP8 ? 1 : 2;            // bytes per element of A (and of 16-bit / fp8 W)
     constexpr int BNT = 64 * TNW;                                 // tile width (output columns)
     constexpr int W_TILE = BNT * BK * (W8 ? 1 : 2);               // fp16 weights: as bf16
     constexpr int STAGE = A_TILE_BYTES + W_TILE;
-    constexpr int TM = 8, TN = TNW;   // MFMA sub-tiles per wavefront (m, n)
-    constexpr int WL = TNW, WL8 = TNW / 2;   // W loads per wavefront per stage (16-bit, int8)
+    // PIPE 2: four wavefronts (one per SIMD) in a 2 x 2 arrangement, each
+    // 128 x 16*TN; otherwise eight (two per SIMD) in 2 x 4
+    constexpr bool W4 = PIPE == 2;
+    constexpr int NWV = W4 ? 4 : 8, NWN = NWV / 2;   // wavefronts, and along n
+    constexpr int TM = 8, TN = W4 ? 2 * TNW : TNW;  // MFMA sub-tiles per wavefront (m, n)
+    constexpr int LA = 32 / NWV;                     // A loads per wavefront per stage
+    constexpr int WL = 8 * TNW / NWV, WL8 = 4 * TNW / NWV;   // W loads per wavefront per stage (16-bit, int8)
     // stage s: A tile at smem + s*STAGE, W tile right after it
 
     const TileCoord tc = tile_of(args, bid, total, BNT, rt0, tmt);
@@ -264,7 +280,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
     const int M = G.m, N = args.n, K = args.k;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave / NWN, wn = wave % NWN;
     // SwiGLU columns start at sw_from (0, or split_n for the split epilogue);
     // sw_half = M, the number of features
     const int sw_from = EPI == MMDIT_EPI_SPLIT_SWIGLU ? args.split_n : 0;
@@ -274,15 +290,15 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
     // row plus a 32-bit per-lane byte offset within the tile (so the loads
     // use the scalar-base addressing form, and the offsets span at most 256
     // rows whatever the matrix size). A tile: 256 rows x 8 chunks; wavefront
-    // w issues loads j = 0..3 of 8 rows each: lane i covers row
-    // r = (4w + j)*8 + i/8 at LDS position p = i%8, fetching chunk
+    // w issues loads j = 0..LA-1 of 8 rows each: lane i covers row
+    // r = (LA w + j)*8 + i/8 at LDS position p = i%8, fetching chunk
     // c = p ^ ((r >> 1) & 7).
     const int lrow = lane >> 3, lpos = lane & 7;
     const char* a_g = reinterpret_cast<const char*>(args.a) + ((size_t)G.row0 + tc.m0) * args.lda * ES;
-    uint32_t a_off_g[4];
+    uint32_t a_off_g[LA];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = (wave * 4 + j) * 8 + lrow;
+    for (int j = 0; j < LA; ++j) {
+        const int r = (wave * LA + j) * 8 + lrow;
         const int c = lpos ^ ((r >> 1) & 7);
         int gr = tc.m0 + r;
         gr = gr < M ? gr : M - 1;
@@ -331,8 +347,8 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
         // not see these writes)
         auto dma = [&](const char* g, uint32_t off, uint32_t l) { g2l_16_asm(g, off, l); };
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            dma(a_g, a_off_g[j] + ka, base + (uint32_t)(((wave_s * 4 + j) * 8) * 128));
+        for (int j = 0; j < LA; ++j)
+            dma(a_g, a_off_g[j] + ka, base + (uint32_t)(((wave_s * LA + j) * 8) * 128));
         const uint32_t wb = base + A_TILE_BYTES;
         if (!W8) {
 #pragma unroll
@@ -355,9 +371,9 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
         const int c = ks * 4 + lg;
         a_off[ks] = (wm * 128 + lr) * 128 + ((c ^ ((lr >> 1) & 7)) * 16);
         if (!W8)
-            w_off[ks] = (wn * 16 * TNW + lr) * 128 + ((c ^ ((lr >> 1) & 7)) * 16);
+            w_off[ks] = (wn * 16 * TN + lr) * 128 + ((c ^ ((lr >> 1) & 7)) * 16);
         else
-            w_off[ks] = (wn * 16 * TNW + lr) * 64 + (((c >> 1) ^ ((lr >> 2) & 3)) * 16) + (c & 1) * 8;
+            w_off[ks] = (wn * 16 * TN + lr) * 64 + (((c >> 1) ^ ((lr >> 2) & 3)) * 16) + (c & 1) * 8;
     }
 
     f32x4_t acc[TN][TM];
@@ -371,6 +387,89 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
     wait_vmcnt0();
     __syncthreads();
 
+    if constexpr (W4) {
+        // Four wavefronts, one per SIMD, each 128 x 16 TN (TN x TM x 4
+        // accumulators, in AGPRs). The MFMAs are instructions tied to their
+        // accumulator registers: issued as builtins, the compiler copied the
+        // 256 accumulators between AGPRs and VGPRs inside the loop. Statements
+        // in asm keep their order, so the loop is laid out here: each
+        // half-stage starts with LEAD MFMAs on fragments read a half earlier,
+        // waits for those reads (an s_waitcnt the compiler counts, so it need
+        // not track the old and the new reads together), then spreads the
+        // other half's fragment reads between its MFMAs; in the second half
+        // the next-but-one stage's direct-to-LDS loads go between the MFMAs
+        // too. With one wavefront per SIMD nothing hides a stalled issue slot
+        // (measured: ~14 cycles of MFMA issue per direct-to-LDS load), so the
+        // loads take their k-advance in the scalar base, not per lane. The
+        // barrier sits between the halves, as in the eight-wavefront loop.
+        constexpr int NM = TN * TM;   // MFMAs per half-stage
+        constexpr int NR = TN + TM;   // fragment reads per half-stage
+        constexpr int ND = LA + WL;   // direct-to-LDS loads per stage
+        constexpr int LEAD = 4;
+        // (the schedule is generated at compile time: every accumulator index
+        // and every placement below is a constant expression)
+        f16x8_t r0a[TM], r0w[TN], r1a[TM], r1w[TN];
+        auto rd = [&](int kt, int ks, f16x8_t* fa, f16x8_t* fw, int j) __attribute__((always_inline)) {
+            const char* sa = smem + (kt & 1) * STAGE;
+            if (j < TM)
+                fa[j] = lds_frag_h(sa + a_off[ks] + j * 16 * 128);
+            else
+                fw[j - TM] = lds_frag_h(sa + A_TILE_BYTES + w_off[ks] + (j - TM) * 16 * 128);
+        };
+        auto dma_j = [&](int kt, int s, int j) __attribute__((always_inline)) {   // load j of stage kt into buffer s
+            const uint32_t base = lds0 + (uint32_t)(s * STAGE);
+            const size_t ka = (size_t)kt * (BK * 2);
+            if (j < LA)
+                g2l_16_asm(a_g + ka, a_off_g[j], base + (uint32_t)(((wave_s * LA + j) * 8) * 128));
+            else
+                g2l_16_asm(w_g + ka, w_off_g[j - LA],
+                           base + A_TILE_BYTES + (uint32_t)(((wave_s * WL + j - LA) * 8) * 128));
+        };
+        issue_stage(nk > 1 ? 1 : 0, 1);
+#pragma unroll
+        for (int j = 0; j < NR; ++j) rd(0, 0, r0a, r0w, j);
+        for (int kt = 0; kt < nk; ++kt) {
+            // first half: MFMAs on r0 (substep 0 of stage kt), reads of r1 (substep 1)
+            static_for<0, NM>([&](auto I) __attribute__((always_inline)) {
+                constexpr int i = decltype(I)::value;
+                asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0"
+                             : "+a"(acc[i / TM][i % TM])
+                             : "v"(r0w[i / TM]), "v"(r0a[i % TM])
+                             : "memory");
+                if constexpr (i == LEAD - 1) __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): r0 was read a half-stage ago
+                static_for<0, NR>([&](auto J) __attribute__((always_inline)) {
+                    constexpr int j = decltype(J)::value;
+                    if constexpr (i == LEAD + ((NM - LEAD) * j) / NR) rd(kt, 1, r1a, r1w, j);
+                });
+            });
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            wait_vmcnt0();
+            __syncthreads();
+            // branch-free: past the end the loads repeat the last stage into the
+            // free buffer and the reads fetch values that are never used
+            const int kn = kt + 2 < nk ? kt + 2 : nk - 1;
+            // second half: MFMAs on r1, reads of r0 (stage kt + 1), loads of stage kn
+            static_for<0, NM>([&](auto I) __attribute__((always_inline)) {
+                constexpr int i = decltype(I)::value;
+                asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0"
+                             : "+a"(acc[i / TM][i % TM])
+                             : "v"(r1w[i / TM]), "v"(r1a[i % TM])
+                             : "memory");
+                static_for<0, NR>([&](auto J) __attribute__((always_inline)) {
+                    constexpr int j = decltype(J)::value;
+                    if constexpr (i == (NM * j) / NR) rd(kt + 1, 0, r0a, r0w, j);
+                });
+                static_for<0, ND>([&](auto J) __attribute__((always_inline)) {
+                    constexpr int j = decltype(J)::value;
+                    if constexpr (i == (NM * j) / ND + 1) dma_j(kn, kt & 1, j);
+                });
+            });
+        }
+        wait_vmcnt0();
+        // the compiler does not know the statements above are MFMAs: wait out
+        // their result latency before the epilogue reads the accumulators
+        asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+    } else
     if constexpr (FP8) {
         // fp8: one v_mfma_scale_f32_16x16x128_f8f6f4 per 16x16 sub-tile and
         // stage (unit block scales). Lane l takes row l%16 and k-bytes
@@ -500,18 +599,21 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
 
     // ---- epilogue. acc[in][im] element j: output column
     // n = n0 + wn*16*TNW + in*16 + lg*4 + j, row m = m0 + wm*128 + im*16 + lr.
-    const int nb = tc.n0 + wn * 16 * TNW + lg * 4;
+    const int nb = tc.n0 + wn * 16 * TN + lg * 4;
     const int mb = tc.m0 + wm * 128 + lr;
     if (SWIGLU && tc.n0 >= sw_from) {
-        // accumulators in = 0, 1 hold gate, in = 2, 3 up of the same features
-        // f = (n0 - sw_from) / 2 + 32 wn + 16 in + 4 lg + j: out fp16 = SiLU(gate) * up
-        const int fb = ((tc.n0 - sw_from) >> 1) + wn * 32 + lg * 4;
+        // in each group of four accumulator columns (64 tile columns), in = 4q,
+        // 4q + 1 hold gate and 4q + 2, 4q + 3 up of the same 32 features
+        // f = (n0 - sw_from) / 2 + 8 TN wn + 32 q + 16 (in & 1) + 4 lg + j:
+        // out fp16 = SiLU(gate) * up
+        const int fb = ((tc.n0 - sw_from) >> 1) + wn * 8 * TN + lg * 4;
         uint16_t* obase = static_cast<uint16_t*>(EPI == MMDIT_EPI_SPLIT_SWIGLU ? args.out2 : args.out);
         const int ld = EPI == MMDIT_EPI_SPLIT_SWIGLU ? args.ldo2 : args.ldo;
         const int ocol = EPI == MMDIT_EPI_SPLIT_SWIGLU ? args.out2_col : 0;
 #pragma unroll
-        for (int in = 0; in < 2; ++in) {
-            const int f = fb + in * 16;
+        for (int pq = 0; pq < TN / 2; ++pq) {
+            const int in = (pq >> 1) * 4 + (pq & 1);
+            const int f = fb + (pq >> 1) * 32 + (pq & 1) * 16;
             const int ng = sw_from + f, nu = sw_from + sw_half + f;
             const uint2 bg = *reinterpret_cast<const uint2*>(G.bias + ng);
             const uint2 bu = *reinterpret_cast<const uint2*>(G.bias + nu);
@@ -584,7 +686,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
             {
                 const char* rtab = reinterpret_cast<const char*>(args.rope);
                 const int rpl = 1024 / RB;                        // rows per 1 KB load
-                const int loads = 256 / rpl / 8;                  // per wavefront
+                const int loads = 256 / rpl / NWV;                // per wavefront
                 for (int j = 0; j < loads; ++j) {
                     const int blk = wave * loads + j;
                     const int r = blk * rpl + lane / CPR;
@@ -611,7 +713,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
             // fp8 operands: the exponents of q's and k's power-of-two scales,
             // from max|g| over both streams' norm scales (partial maxima of
             // the wavefronts that hold norm entries, through LDS)
-            float* gpart = red + 4 * 256;            // [8 wavefronts][2]
+            float* gpart = red + 4 * 256;            // [NWV wavefronts][2]
             if constexpr (FP8) {
                 if (args.q8_out) {
                     float gq = 0.f, gk = 0.f;
@@ -637,7 +739,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
                 if (args.q8_out) {
                     float gq = 0.f, gk = 0.f;
 #pragma unroll
-                    for (int w = 0; w < 8; ++w) {
+                    for (int w = 0; w < NWV; ++w) {
                         gq = fmaxf(gq, gpart[2 * w]);
                         gk = fmaxf(gk, gpart[2 * w + 1]);
                     }
@@ -649,7 +751,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
                     }
                 }
             }
-            const int wph = D / (16 * TNW);        // wavefronts per head: 1, 2 or 4
+            const int wph = D / (16 * TN);         // wavefronts per head: 1, 2 or 4 (D a multiple of 16 TN)
             const int w0 = (wn / wph) * wph;
             const uint16_t* gsc = seg == 0 ? G.qn : G.kn;
             uint16_t* dst = seg == 0 ? args.q_out : args.k_out;
@@ -746,7 +848,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
         // loads are straight-line and stay in bounds) before those rows are
         // stored; loaded one by one between the stores (which may alias
         // them) they were 32 serial round trips per lane
-        constexpr int RB = (INT8 || FP8 || FP8W) ? 2 : 4;   // (those formats hold per-column scales too)
+        constexpr int RB = (INT8 || FP8 || FP8W || TN > 4) ? 2 : 4;   // (those hold per-column scales or twice the columns)
 #pragma unroll
         for (int i0 = 0; i0 < TM; i0 += RB) {
             float4 r[RB][TN];
@@ -863,6 +965,34 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(const GemmArgs args) 
     gemm_tile<WT, EPI, PIPE, 4>(args, smem, blockIdx.x, nf, 0, tmt - args.tail_rows);
 }
 
+// The four-wavefront kernel (fp16 weights): the same tile dispatch as
+// gemm_kernel with 256 threads per workgroup.
+template <int WT, int EPI>
+__global__ __launch_bounds__(NTHREADS / 2, 1) void gemm_kernel4(const GemmArgs args) {
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    constexpr bool SWIGLU = epi_base(EPI) == MMDIT_EPI_SWIGLU || epi_base(EPI) == MMDIT_EPI_SPLIT_SWIGLU;
+    const int tm0 = (args.g[0].m + BM - 1) / BM;
+    const int tmt = args.ngroups == 2 ? tm0 + (args.g[1].m + BM - 1) / BM : tm0;
+    const int nf = args.full_tiles;
+    if constexpr (!SWIGLU) {
+        if (args.head_rows > 0) {
+            const int nh = args.head_rows * ((args.n + BN / 2 - 1) / (BN / 2));
+            if ((int)blockIdx.x < nh) {
+                gemm_tile<WT, EPI, 2, 2>(args, smem, blockIdx.x, nh, 0, args.head_rows);
+                return;
+            }
+            gemm_tile<WT, EPI, 2, 4>(args, smem, blockIdx.x - nh, nf, args.head_rows, tmt - args.head_rows);
+            return;
+        }
+        if ((int)blockIdx.x >= nf) {
+            gemm_tile<WT, EPI, 2, 2>(args, smem, blockIdx.x - nf, gridDim.x - nf, tmt - args.tail_rows,
+                                     args.tail_rows);
+            return;
+        }
+    }
+    gemm_tile<WT, EPI, 2, 4>(args, smem, blockIdx.x, nf, 0, tmt - args.tail_rows);
+}
+
 // Length, in half tile-times, of a launch that dispatches n_half tiles of
 // half a tile-time and then n_full tiles of one tile-time, in grid order,
 // each to the first compute unit that becomes free (cus units).
@@ -924,6 +1054,20 @@ static hipError_t lds_attribute_once(const void* kfn, int lds, std::atomic<uint6
     return e;
 }
 
+// The kernel for weight type WT and epilogue E: fp16 weights take the
+// four-wavefront kernel (w4) or the pipelined eight-wavefront one, the other
+// formats the plain eight-wavefront loop.
+template <int WT, int E>
+static void (*gemm_kernel_for(bool w4))(const GemmArgs) {
+    if constexpr (WT == MMDIT_F16) {
+        if (w4) return gemm_kernel4<WT, E>;
+        return gemm_kernel<WT, E, 1>;
+    } else {
+        (void)w4;
+        return gemm_kernel<WT, E, 0>;
+    }
+}
+
 template <int WT>
 static hipError_t launch_gemm_t(const GemmArgs& a0, hipStream_t s) {
     constexpr bool W8 = WT == MMDIT_INT8 || WT == WT_FP8_W16A;   // one-byte weight tiles
@@ -939,6 +1083,12 @@ static hipError_t launch_gemm_t(const GemmArgs& a0, hipStream_t s) {
     // (which keep the plain loop) run inside the pipelined kernels too,
     // alternating processes on one box).
     const bool pipe = WT == MMDIT_F16;
+    // ... and with fp16 weights the four-wavefront kernel, whose wavefronts
+    // hold 128 x 128 of the tile (a third fewer LDS fragment reads per MFMA);
+    // its attention-layout epilogues need whole heads per wavefront
+    const bool attn_epi0 = a.epilogue == EPI_QKV_ATTN || a.epilogue == EPI_SPLIT_GELU_ATTN ||
+                           a.epilogue == EPI_SPLIT_SWIGLU_ATTN;
+    const bool w4 = WT == MMDIT_F16 && (!attn_epi0 || a.head_dim % 128 == 0);
     // Tail tiles: when the last round of 256-wide tiles would fill at most
     // half of the compute units, and the last r row tiles can be cut off so
     // that the rest fills whole rounds, those r row tiles run as 128-wide
@@ -991,14 +1141,14 @@ static hipError_t launch_gemm_t(const GemmArgs& a0, hipStream_t s) {
     const size_t lds_main = 2 * (size_t)(A_TILE_BYTES + (W8 ? W_TILE_BYTES_I8 : W_TILE_BYTES_BF16));
     const size_t lds_epi = 256 * 128 * 4 + 4 * 256 * 4 + 16 * 4;   // + the fp8 exponents' partial maxima
     const size_t lds = attn_epi && lds_epi > lds_main ? lds_epi : lds_main;
-    dim3 grid(tiles), block(NTHREADS);
+    dim3 grid(tiles), block(w4 ? NTHREADS / 2 : NTHREADS);
 #define GEMM_CASE(E)                                                                        \
     case E: if constexpr (WT == MMDIT_FP8 && (epi_base(E) == MMDIT_EPI_SWIGLU || epi_base(E) == MMDIT_EPI_SPLIT_SWIGLU)) { \
         return hipErrorInvalidValue;                                                        \
     } else {                                                                                \
-        auto kfn = pipe ? gemm_kernel<WT, E, (WT == MMDIT_F16 ? 1 : 0)> : gemm_kernel<WT, E, 0>; \
-        static std::atomic<uint64_t> attr_done[2];                                          \
-        hipError_t e = lds_attribute_once((const void*)kfn, (int)lds, attr_done[pipe]);     \
+        auto kfn = gemm_kernel_for<WT, E>(w4);                                              \
+        static std::atomic<uint64_t> attr_done[3];                                          \
+        hipError_t e = lds_attribute_once((const void*)kfn, (int)lds, attr_done[w4 ? 2 : pipe]); \
         if (e != hipSuccess) return e;                                                      \
         hipLaunchKernelGGL(kfn, grid, block, lds, s, a);                                    \
         break;                                                                              \
