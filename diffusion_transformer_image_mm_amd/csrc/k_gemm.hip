@@ -820,6 +820,139 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
         }
         return;
     }
+    // Four-wavefront tiles stage their outputs through LDS (the stage buffers
+    // are free after the main loop) and store whole rows: stored straight from
+    // the MFMA layout, each instruction writes 16 rows x 32 or 64 bytes, and
+    // with every tile of a round reaching its epilogue together those partial
+    // lines were issued at ~7 bytes/clk per CU (measured; the whole-row stores
+    // below write 2-4 full 128-byte lines per instruction). LDS row r holds
+    // its 16-byte chunk q at position q ^ (r & 15): the 16 rows a store
+    // instruction writes fall in distinct bank groups, and a row read is a
+    // permutation within the row.
+    if constexpr (W4 && (EPI == MMDIT_EPI_BIAS || EPI == MMDIT_EPI_BIAS_GELU || EPI == MMDIT_EPI_SPLIT_GELU)) {
+        const bool mlp = EPI == MMDIT_EPI_BIAS_GELU || (EPI == MMDIT_EPI_SPLIT_GELU && tc.n0 >= args.split_n);
+        uint16_t* obase = static_cast<uint16_t*>(args.out);
+        int ld = args.ldo, ocol = 0;
+        if (EPI == MMDIT_EPI_SPLIT_GELU && mlp) {
+            obase = static_cast<uint16_t*>(args.out2);
+            ld = args.ldo2;
+            ocol = args.out2_col - args.split_n;
+        }
+        const bool one_side = EPI != MMDIT_EPI_SPLIT_GELU || mlp || tc.n0 + BNT <= args.split_n;
+        if (one_side && N % 8 == 0 && ld % 8 == 0 && ocol % 8 == 0) {
+            constexpr int RWB = BNT * 2;          // bytes per staged row
+            constexpr int CPR = RWB / 16;         // 16-byte chunks per row
+            float bv[TN][4];
+#pragma unroll
+            for (int in = 0; in < TN; ++in) {
+                const int n = nb + in * 16;
+                const uint2 braw = *reinterpret_cast<const uint2*>(G.bias + (n < N ? n : N - 4));
+                bv[in][0] = bf2f(braw.x & 0xffff); bv[in][1] = bf2f(braw.x >> 16);
+                bv[in][2] = bf2f(braw.y & 0xffff); bv[in][3] = bf2f(braw.y >> 16);
+            }
+            __syncthreads();   // every wavefront's loads have landed and its reads are done
+#pragma unroll
+            for (int im = 0; im < TM; ++im) {
+                const int r = wm * 128 + im * 16 + lr;
+#pragma unroll
+                for (int in = 0; in < TN; ++in) {
+                    const int q = wn * 2 * TN + in * 2 + (lg >> 1);
+                    float y[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) y[j] = acc[in][im][j] + bv[in][j];
+                    uint2 pk;
+                    if (mlp) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) y[j] = gelu_tanh(y[j]);
+                        pk = make_uint2(pack2h(y[0], y[1]), pack2h(y[2], y[3]));
+                    } else {
+                        pk = make_uint2(pack2bf(y[0], y[1]), pack2bf(y[2], y[3]));
+                    }
+                    *reinterpret_cast<uint2*>(smem + r * RWB + ((q ^ (r & 15)) << 4) + (lg & 1) * 8) = pk;
+                }
+            }
+            __syncthreads();
+#pragma unroll 4
+            for (int i = 0; i < CPR; ++i) {
+                const int idx = i * (NTHREADS / 2) + tid;
+                const int r = idx / CPR, q = idx % CPR;
+                const uint4 v = *reinterpret_cast<const uint4*>(smem + r * RWB + ((q ^ (r & 15)) << 4));
+                const int m = tc.m0 + r, n = tc.n0 + q * 8;
+                if (m < M && n < N)
+                    *reinterpret_cast<uint4*>(obase + (size_t)(G.row0 + m) * ld + ocol + n) = v;
+            }
+            return;
+        }
+    }
+    if constexpr (W4 && EPI == MMDIT_EPI_GATE_RESID) {
+        if (N % 4 == 0 && args.ldo % 4 == 0 && args.ldr % 4 == 0) {
+            // fp32 out = resid + gate * (acc + bias) in two passes of half the
+            // columns: pass p stages column blocks p TN/2 .. of every wavefront
+            // (two stripes of 16 TN/2 columns per row), then the rows are read
+            // back, the residual and gate applied, and stored 16 bytes per lane
+            constexpr int SPW = TN / 2;           // column blocks per wavefront and pass
+            constexpr int RWB = BNT * 2;          // bytes per staged row: BNT/2 fp32
+            constexpr int CPR = RWB / 16;
+            constexpr int CPS = SPW * 4;          // chunks per stripe
+            float bv[TN][4];
+#pragma unroll
+            for (int in = 0; in < TN; ++in) {
+                const int n = nb + in * 16;
+                const uint2 braw = *reinterpret_cast<const uint2*>(G.bias + (n < N ? n : N - 4));
+                bv[in][0] = bf2f(braw.x & 0xffff); bv[in][1] = bf2f(braw.x >> 16);
+                bv[in][2] = bf2f(braw.y & 0xffff); bv[in][3] = bf2f(braw.y >> 16);
+            }
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                __syncthreads();   // the loop's (or the previous pass's) LDS accesses are done
+#pragma unroll
+                for (int im = 0; im < TM; ++im) {
+                    const int r = wm * 128 + im * 16 + lr;
+#pragma unroll
+                    for (int b = 0; b < SPW; ++b) {
+                        const int in = p * SPW + b;
+                        const int q = wn * CPS + b * 4 + lg;
+                        *reinterpret_cast<float4*>(smem + r * RWB + ((q ^ (r & 15)) << 4)) =
+                            make_float4(acc[in][im][0] + bv[in][0], acc[in][im][1] + bv[in][1],
+                                        acc[in][im][2] + bv[in][2], acc[in][im][3] + bv[in][3]);
+                    }
+                }
+                __syncthreads();
+                // out may alias resid: a batch's residual (and gate) loads are
+                // issued together, from clamped addresses, before its stores
+                constexpr int BB = 8;
+#pragma unroll
+                for (int i0 = 0; i0 < CPR; i0 += BB) {
+                    float4 rr[BB], g4[BB];
+#pragma unroll
+                    for (int ii = 0; ii < BB; ++ii) {
+                        const int idx = (i0 + ii) * (NTHREADS / 2) + tid;
+                        const int r = idx / CPR, q = idx % CPR;
+                        const int m = tc.m0 + r;
+                        const int n = tc.n0 + (q / CPS) * 16 * TN + p * SPW * 16 + (q % CPS) * 4;
+                        const size_t grow = (size_t)(G.row0 + (m < M ? m : M - 1));
+                        const int nc = n < N ? n : N - 4;
+                        rr[ii] = *reinterpret_cast<const float4*>(args.resid + grow * args.ldr + nc);
+                        g4[ii] = *reinterpret_cast<const float4*>(G.gate + nc);
+                    }
+#pragma unroll
+                    for (int ii = 0; ii < BB; ++ii) {
+                        const int idx = (i0 + ii) * (NTHREADS / 2) + tid;
+                        const int r = idx / CPR, q = idx % CPR;
+                        const int m = tc.m0 + r;
+                        const int n = tc.n0 + (q / CPS) * 16 * TN + p * SPW * 16 + (q % CPS) * 4;
+                        if (m < M && n < N) {
+                            const float4 y = *reinterpret_cast<const float4*>(smem + r * RWB + ((q ^ (r & 15)) << 4));
+                            *reinterpret_cast<float4*>(static_cast<float*>(args.out) + (size_t)(G.row0 + m) * args.ldo + n) =
+                                make_float4(rr[ii].x + g4[ii].x * y.x, rr[ii].y + g4[ii].y * y.y,
+                                            rr[ii].z + g4[ii].z * y.z, rr[ii].w + g4[ii].w * y.w);
+                        }
+                    }
+                }
+            }
+            return;
+        }
+    }
     // Per-column values of the lane's 4 x TN output columns, then the rows:
     // the TN stores of one row (its 16 x TN columns, i.e. whole 128-byte lines
     // of 16-bit output) are issued back to back.
