@@ -27,9 +27,9 @@ L, H, M = 4608, 3072, 12288
 KERNELS = [
     ("mmdit::attention_kernel<128>", "attention (24 heads x 4608 x 128)", 4 * L * L * H, 1024),
     ("mmdit::attention_fp8_kernel<128>", "fp8 attention (24 heads x 4608 x 128)", 4 * L * L * H, 2048),
-    ("mmdit::gemm_kernel<2, 64, 1>", "QKV GEMM + QK-norm + RoPE", 2 * L * 3 * H * H, 1024),
-    ("mmdit::gemm_kernel<2, 2, 1>", "out-projection and MLP-out GEMMs", None, 1024),
-    ("mmdit::gemm_kernel<2, 1, 1>", "MLP-in GEMM + GELU", 2 * L * M * H, 1024),
+    ("mmdit::gemm_kernel4<2, 64>", "QKV GEMM + QK-norm + RoPE", 2 * L * 3 * H * H, 1024),
+    ("mmdit::gemm_kernel4<2, 2>", "out-projection and MLP-out GEMMs", None, 1024),
+    ("mmdit::gemm_kernel4<2, 1>", "MLP-in GEMM + GELU", 2 * L * M * H, 1024),
     ("mmdit::gemm_kernel<3, 1, 0>", "fp8 MLP-in GEMM + GELU", 2 * L * M * H, 2048),
     ("mmdit::ln_modulate_kernel<3, 4, false>", "LN + modulate", None, 1024),
     ("mmdit::gemv_kernel<2, 6>", "modulation GEMV (both streams)", None, 1024),

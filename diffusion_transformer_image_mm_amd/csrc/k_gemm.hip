@@ -23,14 +23,20 @@
 // v_mfma_scale_f32_16x16x128_f8f6f4 with unit block scales; the two row
 // scales multiply the fp32 sum in the epilogue.
 //
-// Shape of the kernel (gfx950, 64-wide wavefronts):
-// * workgroup tile 256 (rows of A) x 256 (rows of W) x 64 (k), 8 wavefronts
-//   (two per SIMD) in a 2 (m) x 4 (n) arrangement, each owning a 128 x 64
-//   sub-tile = 8 x 4 MFMA tiles of v_mfma_f32_16x16x32_f16 (128 fp32
-//   accumulators per lane). Two wavefronts per SIMD matter on gfx950: one
-//   wavefront per SIMD sustains only ~63 B/clk/CU of 16-byte LDS reads, two
-//   reach ~155 B/clk/CU (measured), and the MFMA pipe reaches 2.2 PFLOP/s
-//   only with at least two wavefronts per SIMD;
+// Shape of the kernels (gfx950, 64-wide wavefronts):
+// * workgroup tile 256 (rows of A) x 256 (rows of W) x 64 (k);
+// * fp16 weights (the block's projections): gemm_kernel4, 4 wavefronts (one
+//   per SIMD) in a 2 x 2 arrangement, each owning a 128 x 128 sub-tile = 8 x 8
+//   MFMA tiles of v_mfma_f32_16x16x32_f16 (256 fp32 accumulators per lane, in
+//   AGPRs). Per MFMA this reads a third fewer operand bytes from LDS than
+//   128 x 64 sub-tiles. With one wavefront per SIMD nothing hides a stalled
+//   issue slot, so the main loop is laid out by hand (see there). Against the
+//   eight-wavefront kernel: FLUX double block -3%, single block -2%, each
+//   projection 7-10% faster alone;
+// * the other weight formats: gemm_kernel, 8 wavefronts (two per SIMD) in a
+//   2 (m) x 4 (n) arrangement, each owning a 128 x 64 sub-tile = 8 x 4 MFMA
+//   tiles (128 fp32 accumulators per lane); their weight fragments are
+//   converted in registers, which the second wavefront of a SIMD overlaps;
 // * W is the MFMA's first operand and A the second, so the hardware result
 //   is the transposed tile and each lane ends up with 4 consecutive output
 //   columns of one row: 8-byte 16-bit / 16-byte fp32 epilogue stores, issued
@@ -44,10 +50,13 @@
 //   distinct 16-byte bank groups;
 // * one barrier per k-step: with bf16, int8 and fp8 weights all fragments of
 //   the current stage are read into registers before the next stage's loads
-//   are issued; with fp16 weights (the block's projections) a half-stage
-//   register pipeline instead interleaves the fragment reads of one
-//   k-substep with the MFMAs of the other (128-wide tail and head tiles keep
-//   the plain loop);
+//   are issued; with fp16 weights a half-stage register pipeline instead
+//   interleaves the fragment reads of one k-substep with the MFMAs of the
+//   other (in its eight-wavefront form for attention-layout epilogues whose
+//   head size is not a multiple of 128: a four-wavefront sub-tile spans 128
+//   columns and its RMSNorm needs whole heads);
+// * four-wavefront tiles stage their 16-bit and gated-residual outputs
+//   through LDS and store whole rows;
 // * grouped launch: up to two weight sets (text / image stream) over
 //   disjoint row ranges in one grid; tiles are laid out per XCD (tile_of);
 // * tail tiles: when the last round of 256-wide tiles would occupy at most

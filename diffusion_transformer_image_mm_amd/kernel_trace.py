@@ -20,7 +20,7 @@ import statistics as st
 import sys
 from collections import defaultdict
 
-DOMINANT = "mmdit::gemm_kernel<2, 1, 1>"   # fp16 weights, bias + GELU epilogue, pipelined main loop
+DOMINANT = "mmdit::gemm_kernel4<2, 1>"   # fp16 weights, bias + GELU epilogue, four-wavefront kernel
 FLOPS = 2 * 4608 * 12288 * 3072
 # the double block's launches in order (the QKV epilogue also does QK-norm +
 # RoPE + the attention layouts)

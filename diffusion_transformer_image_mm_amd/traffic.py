@@ -28,7 +28,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # the kernel's source and the header whose device helpers it inlines
 KERNEL_SOURCES = [os.path.join(ROOT, "diffusion_transformer_image_mm_amd", "csrc", f) for f in ("k_gemm.hip", "common.h")]
 SUMMARY = os.path.join(ROOT, "profiles", "gemm_mlp_in_flux_traffic.txt")
-KERNEL_MATCH = "gemm_kernel<2, 1, 1>"       # fp16 weights, bias + GELU epilogue, pipelined loop
+KERNEL_MATCH = "gemm_kernel4<2, 1>"          # fp16 weights, bias + GELU epilogue, four-wavefront kernel
 COPY_MATCH = "__amd_rocclr_copyBuffer"
 COPY_KIB = 1 << 20                            # the probe copies 1 GiB
 

@@ -9,9 +9,9 @@ import re
 from diffusion_transformer_image_mm_amd import kernel_trace as KT
 
 BLOCK = ["void mmdit::gemv_kernel<2, 6>(float const*)", "void mmdit::ln_modulate_kernel<3, 4, false>(float const*)",
-         "void mmdit::gemm_kernel<2, 64, 1>(mmdit::GemmArgs)", "void mmdit::attention_kernel<128>(unsigned short const*)",
-         "void mmdit::gemm_kernel<2, 2, 1>(mmdit::GemmArgs)", "void mmdit::ln_modulate_kernel<3, 4, false>(float const*)",
-         "void mmdit::gemm_kernel<2, 1, 1>(mmdit::GemmArgs)", "void mmdit::gemm_kernel<2, 2, 1>(mmdit::GemmArgs)"]
+         "void mmdit::gemm_kernel4<2, 64>(mmdit::GemmArgs)", "void mmdit::attention_kernel<128>(unsigned short const*)",
+         "void mmdit::gemm_kernel4<2, 2>(mmdit::GemmArgs)", "void mmdit::ln_modulate_kernel<3, 4, false>(float const*)",
+         "void mmdit::gemm_kernel4<2, 1>(mmdit::GemmArgs)", "void mmdit::gemm_kernel4<2, 2>(mmdit::GemmArgs)"]
 
 
 def _write(path, launches):
