@@ -25,15 +25,15 @@
 //
 // Shape of the kernels (gfx950, 64-wide wavefronts):
 // * workgroup tile 256 (rows of A) x 256 (rows of W) x 64 (k);
-// * fp16 weights (the block's projections): gemm_kernel4, 4 wavefronts (one
-//   per SIMD) in a 2 x 2 arrangement, each owning a 128 x 128 sub-tile = 8 x 8
-//   MFMA tiles of v_mfma_f32_16x16x32_f16 (256 fp32 accumulators per lane, in
-//   AGPRs). Per MFMA this reads a third fewer operand bytes from LDS than
+// * fp16 weights (the block's projections) and fp8 A and W: gemm_kernel4, 4
+//   wavefronts (one per SIMD) in a 2 x 2 arrangement, each owning a 128 x 128
+//   sub-tile = 8 x 8 MFMA tiles of v_mfma_f32_16x16x32_f16 (or of the scaled
+//   fp8 16x16x128 MFMA; 256 fp32 accumulators per lane, in AGPRs). Per MFMA this reads a third fewer operand bytes from LDS than
 //   128 x 64 sub-tiles. With one wavefront per SIMD nothing hides a stalled
 //   issue slot, so the main loop is laid out by hand (see there). Against the
 //   eight-wavefront kernel: FLUX double block -3%, single block -2%, each
 //   projection 7-10% faster alone;
-// * the other weight formats: gemm_kernel, 8 wavefronts (two per SIMD) in a
+// * bf16, int8 and fp8-decoded weights: gemm_kernel, 8 wavefronts (two per SIMD) in a
 //   2 (m) x 4 (n) arrangement, each owning a 128 x 64 sub-tile = 8 x 4 MFMA
 //   tiles (128 fp32 accumulators per lane); their weight fragments are
 //   converted in registers, which the second wavefront of a SIMD overlaps;
@@ -268,7 +268,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
     constexpr bool FP8W = WT == WT_FP8_W16A;   // fp8 W decoded to fp16 against fp16 A
     constexpr bool W8 = INT8 || FP8W;          // one-byte weights in the int8 LDS layout
     constexpr bool SWIGLU = EPI == MMDIT_EPI_SWIGLU || EPI == MMDIT_EPI_SPLIT_SWIGLU;
-    static_assert(PIPE == 0 || F16W, "the pipelined main loops read plain fp16 weight fragments");
+    static_assert(PIPE == 0 || F16W || (PIPE == 2 && FP8), "the pipelined main loops read plain fp16 (or fp8) fragments");
     static_assert(TNW == 4 || (TNW == 2 && PIPE != 1 && !SWIGLU), "tail tiles: plain or 4-wavefront loop, no SwiGLU");
     static_assert(!FP8 || (TNW == 4 && !SWIGLU), "fp8: 256-wide tiles, no SwiGLU epilogue");
     constexpr int ES = FP8 ? 1 : 2;            // bytes per element of A (and of 16-bit / fp8 W)
@@ -396,6 +396,104 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
     wait_vmcnt0();
     __syncthreads();
 
+    if constexpr (W4 && FP8) {
+        // fp8 A and W, four wavefronts: a stage (128 k) is one k-step of
+        // v_mfma_scale_f32_16x16x128_f8f6f4 (unit block scales), so the
+        // half-stages split the columns instead: the first runs column blocks
+        // 0 .. TN/2-1 and reads the other half's W fragments, the second (after
+        // the barrier) runs TN/2 .. TN-1 while reading the next stage's A
+        // fragments (double-buffered) and first-half W fragments and issuing
+        // the next-but-one stage's direct-to-LDS loads. The MFMAs are
+        // instructions tied to AGPR accumulators, in order (see the fp16 loop).
+        constexpr int TH = TN / 2;   // column blocks per half-stage
+        constexpr int NM = TH * TM;  // MFMAs per half-stage
+        constexpr int ND = LA + WL;  // direct-to-LDS loads per stage
+        constexpr int LEAD = 2;
+        const int s127 = 127;        // e8m0 unit block scale
+        int a_off8[2], w_off8[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int c = 2 * lg + h;
+            a_off8[h] = (wm * 128 + lr) * 128 + ((c ^ ((lr >> 1) & 7)) * 16);
+            w_off8[h] = (wn * 16 * TN + lr) * 128 + ((c ^ ((lr >> 1) & 7)) * 16);
+        }
+        i32x8_t fa[2][TM], fw0[TH], fw1[TH];
+        auto frag8 = [&](const char* p0, const char* p1) __attribute__((always_inline)) {
+            const uint4 lo = *reinterpret_cast<const uint4*>(p0);
+            const uint4 hi = *reinterpret_cast<const uint4*>(p1);
+            return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        };
+        auto rd_a = [&](int kt, i32x8_t* fa_, int im) __attribute__((always_inline)) {
+            const char* sa = smem + (kt & 1) * STAGE;
+            fa_[im] = frag8(sa + a_off8[0] + im * 16 * 128, sa + a_off8[1] + im * 16 * 128);
+        };
+        auto rd_w = [&](int kt, i32x8_t* fw_, int half, int j) __attribute__((always_inline)) {
+            const char* sw = smem + (kt & 1) * STAGE + A_TILE_BYTES;
+            const int in = half * TH + j;
+            fw_[j] = frag8(sw + w_off8[0] + in * 16 * 128, sw + w_off8[1] + in * 16 * 128);
+        };
+        auto dma_j = [&](int kt, int s, int j) __attribute__((always_inline)) {   // load j of stage kt into buffer s
+            const uint32_t base = lds0 + (uint32_t)(s * STAGE);
+            const size_t ka = (size_t)kt * (BK * 2);
+            if (j < LA)
+                g2l_16_asm(a_g + ka, a_off_g[j], base + (uint32_t)(((wave_s * LA + j) * 8) * 128));
+            else
+                g2l_16_asm(w_g + ka, w_off_g[j - LA],
+                           base + A_TILE_BYTES + (uint32_t)(((wave_s * WL + j - LA) * 8) * 128));
+        };
+        auto mf8 = [&](f32x4_t& c, const i32x8_t& w, const i32x8_t& a) __attribute__((always_inline)) {
+            asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
+                         : "+a"(c)
+                         : "v"(w), "v"(a), "v"(s127)
+                         : "memory");
+        };
+        issue_stage(nk > 1 ? 1 : 0, 1);
+#pragma unroll
+        for (int im = 0; im < TM; ++im) rd_a(0, fa[0], im);
+#pragma unroll
+        for (int j = 0; j < TH; ++j) rd_w(0, fw0, 0, j);
+        for (int kt = 0; kt < nk; kt += 2) {
+            // two stages per trip so that the A fragment buffers have fixed names
+            static_for<0, 2>([&](auto PP) __attribute__((always_inline)) {
+                constexpr int par = decltype(PP)::value;   // stage kt + par uses fa[par]
+                const int ks = kt + par;
+                if (par == 1 && ks >= nk) return;
+                // first half: column blocks 0 .. TH-1, reads of the second half's W
+                static_for<0, NM>([&](auto I) __attribute__((always_inline)) {
+                    constexpr int i = decltype(I)::value;
+                    mf8(acc[i / TM][i % TM], fw0[i / TM], fa[par][i % TM]);
+                    if constexpr (i == LEAD - 1) __builtin_amdgcn_s_waitcnt(0xC07F);
+                    static_for<0, TH>([&](auto J) __attribute__((always_inline)) {
+                        constexpr int j = decltype(J)::value;
+                        if constexpr (i == LEAD + ((NM - LEAD) * j) / TH) rd_w(ks, fw1, 1, j);
+                    });
+                });
+                __builtin_amdgcn_s_waitcnt(0xC07F);
+                wait_vmcnt0();
+                __syncthreads();
+                const int kn = ks + 2 < nk ? ks + 2 : nk - 1;
+                // second half: column blocks TH .. TN-1; next stage's A and first-half W; loads of stage kn
+                static_for<0, NM>([&](auto I) __attribute__((always_inline)) {
+                    constexpr int i = decltype(I)::value;
+                    mf8(acc[TH + i / TM][i % TM], fw1[i / TM], fa[par][i % TM]);
+                    static_for<0, TM>([&](auto J) __attribute__((always_inline)) {
+                        constexpr int j = decltype(J)::value;
+                        if constexpr (i == (NM * j) / (TM + TH)) rd_a(ks + 1, fa[par ^ 1], j);
+                    });
+                    static_for<0, TH>([&](auto J) __attribute__((always_inline)) {
+                        constexpr int j = decltype(J)::value;
+                        if constexpr (i == (NM * (TM + j)) / (TM + TH)) rd_w(ks + 1, fw0, 0, j);
+                    });
+                    static_for<0, ND>([&](auto J) __attribute__((always_inline)) {
+                        constexpr int j = decltype(J)::value;
+                        if constexpr (i == (NM * j) / ND) dma_j(kn, ks & 1, j);
+                    });
+                });
+            });
+        }
+        wait_vmcnt0();
+        asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+    } else
     if constexpr (W4) {
         // Four wavefronts, one per SIMD, each 128 x 16 TN (TN x TM x 4
         // accumulators, in AGPRs). The MFMAs are instructions tied to their
@@ -838,7 +936,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
     // its 16-byte chunk q at position q ^ (r & 15): the 16 rows a store
     // instruction writes fall in distinct bank groups, and a row read is a
     // permutation within the row.
-    if constexpr (W4 && (EPI == MMDIT_EPI_BIAS || EPI == MMDIT_EPI_BIAS_GELU || EPI == MMDIT_EPI_SPLIT_GELU)) {
+    if constexpr (W4 && (F16W || FP8) && (EPI == MMDIT_EPI_BIAS || EPI == MMDIT_EPI_BIAS_GELU || EPI == MMDIT_EPI_SPLIT_GELU)) {
         const bool mlp = EPI == MMDIT_EPI_BIAS_GELU || (EPI == MMDIT_EPI_SPLIT_GELU && tc.n0 >= args.split_n);
         uint16_t* obase = static_cast<uint16_t*>(args.out);
         int ld = args.ldo, ocol = 0;
@@ -851,24 +949,32 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
         if (one_side && N % 8 == 0 && ld % 8 == 0 && ocol % 8 == 0) {
             constexpr int RWB = BNT * 2;          // bytes per staged row
             constexpr int CPR = RWB / 16;         // 16-byte chunks per row
-            float bv[TN][4];
+            float bv[TN][4], scv[TN][4];
 #pragma unroll
             for (int in = 0; in < TN; ++in) {
                 const int n = nb + in * 16;
-                const uint2 braw = *reinterpret_cast<const uint2*>(G.bias + (n < N ? n : N - 4));
+                const int nc = n < N ? n : N - 4;
+                const uint2 braw = *reinterpret_cast<const uint2*>(G.bias + nc);
                 bv[in][0] = bf2f(braw.x & 0xffff); bv[in][1] = bf2f(braw.x >> 16);
                 bv[in][2] = bf2f(braw.y & 0xffff); bv[in][3] = bf2f(braw.y >> 16);
+                if constexpr (FP8) {
+                    const float4 s4 = *reinterpret_cast<const float4*>(G.scale + nc);
+                    scv[in][0] = s4.x; scv[in][1] = s4.y; scv[in][2] = s4.z; scv[in][3] = s4.w;
+                }
             }
             __syncthreads();   // every wavefront's loads have landed and its reads are done
 #pragma unroll
             for (int im = 0; im < TM; ++im) {
                 const int r = wm * 128 + im * 16 + lr;
+                float sa = 1.f;
+                if constexpr (FP8) sa = args.a_scale[G.row0 + (mb + im * 16 < M ? mb + im * 16 : M - 1)];
 #pragma unroll
                 for (int in = 0; in < TN; ++in) {
                     const int q = wn * 2 * TN + in * 2 + (lg >> 1);
                     float y[4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) y[j] = acc[in][im][j] + bv[in][j];
+                    for (int j = 0; j < 4; ++j)
+                        y[j] = FP8 ? (acc[in][im][j] * sa) * scv[in][j] + bv[in][j] : acc[in][im][j] + bv[in][j];
                     uint2 pk;
                     if (mlp) {
 #pragma unroll
@@ -893,7 +999,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
             return;
         }
     }
-    if constexpr (W4 && EPI == MMDIT_EPI_GATE_RESID) {
+    if constexpr (W4 && (F16W || FP8) && EPI == MMDIT_EPI_GATE_RESID) {
         if (N % 4 == 0 && args.ldo % 4 == 0 && args.ldr % 4 == 0) {
             // fp32 out = resid + gate * (acc + bias) in two passes of half the
             // columns: pass p stages column blocks p TN/2 .. of every wavefront
@@ -903,13 +1009,23 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
             constexpr int RWB = BNT * 2;          // bytes per staged row: BNT/2 fp32
             constexpr int CPR = RWB / 16;
             constexpr int CPS = SPW * 4;          // chunks per stripe
-            float bv[TN][4];
+            float bv[TN][4], scv[TN][4], sav[TM];
 #pragma unroll
             for (int in = 0; in < TN; ++in) {
                 const int n = nb + in * 16;
-                const uint2 braw = *reinterpret_cast<const uint2*>(G.bias + (n < N ? n : N - 4));
+                const int nc = n < N ? n : N - 4;
+                const uint2 braw = *reinterpret_cast<const uint2*>(G.bias + nc);
                 bv[in][0] = bf2f(braw.x & 0xffff); bv[in][1] = bf2f(braw.x >> 16);
                 bv[in][2] = bf2f(braw.y & 0xffff); bv[in][3] = bf2f(braw.y >> 16);
+                if constexpr (FP8) {
+                    const float4 s4 = *reinterpret_cast<const float4*>(G.scale + nc);
+                    scv[in][0] = s4.x; scv[in][1] = s4.y; scv[in][2] = s4.z; scv[in][3] = s4.w;
+                }
+            }
+            if constexpr (FP8) {
+#pragma unroll
+                for (int im = 0; im < TM; ++im)
+                    sav[im] = args.a_scale[G.row0 + (mb + im * 16 < M ? mb + im * 16 : M - 1)];
             }
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
@@ -921,9 +1037,12 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
                     for (int b = 0; b < SPW; ++b) {
                         const int in = p * SPW + b;
                         const int q = wn * CPS + b * 4 + lg;
+                        float y[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            y[j] = FP8 ? (acc[in][im][j] * sav[im]) * scv[in][j] + bv[in][j] : acc[in][im][j] + bv[in][j];
                         *reinterpret_cast<float4*>(smem + r * RWB + ((q ^ (r & 15)) << 4)) =
-                            make_float4(acc[in][im][0] + bv[in][0], acc[in][im][1] + bv[in][1],
-                                        acc[in][im][2] + bv[in][2], acc[in][im][3] + bv[in][3]);
+                            make_float4(y[0], y[1], y[2], y[3]);
                     }
                 }
                 __syncthreads();
@@ -1116,7 +1235,7 @@ __global__ __launch_bounds__(NTHREADS / 2, 1) void gemm_kernel4(const GemmArgs a
     const int tm0 = (args.g[0].m + BM - 1) / BM;
     const int tmt = args.ngroups == 2 ? tm0 + (args.g[1].m + BM - 1) / BM : tm0;
     const int nf = args.full_tiles;
-    if constexpr (!SWIGLU) {
+    if constexpr (!SWIGLU && WT != MMDIT_FP8) {
         if (args.head_rows > 0) {
             const int nh = args.head_rows * ((args.n + BN / 2 - 1) / (BN / 2));
             if ((int)blockIdx.x < nh) {
@@ -1204,6 +1323,9 @@ static void (*gemm_kernel_for(bool w4))(const GemmArgs) {
     if constexpr (WT == MMDIT_F16) {
         if (w4) return gemm_kernel4<WT, E>;
         return gemm_kernel<WT, E, 1>;
+    } else if constexpr (WT == MMDIT_FP8 && epi_base(E) != MMDIT_EPI_SWIGLU && epi_base(E) != MMDIT_EPI_SPLIT_SWIGLU) {
+        if (w4) return gemm_kernel4<WT, E>;
+        return gemm_kernel<WT, E, 0>;
     } else {
         (void)w4;
         return gemm_kernel<WT, E, 0>;
@@ -1230,7 +1352,7 @@ static hipError_t launch_gemm_t(const GemmArgs& a0, hipStream_t s) {
     // its attention-layout epilogues need whole heads per wavefront
     const bool attn_epi0 = a.epilogue == EPI_QKV_ATTN || a.epilogue == EPI_SPLIT_GELU_ATTN ||
                            a.epilogue == EPI_SPLIT_SWIGLU_ATTN;
-    const bool w4 = WT == MMDIT_F16 && (!attn_epi0 || a.head_dim % 128 == 0);
+    const bool w4 = (WT == MMDIT_F16 || WT == MMDIT_FP8) && (!attn_epi0 || a.head_dim % 128 == 0);
     // Tail tiles: when the last round of 256-wide tiles would fill at most
     // half of the compute units, and the last r row tiles can be cut off so
     // that the rest fills whole rounds, those r row tiles run as 128-wide
