@@ -30,7 +30,7 @@ KERNELS = [
     ("mmdit::gemm_kernel4<2, 64>", "QKV GEMM + QK-norm + RoPE", 2 * L * 3 * H * H, 1024),
     ("mmdit::gemm_kernel4<2, 2>", "out-projection and MLP-out GEMMs", None, 1024),
     ("mmdit::gemm_kernel4<2, 1>", "MLP-in GEMM + GELU", 2 * L * M * H, 1024),
-    ("mmdit::gemm_kernel<3, 1, 0>", "fp8 MLP-in GEMM + GELU", 2 * L * M * H, 2048),
+    ("mmdit::gemm_kernel4<3, 1>", "fp8 MLP-in GEMM + GELU", 2 * L * M * H, 2048),
     ("mmdit::ln_modulate_kernel<3, 4, false>", "LN + modulate", None, 1024),
     ("mmdit::gemv_kernel<2, 6>", "modulation GEMV (both streams)", None, 1024),
 ]
