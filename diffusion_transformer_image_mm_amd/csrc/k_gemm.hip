@@ -25,15 +25,20 @@
 //
 // Shape of the kernels (gfx950, 64-wide wavefronts):
 // * workgroup tile 256 (rows of A) x 256 (rows of W) x 64 (k);
-// * fp16 weights (the block's projections) and fp8 A and W: gemm_kernel4, 4
-//   wavefronts (one per SIMD) in a 2 x 2 arrangement, each owning a 128 x 128
+// * fp16 and int8 weights (the block's projections) and fp8 A and W:
+//   gemm_kernel4, 4 wavefronts (one per SIMD) in a 2 x 2 arrangement, each
+//   owning a 128 x 128
 //   sub-tile = 8 x 8 MFMA tiles of v_mfma_f32_16x16x32_f16 (or of the scaled
 //   fp8 16x16x128 MFMA; 256 fp32 accumulators per lane, in AGPRs). Per MFMA this reads a third fewer operand bytes from LDS than
 //   128 x 64 sub-tiles. With one wavefront per SIMD nothing hides a stalled
 //   issue slot, so the main loop is laid out by hand (see there). Against the
 //   eight-wavefront kernel: FLUX double block -3%, single block -2%, each
-//   projection 7-10% faster alone;
-// * bf16, int8 and fp8-decoded weights: gemm_kernel, 8 wavefronts (two per SIMD) in a
+//   projection 7-10% faster alone; int8 codes are converted to fp16 in
+//   small pieces between the MFMAs (FLUX-sized int8 projections 8-11% slower
+//   than fp16 ones alone, against 12-16% with whole-fragment conversions;
+//   the eight-wavefront kernel left the int8 denoise step 6.8% behind the
+//   fp16 one);
+// * bf16 and fp8-decoded weights: gemm_kernel, 8 wavefronts (two per SIMD) in a
 //   2 (m) x 4 (n) arrangement, each owning a 128 x 64 sub-tile = 8 x 4 MFMA
 //   tiles (128 fp32 accumulators per lane); their weight fragments are
 //   converted in registers, which the second wavefront of a SIMD overlaps;
@@ -48,7 +53,7 @@
 //   16-byte chunk c of row r stored at position c ^ ((r >> 1) & 7), so the
 //   16 lanes that read one MFMA operand (16 rows, same chunk) hit 16
 //   distinct 16-byte bank groups;
-// * one barrier per k-step: with bf16, int8 and fp8 weights all fragments of
+// * one barrier per k-step: in the eight-wavefront loop all fragments of
 //   the current stage are read into registers before the next stage's loads
 //   are issued; with fp16 weights a half-stage register pipeline instead
 //   interleaves the fragment reads of one k-substep with the MFMAs of the
@@ -268,7 +273,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
     constexpr bool FP8W = WT == WT_FP8_W16A;   // fp8 W decoded to fp16 against fp16 A
     constexpr bool W8 = INT8 || FP8W;          // one-byte weights in the int8 LDS layout
     constexpr bool SWIGLU = EPI == MMDIT_EPI_SWIGLU || EPI == MMDIT_EPI_SPLIT_SWIGLU;
-    static_assert(PIPE == 0 || F16W || (PIPE == 2 && FP8), "the pipelined main loops read plain fp16 (or fp8) fragments");
+    static_assert(PIPE == 0 || F16W || (PIPE == 2 && (FP8 || INT8)), "the pipelined main loops read plain fp16, fp8 or int8 fragments");
     static_assert(TNW == 4 || (TNW == 2 && PIPE != 1 && !SWIGLU), "tail tiles: plain or 4-wavefront loop, no SwiGLU");
     static_assert(!FP8 || (TNW == 4 && !SWIGLU), "fp8: 256-wide tiles, no SwiGLU epilogue");
     constexpr int ES = FP8 ? 1 : 2;            // bytes per element of A (and of 16-bit / fp8 W)
@@ -488,6 +493,123 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
                         constexpr int j = decltype(J)::value;
                         if constexpr (i == (NM * j) / ND) dma_j(kn, ks & 1, j);
                     });
+                });
+            });
+        }
+        wait_vmcnt0();
+        asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+    } else
+    if constexpr (W4 && INT8) {
+        // int8 weights, four wavefronts: the fp16 loop's schedule (below) with
+        // each W fragment read as its 8 codes (one 8-byte LDS read) and turned
+        // into fp16 as i8x8_to_f16x8 does (per 4 codes: one xor, two byte
+        // permutes, two packed fp16 subtractions). An MFMA here issues every
+        // 16 cycles, so the 10 instructions of a fragment are cut into six
+        // parts of at most two, each placed after its own MFMA (empty asm
+        // statements on a part's inputs and outputs keep it there): fragment
+        // n + 1 of a half-stage after MFMAs 8n .. 8n + 5, and fragment 0 of
+        // the next half-stage (read earlier in this one) after MFMAs 56 .. 61.
+        // The two halves convert into separate registers, so no VALU write
+        // follows an MFMA's read of the same register closely.
+        static_assert(TM == 8, "six conversion parts per group of TM MFMAs");
+        constexpr int NM = TN * TM;   // MFMAs per half-stage
+        constexpr int NR = TN + TM;   // fragment reads per half-stage
+        constexpr int ND = LA + WL8;  // direct-to-LDS loads per stage
+        constexpr int LEAD = 4;
+        f16x8_t r0a[TM], r1a[TM];
+        uint2 r0w[TN], r1w[TN];       // codes
+        uint4 c0w[TN], c1w[TN];       // fp16 fragments of the first / second half
+        uint32_t t_w[2], t_lo[2], t_hi[2];   // a conversion's temporaries, per dword
+        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+        auto rd = [&](int kt, int ks, f16x8_t* fa, uint2* fw, int j) __attribute__((always_inline)) {
+            const char* sa = smem + (kt & 1) * STAGE;
+            if (j < TM)
+                fa[j] = lds_frag_h(sa + a_off[ks] + j * 16 * 128);
+            else
+                fw[j - TM] = *reinterpret_cast<const uint2*>(sa + A_TILE_BYTES + w_off[ks] + (j - TM) * 16 * 64);
+        };
+        auto dma_j = [&](int kt, int s, int j) __attribute__((always_inline)) {   // load j of stage kt into buffer s
+            const uint32_t base = lds0 + (uint32_t)(s * STAGE);
+            if (j < LA)
+                g2l_16_asm(a_g + (size_t)kt * (BK * 2), a_off_g[j], base + (uint32_t)(((wave_s * LA + j) * 8) * 128));
+            else
+                g2l_16_asm(w_g + (size_t)kt * BK, w_off_g[j - LA],
+                           base + A_TILE_BYTES + (uint32_t)(((wave_s * WL8 + j - LA) * 16) * 64));
+        };
+        // part q (0..5) of converting codes raw into out: dword h = q & 1,
+        // step q >> 1
+        auto cvt_part = [&](const uint2& raw, uint4& out, int q) __attribute__((always_inline)) {
+            const int h = q & 1, st = q >> 1;
+            const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+            if (st == 0) {
+                uint32_t x = h ? raw.y : raw.x;
+                asm volatile("" : "+v"(x));
+                t_w[h] = x ^ 0x80808080u;
+                t_lo[h] = __builtin_amdgcn_perm(0x64646464u, t_w[h], 0x04010400u);
+                asm volatile("" : "+v"(t_w[h]), "+v"(t_lo[h]));
+            } else if (st == 1) {
+                t_hi[h] = __builtin_amdgcn_perm(0x64646464u, t_w[h], 0x04030402u);
+                uint32_t o = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, t_lo[h]) - bias);
+                asm volatile("" : "+v"(t_hi[h]), "+v"(o));
+                if (h) out.z = o; else out.x = o;
+            } else {
+                uint32_t o = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, t_hi[h]) - bias);
+                asm volatile("" : "+v"(o));
+                if (h) out.w = o; else out.y = o;
+            }
+        };
+        // one half-stage: MFMAs on (fa, cw), conversions of fw[1..] into cw
+        // and of nfw[0] into ncw[0], the extra work xtra(i) after MFMA i
+        auto half = [&](const f16x8_t* fa, const uint2* fw, uint4* cw, const uint2* nfw, uint4* ncw,
+                        auto&& xtra) __attribute__((always_inline)) {
+            static_for<0, NM>([&](auto I) __attribute__((always_inline)) {
+                constexpr int i = decltype(I)::value;
+                asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0"
+                             : "+a"(acc[i / TM][i % TM])
+                             : "v"(__builtin_bit_cast(f16x8_t, cw[i / TM])), "v"(fa[i % TM])
+                             : "memory");
+                xtra(I);
+                if constexpr (i % TM < 6) {
+                    if constexpr (i / TM + 1 < TN)
+                        cvt_part(fw[i / TM + 1], cw[i / TM + 1], i % TM);
+                    else
+                        cvt_part(nfw[0], ncw[0], i % TM);
+                }
+            });
+        };
+        auto cvt_all = [&](const uint2& raw, uint4& out) __attribute__((always_inline)) {
+#pragma unroll
+            for (int q = 0; q < 6; ++q) cvt_part(raw, out, q);
+        };
+        issue_stage(nk > 1 ? 1 : 0, 1);
+#pragma unroll
+        for (int j = 0; j < NR; ++j) rd(0, 0, r0a, r0w, j);
+        cvt_all(r0w[0], c0w[0]);
+        asm volatile("s_nop 4" ::: "memory");
+        for (int kt = 0; kt < nk; ++kt) {
+            // first half: MFMAs on r0 (substep 0 of stage kt), reads of r1 (substep 1)
+            half(r0a, r0w, c0w, r1w, c1w, [&](auto I) __attribute__((always_inline)) {
+                constexpr int i = decltype(I)::value;
+                if constexpr (i == LEAD - 1) __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+                static_for<0, NR>([&](auto J) __attribute__((always_inline)) {
+                    constexpr int j = decltype(J)::value;
+                    if constexpr (i == LEAD + ((NM - LEAD) * j) / NR) rd(kt, 1, r1a, r1w, j);
+                });
+            });
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            wait_vmcnt0();
+            __syncthreads();
+            const int kn = kt + 2 < nk ? kt + 2 : nk - 1;
+            // second half: MFMAs on r1, reads of r0 (stage kt + 1), loads of stage kn
+            half(r1a, r1w, c1w, r0w, c0w, [&](auto I) __attribute__((always_inline)) {
+                constexpr int i = decltype(I)::value;
+                static_for<0, NR>([&](auto J) __attribute__((always_inline)) {
+                    constexpr int j = decltype(J)::value;
+                    if constexpr (i == (NM * j) / NR) rd(kt + 1, 0, r0a, r0w, j);
+                });
+                static_for<0, ND>([&](auto J) __attribute__((always_inline)) {
+                    constexpr int j = decltype(J)::value;
+                    if constexpr (i == (NM * j) / ND + 1) dma_j(kn, kt & 1, j);
                 });
             });
         }
@@ -936,7 +1058,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
     // its 16-byte chunk q at position q ^ (r & 15): the 16 rows a store
     // instruction writes fall in distinct bank groups, and a row read is a
     // permutation within the row.
-    if constexpr (W4 && (F16W || FP8) && (EPI == MMDIT_EPI_BIAS || EPI == MMDIT_EPI_BIAS_GELU || EPI == MMDIT_EPI_SPLIT_GELU)) {
+    if constexpr (W4 && (F16W || FP8 || INT8) && (EPI == MMDIT_EPI_BIAS || EPI == MMDIT_EPI_BIAS_GELU || EPI == MMDIT_EPI_SPLIT_GELU)) {
         const bool mlp = EPI == MMDIT_EPI_BIAS_GELU || (EPI == MMDIT_EPI_SPLIT_GELU && tc.n0 >= args.split_n);
         uint16_t* obase = static_cast<uint16_t*>(args.out);
         int ld = args.ldo, ocol = 0;
@@ -957,7 +1079,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
                 const uint2 braw = *reinterpret_cast<const uint2*>(G.bias + nc);
                 bv[in][0] = bf2f(braw.x & 0xffff); bv[in][1] = bf2f(braw.x >> 16);
                 bv[in][2] = bf2f(braw.y & 0xffff); bv[in][3] = bf2f(braw.y >> 16);
-                if constexpr (FP8) {
+                if constexpr (FP8 || INT8) {
                     const float4 s4 = *reinterpret_cast<const float4*>(G.scale + nc);
                     scv[in][0] = s4.x; scv[in][1] = s4.y; scv[in][2] = s4.z; scv[in][3] = s4.w;
                 }
@@ -974,7 +1096,9 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
                     float y[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        y[j] = FP8 ? (acc[in][im][j] * sa) * scv[in][j] + bv[in][j] : acc[in][im][j] + bv[in][j];
+                        y[j] = FP8    ? (acc[in][im][j] * sa) * scv[in][j] + bv[in][j]
+                               : INT8 ? acc[in][im][j] * scv[in][j] + bv[in][j]
+                                      : acc[in][im][j] + bv[in][j];
                     uint2 pk;
                     if (mlp) {
 #pragma unroll
@@ -999,7 +1123,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
             return;
         }
     }
-    if constexpr (W4 && (F16W || FP8) && EPI == MMDIT_EPI_GATE_RESID) {
+    if constexpr (W4 && (F16W || FP8 || INT8) && EPI == MMDIT_EPI_GATE_RESID) {
         if (N % 4 == 0 && args.ldo % 4 == 0 && args.ldr % 4 == 0) {
             // fp32 out = resid + gate * (acc + bias) in two passes of half the
             // columns: pass p stages column blocks p TN/2 .. of every wavefront
@@ -1017,7 +1141,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
                 const uint2 braw = *reinterpret_cast<const uint2*>(G.bias + nc);
                 bv[in][0] = bf2f(braw.x & 0xffff); bv[in][1] = bf2f(braw.x >> 16);
                 bv[in][2] = bf2f(braw.y & 0xffff); bv[in][3] = bf2f(braw.y >> 16);
-                if constexpr (FP8) {
+                if constexpr (FP8 || INT8) {
                     const float4 s4 = *reinterpret_cast<const float4*>(G.scale + nc);
                     scv[in][0] = s4.x; scv[in][1] = s4.y; scv[in][2] = s4.z; scv[in][3] = s4.w;
                 }
@@ -1040,7 +1164,9 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
                         float y[4];
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
-                            y[j] = FP8 ? (acc[in][im][j] * sav[im]) * scv[in][j] + bv[in][j] : acc[in][im][j] + bv[in][j];
+                            y[j] = FP8    ? (acc[in][im][j] * sav[im]) * scv[in][j] + bv[in][j]
+                                   : INT8 ? acc[in][im][j] * scv[in][j] + bv[in][j]
+                                          : acc[in][im][j] + bv[in][j];
                         *reinterpret_cast<float4*>(smem + r * RWB + ((q ^ (r & 15)) << 4)) =
                             make_float4(y[0], y[1], y[2], y[3]);
                     }
@@ -1326,6 +1452,9 @@ static void (*gemm_kernel_for(bool w4))(const GemmArgs) {
     } else if constexpr (WT == MMDIT_FP8 && epi_base(E) != MMDIT_EPI_SWIGLU && epi_base(E) != MMDIT_EPI_SPLIT_SWIGLU) {
         if (w4) return gemm_kernel4<WT, E>;
         return gemm_kernel<WT, E, 0>;
+    } else if constexpr (WT == MMDIT_INT8) {
+        if (w4) return gemm_kernel4<WT, E>;
+        return gemm_kernel<WT, E, 0>;
     } else {
         (void)w4;
         return gemm_kernel<WT, E, 0>;
@@ -1347,12 +1476,13 @@ static hipError_t launch_gemm_t(const GemmArgs& a0, hipStream_t s) {
     // (which keep the plain loop) run inside the pipelined kernels too,
     // alternating processes on one box).
     const bool pipe = WT == MMDIT_F16;
-    // ... and with fp16 weights the four-wavefront kernel, whose wavefronts
-    // hold 128 x 128 of the tile (a third fewer LDS fragment reads per MFMA);
-    // its attention-layout epilogues need whole heads per wavefront
+    // ... and with fp16, int8 or fp8 operands the four-wavefront kernel,
+    // whose wavefronts hold 128 x 128 of the tile (a third fewer LDS fragment
+    // reads per MFMA); its attention-layout epilogues need whole heads per
+    // wavefront
     const bool attn_epi0 = a.epilogue == EPI_QKV_ATTN || a.epilogue == EPI_SPLIT_GELU_ATTN ||
                            a.epilogue == EPI_SPLIT_SWIGLU_ATTN;
-    const bool w4 = (WT == MMDIT_F16 || WT == MMDIT_FP8) && (!attn_epi0 || a.head_dim % 128 == 0);
+    const bool w4 = (WT == MMDIT_F16 || WT == MMDIT_FP8 || WT == MMDIT_INT8) && (!attn_epi0 || a.head_dim % 128 == 0);
     // Tail tiles: when the last round of 256-wide tiles would fill at most
     // half of the compute units, and the last r row tiles can be cut off so
     // that the rest fills whole rounds, those r row tiles run as 128-wide
@@ -1404,7 +1534,10 @@ static hipError_t launch_gemm_t(const GemmArgs& a0, hipStream_t s) {
                           a.epilogue == EPI_SPLIT_SWIGLU_ATTN;
     const size_t lds_main = 2 * (size_t)(A_TILE_BYTES + (W8 ? W_TILE_BYTES_I8 : W_TILE_BYTES_BF16));
     const size_t lds_epi = 256 * 128 * 4 + 4 * 256 * 4 + 16 * 4;   // + the fp8 exponents' partial maxima
-    const size_t lds = attn_epi && lds_epi > lds_main ? lds_epi : lds_main;
+    size_t lds = attn_epi && lds_epi > lds_main ? lds_epi : lds_main;
+    // the four-wavefront tiles stage their 16-bit and gated-residual outputs
+    // in LDS: 256 rows x 512 bytes (more than two int8-weight stages)
+    if (w4 && lds < (size_t)256 * 512) lds = (size_t)256 * 512;
     dim3 grid(tiles), block(w4 ? NTHREADS / 2 : NTHREADS);
 #define GEMM_CASE(E)                                                                        \
     case E: if constexpr (WT == MMDIT_FP8 && (epi_base(E) == MMDIT_EPI_SWIGLU || epi_base(E) == MMDIT_EPI_SPLIT_SWIGLU)) { \

@@ -344,6 +344,17 @@ def test_gemm_full_size_sampled_rows(m, n, k, epi):
     assert _gemm_err(g, ref, epi, k) <= TOL
 
 
+@pytest.mark.parametrize("m,n,k,epi", [(4608, 12288, 3072, B.MMDIT_EPI_BIAS_GELU), (4096, 3072, 12288, B.MMDIT_EPI_GATE_RESID),
+                                       (4608, 21504, 3072, B.MMDIT_EPI_SPLIT_GELU)])
+def test_gemm_int8_full_size_sampled_rows(m, n, k, epi):
+    """int8 weight-only projections at FLUX sizes (the four-wavefront loop with
+    in-loop code conversion and the staged epilogues), on sampled rows."""
+    say(f"gemm int8 full m={m} n={n} k={k} epi={epi}")
+    rows = np.unique(np.r_[0, 255, 256, m - 1, np.random.default_rng(m + 1).integers(0, m, 40)])
+    g, ref = _run_gemm(m, n, k, epi, True, rows=rows, tid=62)
+    assert _gemm_err(g, ref, epi, k) <= TOL
+
+
 @pytest.mark.parametrize("m,n,k,epi,wt", [
     (513, 1024, 256, B.MMDIT_EPI_SWIGLU, "bf16"), (300, 512, 448, B.MMDIT_EPI_SWIGLU, "int8"),
     (77, 2048, 320, B.MMDIT_EPI_SWIGLU, "f16"), (1, 256, 64, B.MMDIT_EPI_SWIGLU, "bf16"),
