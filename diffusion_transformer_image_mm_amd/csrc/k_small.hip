@@ -100,17 +100,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ x, 
                         acc += hi[0] * xs[i][4 * j + 2] + hi[1] * xs[i][4 * j + 3];
                     }
                 } else if (WT == MMDIT_F16) {
-                    // fp16 -> fp32 by rescaling the bits: magnitude bits shifted
-                    // into the fp32 exponent/mantissa position, times 2^112
-                    // (exact for normal and subnormal fp16), then the sign
-                    const uint32_t w[4] = {raw[rr][i].x, raw[rr][i].y, raw[rr][i].z, raw[rr][i].w};
+                    // fp16 -> fp32 is exact; converted by the hardware (a bit
+                    // rescale with the sign patched in took ~4 VALU operations
+                    // per weight: 21.0 -> 19.6 us per 113 MB, bit-identical)
+                    const _Float16* e = reinterpret_cast<const _Float16*>(&raw[rr][i]);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float lo = __uint_as_float((w[j] & 0x7fffu) << 13) * 0x1p112f;
-                        const float hi = __uint_as_float((w[j] & 0x7fff0000u) >> 3) * 0x1p112f;
-                        acc += __uint_as_float(__float_as_uint(lo) | ((w[j] & 0x8000u) << 16)) * xs[i][2 * j];
-                        acc += __uint_as_float(__float_as_uint(hi) | (w[j] & 0x80000000u)) * xs[i][2 * j + 1];
-                    }
+                    for (int j = 0; j < 8; ++j) acc += static_cast<float>(e[j]) * xs[i][j];
                 } else {
                     const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw[rr][i]);
 #pragma unroll
