@@ -239,6 +239,9 @@ GEMM_CASES = [
     (513, 1024, 256, B.MMDIT_EPI_BIAS_GELU, True),
     (4096, 64, 3072, B.MMDIT_EPI_EULER, True),
     (320, 1792, 256, B.MMDIT_EPI_SPLIT_GELU, True),
+    # one k-step (K = 64): the int8 loop's prologue conversion and a single stage
+    (513, 1024, 64, B.MMDIT_EPI_BIAS_GELU, True),
+    (257, 3072, 64, B.MMDIT_EPI_GATE_RESID, True),
 ]
 
 
