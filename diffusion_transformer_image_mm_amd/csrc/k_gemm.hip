@@ -634,7 +634,7 @@ MMDIT_DEV void gemm_tile(const GemmArgs& args, char* smem, int bid, int total, i
         constexpr int NM = TN * TM;   // MFMAs per half-stage
         constexpr int NR = TN + TM;   // fragment reads per half-stage
         constexpr int ND = LA + WL;   // direct-to-LDS loads per stage
-        constexpr int LEAD = 4;
+        constexpr int LEAD = 6;       // (4: MLP-in 333-338 us, 6: 328-329 us alone; other shapes equal)
         // (the schedule is generated at compile time: every accumulator index
         // and every placement below is a constant expression)
         f16x8_t r0a[TM], r0w[TN], r1a[TM], r1w[TN];
